@@ -1,0 +1,34 @@
+"""MI355X (gfx950) routed-expert MXFP4 MoE layer.
+
+Python binding of the C ABI in include/moe_mxfp4.h.  Every function here
+only marshals torch tensors into pointers, sizes and the current HIP stream
+and calls the library; all arithmetic runs in the HIP kernels.  There is no
+CPU fallback: if libmoe_mxfp4.so is missing or the device is not gfx950 the
+calls raise.
+
+One layer (the routed experts of a Kimi K3 layer: 16 experts picked per
+token, MXFP4 weights, SwiGLU FFN, weighted combine):
+
+    ids, w = route_topk(logits, k)
+    grp = group_rows(ids, E, workspace)
+    y_rows = expert_ffn_mxfp4(x, k, pool, grp, workspace)
+    out = combine(y_rows, w, grp.row_pos)
+"""
+from ._binding import (  # noqa: F401
+    LIB_PATH,
+    MoeError,
+    ExpertPool,
+    Grouping,
+    MoeWeights,
+    combine,
+    expert_ffn_mxfp4,
+    group_rows,
+    lib,
+    rms_rescale_bf16,
+    route_topk,
+    status_string,
+    workspace_bytes,
+    MAX_EXPERTS,
+    MAX_TOPK,
+    MAX_DIM,
+)

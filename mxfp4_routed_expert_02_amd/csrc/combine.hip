@@ -1,0 +1,89 @@
+// combine.hip - weighted combine of the routed rows back to tokens, and the
+// RMS rescale that joins stacked layers (gfx950).
+//
+// combine: out[t][n] = sum_j w[t][j] * y_rows[row_pos[t*k+j]][n], j ascending.
+// nck blocks per token (blockIdx.x = t * nck + chunk), 4 consecutive outputs per thread
+// with 16-byte loads; the k (weight, position) pairs are wave-uniform.
+#include "moe_internal.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void combine_vec4_kernel(const float* __restrict__ y_rows,
+                                                                const float* __restrict__ w,
+                                                                const int32_t* __restrict__ row_pos, int k,
+                                                                int H, int nck, float* __restrict__ out) {
+  const int t = blockIdx.x / nck;
+  const int i = (blockIdx.x - t * nck) * kThreads + threadIdx.x;  // float4 index
+  if (4 * i >= H) return;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < k; ++j) {
+    const float wt = w[(int64_t)t * k + j];
+    const int64_t p = row_pos[(int64_t)t * k + j];
+    const float4 y = ((const float4*)(y_rows + p * H))[i];
+    acc.x += wt * y.x;
+    acc.y += wt * y.y;
+    acc.z += wt * y.z;
+    acc.w += wt * y.w;
+  }
+  ((float4*)(out + (int64_t)t * H))[i] = acc;
+}
+
+__global__ __launch_bounds__(kThreads) void combine_scalar_kernel(const float* __restrict__ y_rows,
+                                                                  const float* __restrict__ w,
+                                                                  const int32_t* __restrict__ row_pos, int k,
+                                                                  int H, int nck, float* __restrict__ out) {
+  const int t = blockIdx.x / nck;
+  const int n = (blockIdx.x - t * nck) * kThreads + threadIdx.x;
+  if (n >= H) return;
+  float acc = 0.0f;
+  for (int j = 0; j < k; ++j)
+    acc += w[(int64_t)t * k + j] * y_rows[(int64_t)row_pos[(int64_t)t * k + j] * H + n];
+  out[(int64_t)t * H + n] = acc;
+}
+
+// one block per token: sum of squares -> 1/sqrt(mean + eps) -> bf16 RNE
+__global__ __launch_bounds__(kThreads) void rms_rescale_kernel(const float* __restrict__ y, int H, float eps,
+                                                               uint16_t* __restrict__ x_next) {
+  __shared__ float s_part[kThreads / MOE_WAVE];
+  const int t = blockIdx.x;
+  const float* yr = y + (int64_t)t * H;
+  float ss = 0.0f;
+  for (int n = threadIdx.x; n < H; n += kThreads) ss += yr[n] * yr[n];
+  ss = wave_sum(ss);
+  if ((threadIdx.x & (MOE_WAVE - 1)) == 0) s_part[threadIdx.x / MOE_WAVE] = ss;
+  __syncthreads();
+  float tot = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kThreads / MOE_WAVE; ++i) tot += s_part[i];
+  const float r = 1.0f / sqrtf(tot / (float)H + eps);
+  for (int n = threadIdx.x; n < H; n += kThreads) x_next[(int64_t)t * H + n] = f32_to_bf16_rne_dev(yr[n] * r);
+}
+
+}  // namespace
+
+namespace moe {
+
+hipError_t launch_combine(const float* y_rows, const float* w, const int32_t* row_pos, int T, int k, int H,
+                          float* out, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (H % 4 == 0) {
+    const int nck = (H / 4 + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(combine_vec4_kernel, dim3((unsigned)T * nck), dim3(kThreads), 0, s, y_rows, w, row_pos, k,
+                       H, nck, out);
+  } else {
+    const int nck = (H + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(combine_scalar_kernel, dim3((unsigned)T * nck), dim3(kThreads), 0, s, y_rows, w, row_pos,
+                       k, H, nck, out);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rms_rescale(const float* y, int T, int H, float eps, uint16_t* x_next, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(rms_rescale_kernel, dim3(T), dim3(kThreads), 0, s, y, H, eps, x_next);
+  return hipGetLastError();
+}
+
+}  // namespace moe

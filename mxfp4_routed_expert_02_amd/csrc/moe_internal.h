@@ -1,0 +1,78 @@
+// moe_internal.h - device helpers and launcher declarations shared by the
+// HIP sources of libmoe_mxfp4 (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe_mxfp4.h"
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+#define MOE_WAVE 64
+
+// ------------------------------------------------------------------ device --
+// E8M0 scale byte -> 2^(s-127) as fp32 (s = 0 is the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
+  return s == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(s << 23);
+}
+
+// Two E2M1 codes (byte `sel` of `v`, low nibble first) -> two bf16, unscaled.
+// v_cvt_scalef32_pk_bf16_fp4 with scale 1.0: every E2M1 value is exact in bf16.
+template <int SEL>
+__device__ __forceinline__ bf16x2_t fp4x2_to_bf16x2(uint32_t v) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, SEL);
+}
+
+// Two E2M1 codes -> two fp32, unscaled (exact).
+template <int SEL>
+__device__ __forceinline__ f32x2_t fp4x2_to_f32x2(uint32_t v) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, SEL);
+}
+
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2_t, u); }
+
+// a.lo*b.lo + a.hi*b.hi + c in fp32 (v_dot2_f32_bf16); bf16 products are exact.
+__device__ __forceinline__ float dot2_bf16(bf16x2_t a, bf16x2_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+}
+
+// Butterfly sum over the 64 lanes; every lane ends with the same bits.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, MOE_WAVE);
+  return v;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne_dev(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u));
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------- launchers --
+// Each returns hipSuccess or the launch error; all arguments were validated.
+namespace moe {
+
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
+
+hipError_t launch_group_rows(const int32_t* ids, int T, int k, int E, int32_t* offsets, int32_t* sorted_rows,
+                             int32_t* row_pos, int32_t* active, void* ws, hipStream_t s);
+size_t group_rows_workspace(int T, int k, int E);
+
+hipError_t launch_expert_ffn(const uint16_t* x, int T, int k, const moe_mxfp4_weights& w, const int32_t* offsets,
+                             const int32_t* sorted_rows, const int32_t* active, float* y_rows, void* ws,
+                             hipStream_t s);
+size_t expert_ffn_workspace(int T, int k, int E, int H, int I);
+
+hipError_t launch_combine(const float* y_rows, const float* w, const int32_t* row_pos, int T, int k, int H,
+                          float* out, hipStream_t s);
+
+hipError_t launch_rms_rescale(const float* y, int T, int H, float eps, uint16_t* x_next, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,55 @@
+"""A routed-expert layer object: owns the workspace and output buffers for a
+maximum token count and issues the four C-ABI calls on the current stream.
+Reusing one object across stacked layers reuses its buffers (the buffers of
+one layer template serve every layer)."""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _binding as B
+
+
+class RoutedExpertLayer:
+    def __init__(self, E: int, H: int, I: int, k: int, max_tokens: int, device="cuda"):
+        self.E, self.H, self.I, self.k, self.max_tokens = E, H, I, k, max_tokens
+        self.device = torch.device(device)
+        ws = B.workspace_bytes(max_tokens, k, E, H, I)
+        if ws == 0:
+            raise ValueError("shape outside the library's supported ranges")
+        R = max_tokens * k
+        dev = self.device
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+        self.ids = torch.empty((max_tokens, k), dtype=torch.int32, device=dev)
+        self.weights = torch.empty((max_tokens, k), dtype=torch.float32, device=dev)
+        self.grp = B.Grouping(torch.empty(E + 1, dtype=torch.int32, device=dev),
+                              torch.empty(R, dtype=torch.int32, device=dev),
+                              torch.empty(R, dtype=torch.int32, device=dev),
+                              torch.empty(E + 1, dtype=torch.int32, device=dev))
+        self.y_rows = torch.empty((R, H), dtype=torch.float32, device=dev)
+        self.out = torch.empty((max_tokens, H), dtype=torch.float32, device=dev)
+
+    def _views(self, T: int):
+        R = T * self.k
+        grp = B.Grouping(self.grp.expert_offsets, self.grp.sorted_rows[:R], self.grp.row_pos[:R], self.grp.active)
+        return self.ids[:T], self.weights[:T], grp, self.y_rows[:R], self.out[:T]
+
+    def route(self, logits: torch.Tensor):
+        T = logits.shape[0]
+        ids, w, grp, _, _ = self._views(T)
+        B.route_topk(logits, self.k, ids, w)
+        B.group_rows(ids, self.E, self.workspace, grp)
+        return ids, w, grp
+
+    def __call__(self, x: torch.Tensor, logits: torch.Tensor, pool: B.ExpertPool,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """x [T, H] bf16, logits [T, E] fp32 -> out [T, H] fp32."""
+        T = x.shape[0]
+        if T > self.max_tokens:
+            raise ValueError("more tokens than the layer was sized for")
+        ids, w, grp, y_rows, o = self._views(T)
+        B.route_topk(logits, self.k, ids, w)
+        B.group_rows(ids, self.E, self.workspace, grp)
+        B.expert_ffn_mxfp4(x, self.k, pool, grp, self.workspace, y_rows)
+        return B.combine(y_rows, w, grp.row_pos, o if out is None else out)

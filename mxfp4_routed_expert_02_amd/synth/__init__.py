@@ -197,3 +197,29 @@ def router_logits(seed: int, wl: Workload, layer: int = 0, variant: int = 0) -> 
         b[:16] = 64.0
         return (base + b[None, :]).astype(np.float32)
     raise ValueError(f"unknown logits recipe {wl.logits}")
+
+
+def upload_pool(seed: int, pool: int, layer: int, E: int, H: int, I: int, device, nthreads: int = 16,
+                chunk_experts: int = 8):
+    """Generates experts 0..E-1 of (pool, layer) on the host in pinned staging
+    buffers and copies them to a device uint8 tensor [E, slab]."""
+    import torch
+
+    sb = slab_bytes(H, I)
+    dst = torch.empty((E, sb), dtype=torch.uint8, device=device)
+    n = max(1, min(chunk_experts, E))
+    stage = [torch.empty((n, sb), dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+    done = [None, None]
+    stream = torch.cuda.current_stream(device)
+    for i, e0 in enumerate(range(0, E, n)):
+        b = i & 1
+        if done[b] is not None:
+            done[b].synchronize()
+        cnt = min(n, E - e0)
+        fill_slabs_ptr(seed, pool, layer, e0, cnt, H, I, stage[b].data_ptr(), sb, nthreads)
+        dst[e0:e0 + cnt].copy_(stage[b][:cnt], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        done[b] = ev
+    torch.cuda.synchronize(device)
+    return dst

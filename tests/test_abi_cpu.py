@@ -1,0 +1,111 @@
+"""The C-ABI library on a host without a GPU: it loads, exports every entry
+point include/moe_mxfp4.h declares, and rejects bad arguments before it
+touches the device (CPU only; no compute call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mxfp4.h")
+LIB = os.path.join(ROOT, "mxfp4_routed_expert_02_amd", "lib", "libmoe_mxfp4.so")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL, HIPERR = 0, 1, 2, 3, 4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"MOE_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", text)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(LIB):
+        pytest.fail("libmoe_mxfp4.so is not built (run __graft_entry__.build())")
+    from mxfp4_routed_expert_02_amd import _binding
+
+    return _binding.lib()
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for f in ("moe_route_topk", "moe_group_rows", "moe_expert_ffn_mxfp4", "moe_combine"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for s in range(5):
+        assert L.moe_status_string(s).startswith(b"MOE_")
+
+
+def test_workspace_bytes_ranges(L):
+    assert L.moe_workspace_bytes(1, 16, 896, 7168, 1536) >= 16 * 1536 * 4
+    assert L.moe_workspace_bytes(512, 16, 896, 7168, 1536) >= 8192 * 1536 * 4
+    assert L.moe_workspace_bytes(1, 0, 896, 7168, 1536) == 0
+    assert L.moe_workspace_bytes(1, 16, 896, 7100, 1536) == 0  # H not a multiple of 32
+    assert L.moe_workspace_bytes(1, 16, 5000, 7168, 1536) == 0  # E above the maximum
+    assert L.moe_workspace_bytes(1, 33, 896, 7168, 1536) == 0  # k above the maximum
+
+
+FAKE = 0x10000  # a 16-byte aligned non-null pointer value; never dereferenced
+
+
+def test_route_rejects_bad_arguments(L):
+    assert L.moe_route_topk(None, 1, 8, 2, FAKE, FAKE, None) == INVALID
+    assert L.moe_route_topk(FAKE, -1, 8, 2, FAKE, FAKE, None) == INVALID
+    assert L.moe_route_topk(FAKE, 1, 8, 9, FAKE, FAKE, None) == INVALID  # k > E
+    assert L.moe_route_topk(FAKE, 1, 64, 33, FAKE, FAKE, None) == INVALID  # k > 32
+    assert L.moe_route_topk(FAKE, 1, 0, 1, FAKE, FAKE, None) == INVALID
+    assert L.moe_route_topk(FAKE, 1, 4097, 1, FAKE, FAKE, None) == INVALID
+
+
+def test_group_rejects_bad_arguments(L):
+    assert L.moe_group_rows(FAKE, 1, 2, 8, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == INVALID
+    assert L.moe_group_rows(FAKE, 1, 0, 8, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == INVALID
+    assert L.moe_group_rows(FAKE, 1, 2, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == INVALID
+
+
+def _weights(H=256, I=128, E=8, misalign=0, stride=None):
+    from mxfp4_routed_expert_02_amd._binding import MoeWeights
+
+    sb = 3 * (I * H // 2 + I * H // 32)
+    return MoeWeights(FAKE + misalign, FAKE, FAKE, FAKE, FAKE, FAKE, sb if stride is None else stride, E, H, I)
+
+
+def test_ffn_rejects_bad_arguments(L):
+    big = 1 << 30
+    w = _weights()
+    assert L.moe_expert_ffn_mxfp4(None, 4, 2, ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == INVALID
+    assert L.moe_expert_ffn_mxfp4(FAKE + 2, 4, 2, ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, big,
+                                  None) == INVALID  # x misaligned
+    assert L.moe_expert_ffn_mxfp4(FAKE, 4, 2, None, FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == INVALID
+    bad = _weights(misalign=8)
+    assert L.moe_expert_ffn_mxfp4(FAKE, 4, 2, ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == INVALID
+    bad = _weights(H=250)
+    assert L.moe_expert_ffn_mxfp4(FAKE, 4, 2, ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == INVALID
+    bad = _weights(stride=100)
+    assert L.moe_expert_ffn_mxfp4(FAKE, 4, 2, ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == INVALID
+    assert L.moe_expert_ffn_mxfp4(FAKE, 4, 2, ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, 16,
+                                  None) == WS_SMALL
+
+
+def test_combine_and_rescale_reject_bad_arguments(L):
+    assert L.moe_combine(FAKE, FAKE, FAKE, 1, 2, 64, None, None) == INVALID
+    assert L.moe_combine(FAKE + 4, FAKE, FAKE, 1, 2, 64, FAKE, None) == INVALID
+    assert L.moe_combine(FAKE, FAKE, FAKE, 1, 2, 0, FAKE, None) == INVALID
+    assert L.moe_rms_rescale_bf16(FAKE, 1, 0, 1e-6, FAKE, None) == INVALID
+    assert L.moe_rms_rescale_bf16(FAKE, 1, 64, -1.0, FAKE, None) == INVALID
+
+
+def test_valid_call_without_gpu_reports_hip_error(L):
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; this checks the no-device path only")
+    assert L.moe_route_topk(FAKE, 1, 8, 2, FAKE, FAKE, None) == HIPERR

@@ -1,0 +1,192 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Integer results (top-k ids, grouping) must match bit for bit; the routing
+weights within 1e-6; y_rows and the layer output within rel-L2 2e-3 and
+max-abs 1e-2 * rms(ref).  Full-size workloads compare every output the
+oracle can afford and sampled tokens where it cannot.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mxfp4_routed_expert_02_amd import synth
+from tests.gpu_common import (assert_close, check_routing, device_pool, host_pool_subset, run_gpu_layer, say)
+
+pytestmark = pytest.mark.gpu
+NTH = 16
+
+
+def _ref_routing(wl, logits):
+    ids, w = oracle.route_topk(logits, wl.k)
+    grp = oracle.group_rows(ids, wl.E)
+    return dict(ids=ids, w=w, **grp)
+
+
+# ------------------------------------------------------------------ small --
+def _small_case(wl, seed=0):
+    say(f"case {wl.name}: E={wl.E} H={wl.H} I={wl.I} k={wl.k} T={wl.T} logits={wl.logits}")
+    x = synth.activations_bf16(seed, wl)
+    logits = synth.router_logits(seed, wl)
+    pool = device_pool(wl, seed=seed)
+    hpool = oracle.Pool(synth.expert_slabs(seed, wl.pool, 0, 0, wl.E, wl.H, wl.I), wl.H, wl.I)
+    ref = oracle.layer(x, logits, wl.k, hpool, nthreads=NTH)
+    gpu = run_gpu_layer(wl, pool, x, logits)
+    check_routing(gpu, ref, wl.E)
+    if wl.T > 0:
+        assert_close(gpu["y_rows"], ref["y_rows"], "y_rows")
+        assert_close(gpu["out"], ref["out"], "out")
+    return gpu, ref
+
+
+def test_tiny():
+    _small_case(synth.WORKLOADS["tiny"])
+
+
+SMALL = [
+    synth.Workload("one_expert", E=1, H=64, I=32, k=1, T=3, pool=20, sub=20),
+    synth.Workload("k_equals_E", E=8, H=128, I=64, k=8, T=5, pool=21, sub=21),
+    synth.Workload("k32", E=64, H=96, I=64, k=32, T=3, pool=22, sub=22),
+    synth.Workload("ragged_dims", E=12, H=288, I=96, k=3, T=7, pool=23, sub=23),
+    synth.Workload("ties", E=40, H=64, I=64, k=8, T=9, logits="ties", pool=24, sub=24),
+    synth.Workload("hot_experts", E=16, H=64, I=32, k=4, T=70, logits="dense16", pool=25, sub=25),
+    synth.Workload("many_rows_chunks", E=24, H=64, I=32, k=6, T=400, pool=26, sub=26),
+    synth.Workload("wide_rows", E=4, H=4096, I=64, k=2, T=6, pool=27, sub=27),
+    synth.Workload("long_rows_down", E=4, H=64, I=4096, k=2, T=6, pool=28, sub=28),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
+def test_small_shapes(wl):
+    _small_case(wl)
+
+
+def test_empty_batch_is_a_no_op():
+    wl = synth.Workload("empty", E=8, H=64, I=32, k=2, T=0, pool=29, sub=29)
+    pool = device_pool(wl)
+    from mxfp4_routed_expert_02_amd.layer import RoutedExpertLayer
+
+    L = RoutedExpertLayer(wl.E, wl.H, wl.I, wl.k, 1, torch.device("cuda", 0))
+    L.out.fill_(7.0)
+    x = torch.zeros((0, wl.H), dtype=torch.bfloat16, device="cuda")
+    logits = torch.zeros((0, wl.E), dtype=torch.float32, device="cuda")
+    out = L(x, logits, pool)
+    torch.cuda.synchronize()
+    assert out.shape == (0, wl.H)
+    assert torch.all(L.out == 7.0)
+
+
+def test_routing_max_experts_and_ties():
+    from mxfp4_routed_expert_02_amd import route_topk, group_rows
+
+    for wl in (synth.Workload("E4096", E=4096, H=32, I=32, k=32, T=37, sub=30),
+               synth.Workload("ties4096", E=4096, H=32, I=32, k=16, T=19, logits="ties", sub=31),
+               synth.Workload("E896_T2000", E=896, H=32, I=32, k=16, T=2000, logits="zipf", sub=32)):
+        say(f"case {wl.name}")
+        logits = synth.router_logits(0, wl)
+        ref = _ref_routing(wl, logits)
+        dl = torch.from_numpy(logits).cuda()
+        ids, w = route_topk(dl, wl.k)
+        ws = torch.empty(max(256, 1 << 16), dtype=torch.uint8, device="cuda")
+        g = group_rows(ids, wl.E, ws)
+        torch.cuda.synchronize()
+        gpu = dict(ids=ids.cpu().numpy(), w=w.cpu().numpy(), expert_offsets=g.expert_offsets.cpu().numpy(),
+                   sorted_rows=g.sorted_rows.cpu().numpy(), row_pos=g.row_pos.cpu().numpy(),
+                   active=g.active.cpu().numpy())
+        check_routing(gpu, ref, wl.E)
+
+
+def test_group_rows_accepts_repeated_ids():
+    from mxfp4_routed_expert_02_amd import group_rows
+
+    ids_np = np.array([[3, 3, 1], [0, 3, 3], [1, 1, 1], [2, 0, 3]], np.int32)
+    ref = oracle.group_rows(ids_np, 5)
+    ws = torch.empty(1 << 16, dtype=torch.uint8, device="cuda")
+    g = group_rows(torch.from_numpy(ids_np).cuda(), 5, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(g.expert_offsets.cpu().numpy(), ref["expert_offsets"])
+    assert np.array_equal(g.sorted_rows.cpu().numpy(), ref["sorted_rows"])
+    assert np.array_equal(g.row_pos.cpu().numpy(), ref["row_pos"])
+
+
+def test_rms_rescale_matches_oracle():
+    from mxfp4_routed_expert_02_amd import rms_rescale_bf16
+
+    y = synth.normal_f32(synth.key(0, 61), 5 * 7168, stddev=900.0).reshape(5, 7168)
+    ref = oracle.rms_rescale_bf16(y, 1e-6)
+    got = rms_rescale_bf16(torch.from_numpy(y).cuda(), 1e-6).view(torch.int16).cpu().numpy().view(np.uint16)
+    # same arithmetic up to the order of the sum of squares: at most one bf16 ulp apart
+    diff = np.abs(got.astype(np.int32) - ref.astype(np.int32))
+    assert diff.max() <= 1, diff.max()
+    assert (diff > 0).mean() < 1e-3
+
+
+# ---------------------------------------------------------- full shapes ----
+@pytest.fixture(scope="module")
+def pool896():
+    wl = synth.WORKLOADS["decode896"]
+    say("uploading the 896-expert pool (15.7 GB)")
+    p = device_pool(wl)
+    yield p
+    del p
+    torch.cuda.empty_cache()
+
+
+def _full_case(wl, pool, tokens=None, variant=0):
+    x = synth.activations_bf16(0, wl, variant=variant)
+    logits = synth.router_logits(0, wl, variant=variant)
+    ref = _ref_routing(wl, logits)
+    gpu = run_gpu_layer(wl, pool, x, logits)
+    check_routing(gpu, ref, wl.E)
+    toks = list(range(wl.T)) if tokens is None else tokens
+    hpool = host_pool_subset(wl, ref["ids"][toks].reshape(-1))
+    out_ref = oracle.token_layers_parallel(x, ref["ids"], ref["w"], hpool, toks, nthreads=NTH)
+    assert_close(gpu["out"][toks], out_ref, f"out[{len(toks)} tokens]")
+    return gpu, ref, x, logits
+
+
+def test_decode896(pool896):
+    say("case decode896")
+    gpu, ref, _, _ = _full_case(synth.WORKLOADS["decode896"], pool896)
+    again = run_gpu_layer(synth.WORKLOADS["decode896"], pool896, synth.activations_bf16(0, synth.WORKLOADS[
+        "decode896"]), synth.router_logits(0, synth.WORKLOADS["decode896"]))
+    assert np.array_equal(again["out"], gpu["out"]), "run-to-run bits differ"
+
+
+def test_verify8(pool896):
+    say("case verify8")
+    wl = synth.WORKLOADS["verify8"]
+    gpu, ref, x, logits = _full_case(wl, pool896)
+    # each token alone (batch 1) gives the same bits as inside the batch
+    one = synth.Workload("verify8_single", E=wl.E, H=wl.H, I=wl.I, k=wl.k, T=1, pool=wl.pool)
+    for t in (0, 5):
+        single = run_gpu_layer(one, pool896, x[t:t + 1], logits[t:t + 1])
+        assert np.array_equal(single["out"][0], gpu["out"][t]), f"token {t}: batch-1 bits differ from batch-8"
+
+
+def _sample_tokens(ref, T, k, n_hot=4, n_cold=4):
+    counts = np.diff(ref["expert_offsets"])
+    ids = ref["ids"]
+    hot = np.argsort(-counts)[0]
+    cold = [e for e in range(counts.size) if counts[e] == 1]
+    toks = [int(np.nonzero((ids == hot).any(axis=1))[0][i]) for i in range(min(n_hot, counts[hot]))]
+    for e in cold[:n_cold]:
+        toks.append(int(np.nonzero((ids == e).any(axis=1))[0][0]))
+    toks += [0, T - 1]
+    return sorted(set(toks))
+
+
+def test_prefill512(pool896):
+    say("case prefill512")
+    wl = synth.WORKLOADS["prefill512"]
+    x = synth.activations_bf16(0, wl)
+    logits = synth.router_logits(0, wl)
+    ref = _ref_routing(wl, logits)
+    toks = _sample_tokens(ref, wl.T, wl.k)
+    _full_case(wl, pool896, tokens=toks)
+
+
+def test_prefill_dense(pool896):
+    say("case prefill_dense")
+    wl = synth.WORKLOADS["prefill_dense"]
+    _full_case(wl, pool896, tokens=[0, 1, 255, 511])
