@@ -1,0 +1,214 @@
+"""Throughput of the routed-expert MXFP4 layer on one MI355X.
+
+A step is one pass of the whole layer (route top-k -> group rows -> fused
+MXFP4 dequant + SwiGLU expert FFN -> weighted combine) over one batch of
+synthetic input already resident in HBM.  The default workload is batch-1
+decode on one layer of 896 resident experts (hidden 7168, intermediate
+1536, top-16): every step reads the 16 routed experts' MXFP4 weights,
+16 x 17,547,264 bytes.  Steps rotate over 64 seeded (x, logits) variants so
+the routed experts differ from step to step and the 256 MB last-level cache
+cannot serve them.
+
+Prints one JSON line: value = routed-expert weight GB/s of the whole layer,
+plus the roofline of the expert-FFN call (HIP events on the launch stream)
+and the CPU oracle's rate on the host cores as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+FP4_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4 MFMA
+METRIC = "MoE MXFP4 expert layer: decode weight GB/s + prefill TFLOP/s, % of roofline"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--variants", type=int, default=64)
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="bounded oracle sample (0 = skip)")
+    p.add_argument("--cpu-threads", type=int, default=16)
+    p.add_argument("--prefill-reps", type=int, default=10, help="prefill512 side measurement (0 = skip)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world})", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from mxfp4_routed_expert_02_amd import ExpertPool, synth, expert_ffn_mxfp4
+    from mxfp4_routed_expert_02_amd.layer import RoutedExpertLayer
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    wl = synth.WORKLOADS["decode896"]
+    V = args.variants
+    t0 = time.time()
+    slabs = synth.upload_pool(args.seed, wl.pool, 0, wl.E, wl.H, wl.I, dev)
+    pool = ExpertPool(slabs, wl.H, wl.I)
+    log(f"pool: {wl.E} experts, {slabs.numel() / 1e9:.2f} GB resident ({time.time() - t0:.1f} s)")
+    xs = torch.stack([torch.from_numpy(synth.activations_bf16(args.seed, wl, variant=v).view(np.int16))
+                      for v in range(V)]).to(dev).view(torch.bfloat16)  # [V, 1, H]
+    ls = torch.stack([torch.from_numpy(synth.router_logits(args.seed, wl, variant=v)) for v in range(V)]).to(dev)
+    layer = RoutedExpertLayer(wl.E, wl.H, wl.I, wl.k, wl.T, dev)
+    out = torch.empty((wl.T, wl.H), dtype=torch.float32, device=dev)
+    slab_b = synth.slab_bytes(wl.H, wl.I)
+    weight_bytes = wl.T * wl.k * slab_b  # top-16 distinct experts per token, each read once
+    ffn_bytes = weight_bytes + wl.T * wl.H * 2 + wl.R * wl.H * 4  # + x read + y_rows written
+
+    def step(i):
+        layer(xs[i % V], ls[i % V], pool, out)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K whole-layer steps
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    value = weight_bytes / (ms_step * 1e-3) / 1e9
+    log(f"layer: {ms_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us), {value:.0f} GB/s")
+
+    # expert-FFN call alone, events on its launch stream around every call
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    groupings = []
+    for v in range(V):
+        _, _, g = layer.route(ls[v])
+        groupings.append(tuple(t.clone() for t in (g.expert_offsets, g.sorted_rows, g.row_pos, g.active)))
+    from mxfp4_routed_expert_02_amd import Grouping
+
+    gobjs = [Grouping(*g) for g in groupings]
+    y_rows = torch.empty((wl.R, wl.H), dtype=torch.float32, device=dev)
+    for i in range(args.warmup):
+        expert_ffn_mxfp4(xs[i % V], wl.k, pool, gobjs[i % V], layer.workspace, y_rows)
+    torch.cuda.synchronize()
+    for i in range(K):
+        a, b = evs[i]
+        a.record(stream)
+        expert_ffn_mxfp4(xs[i % V], wl.k, pool, gobjs[i % V], layer.workspace, y_rows)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ffn_us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    achieved = ffn_bytes / (ffn_us * 1e-6) / 1e9
+    log(f"expert FFN call: {ffn_us:.1f} us, {achieved:.0f} GB/s of {ffn_bytes} algorithmic bytes")
+
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "mxfp4", "data": "synthetic",
+        "config": {"workload": "decode896", "experts": wl.E, "hidden": wl.H, "inter": wl.I, "topk": wl.k,
+                   "tokens": wl.T, "variants": V, "weight_bytes_per_step": weight_bytes},
+        "roofline": {"bound": "hbm", "kernel": "moe_expert_ffn_mxfp4 call", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "launch_us": round(ffn_us, 2), "algorithmic_bytes": ffn_bytes},
+    }
+
+    if args.prefill_reps > 0:
+        res["prefill512"] = prefill_side(dev, pool, args.seed, args.prefill_reps)
+
+    if args.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(args, wl)
+    print(json.dumps(res), flush=True)
+
+
+def prefill_side(dev, pool, seed, reps):
+    """512-token expert-major prefill on the same pool: algorithmic TFLOP/s."""
+    import numpy as np
+    import torch
+
+    from mxfp4_routed_expert_02_amd import synth
+    from mxfp4_routed_expert_02_amd.layer import RoutedExpertLayer
+
+    wl = synth.WORKLOADS["prefill512"]
+    x = torch.from_numpy(synth.activations_bf16(seed, wl).view(np.int16)).to(dev).view(torch.bfloat16)
+    logits = torch.from_numpy(synth.router_logits(seed, wl)).to(dev)
+    layer = RoutedExpertLayer(wl.E, wl.H, wl.I, wl.k, wl.T, dev)
+    for _ in range(2):
+        layer(x, logits, pool)
+    torch.cuda.synchronize()
+    offs = layer.grp.expert_offsets.cpu().numpy()
+    touched = int((np.diff(offs) > 0).sum())
+    stream = torch.cuda.current_stream(dev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        layer(x, logits, pool)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    flops = 2.0 * wl.R * 3 * wl.H * wl.I
+    tflops = flops / (ms * 1e-3) / 1e12
+    bytes_touched = touched * synth.slab_bytes(wl.H, wl.I)
+    floor_ms = max(bytes_touched / (HBM_PEAK_GBS * 1e9), flops / (FP4_PEAK_TFLOPS * 1e12)) * 1e3
+    log(f"prefill512: {ms:.3f} ms/layer, {tflops:.1f} TFLOP/s, {touched} experts touched")
+    return {"ms_per_layer": round(ms, 4), "tflops": round(tflops, 2), "frac_fp4_peak": round(tflops / FP4_PEAK_TFLOPS, 4),
+            "experts_touched": touched, "binding_floor_ms": round(floor_ms, 4),
+            "frac_binding_roofline": round(floor_ms / ms, 4)}
+
+
+def cpu_baseline(args, wl):
+    """The CPU oracle (as it stands) on the host cores: whole decode896 layers
+    for successive variants until about --cpu-seconds have passed."""
+    import numpy as np
+
+    import oracle
+    from mxfp4_routed_expert_02_amd import synth
+
+    threads = max(1, min(args.cpu_threads, os.cpu_count() or 1))
+    done, t_acc, nbytes = 0, 0.0, 0
+    v = 0
+    while t_acc < args.cpu_seconds and v < args.variants:
+        x = synth.activations_bf16(args.seed, wl, variant=v)
+        logits = synth.router_logits(args.seed, wl, variant=v)
+        ids, _ = oracle.route_topk(logits, wl.k)
+        sb = synth.slab_bytes(wl.H, wl.I)
+        slabs = np.zeros((wl.E, sb), np.uint8)
+        for e in ids.reshape(-1):
+            synth.expert_slabs(args.seed, wl.pool, 0, int(e), 1, wl.H, wl.I, out=slabs[e:e + 1])
+        hp = oracle.Pool(slabs, wl.H, wl.I)
+        t = time.perf_counter()
+        oracle.layer(x, logits, wl.k, hp, nthreads=threads)
+        t_acc += time.perf_counter() - t
+        nbytes += wl.T * wl.k * sb
+        done += 1
+        v += 1
+    gbs = nbytes / t_acc / 1e9
+    log(f"cpu oracle: {done} decode896 layers in {t_acc:.1f} s on {threads} threads, {gbs:.3f} GB/s")
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} whole decode896 layers (1 token, 16 of 896 experts each, variants 0..{done - 1}), "
+                      f"{t_acc:.1f} s of oracle time"}
+
+
+if __name__ == "__main__":
+    main()

@@ -9,23 +9,34 @@
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kCombineThreads = 64;
 
-__global__ __launch_bounds__(kThreads) void combine_vec4_kernel(const float* __restrict__ y_rows,
-                                                                const float* __restrict__ w,
-                                                                const int32_t* __restrict__ row_pos, int k,
-                                                                int H, int nck, float* __restrict__ out) {
+// all k loads of a thread are issued before the sums (k <= 32, 8 at a time)
+__global__ __launch_bounds__(kCombineThreads) void combine_vec4_kernel(const float* __restrict__ y_rows,
+                                                                       const float* __restrict__ w,
+                                                                       const int32_t* __restrict__ row_pos, int k,
+                                                                       int H, int nck, float* __restrict__ out) {
   const int t = blockIdx.x / nck;
-  const int i = (blockIdx.x - t * nck) * kThreads + threadIdx.x;  // float4 index
+  const int i = (blockIdx.x - t * nck) * kCombineThreads + threadIdx.x;  // float4 index
   if (4 * i >= H) return;
+  const float* wt = w + (int64_t)t * k;
+  const int32_t* rp = row_pos + (int64_t)t * k;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
-    const float wt = w[(int64_t)t * k + j];
-    const int64_t p = row_pos[(int64_t)t * k + j];
-    const float4 y = ((const float4*)(y_rows + p * H))[i];
-    acc.x += wt * y.x;
-    acc.y += wt * y.y;
-    acc.z += wt * y.z;
-    acc.w += wt * y.w;
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    float4 y[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (j0 + u < k) y[u] = ((const float4*)(y_rows + (int64_t)rp[j0 + u] * H))[i];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (j0 + u < k) {
+        const float c = wt[j0 + u];
+        acc.x += c * y[u].x;
+        acc.y += c * y[u].y;
+        acc.z += c * y[u].z;
+        acc.w += c * y[u].w;
+      }
+    }
   }
   ((float4*)(out + (int64_t)t * H))[i] = acc;
 }
@@ -69,9 +80,9 @@ hipError_t launch_combine(const float* y_rows, const float* w, const int32_t* ro
                           float* out, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (H % 4 == 0) {
-    const int nck = (H / 4 + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL(combine_vec4_kernel, dim3((unsigned)T * nck), dim3(kThreads), 0, s, y_rows, w, row_pos, k,
-                       H, nck, out);
+    const int nck = (H / 4 + kCombineThreads - 1) / kCombineThreads;
+    hipLaunchKernelGGL(combine_vec4_kernel, dim3((unsigned)T * nck), dim3(kCombineThreads), 0, s, y_rows, w, row_pos,
+                       k, H, nck, out);
   } else {
     const int nck = (H + kThreads - 1) / kThreads;
     hipLaunchKernelGGL(combine_scalar_kernel, dim3((unsigned)T * nck), dim3(kThreads), 0, s, y_rows, w, row_pos,

@@ -13,6 +13,8 @@
 //          v_dot2_f32_bf16 against the bf16 activations (exact products,
 //          fp32 sums); the E8M0 scale multiplies each block's partial sum.
 // down:    E2M1 -> fp32 (exact) and fp32 FMA against the fp32 h rows.
+#include <climits>
+
 #include "moe_internal.h"
 
 namespace {
@@ -20,6 +22,11 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / MOE_WAVE;
 constexpr int kRowsPerBlock = 16;
+constexpr int kRegRows = 4;  // rows per expert the register path takes at once
+// row-group unroll of the kernels specialized for 224-block (H = 7168) and
+// 48-block (I = 1536) rows; the host grid uses the same constants
+constexpr int kGateU224 = 1;
+constexpr int kDownU48 = 2;
 
 // 16 bytes = 32 E2M1 codes -> 16 bf16 pairs; pair j holds elements 2j, 2j+1.
 __device__ __forceinline__ void dequant_bf16(const uint4 q, bf16x2_t (&v)[16]) {
@@ -74,12 +81,12 @@ __device__ __forceinline__ float chunk_dot_f32(const f32x2_t (&wv)[16], const fl
 }
 
 template <int MT>
-__global__ __launch_bounds__(kThreads) void gateup_gemv_kernel(const uint16_t* __restrict__ x, int k,
-                                                               moe_mxfp4_weights w,
-                                                               const int32_t* __restrict__ offsets,
-                                                               const int32_t* __restrict__ sorted_rows,
-                                                               const int32_t* __restrict__ active,
-                                                               float* __restrict__ h) {
+__global__ __launch_bounds__(kThreads) void gateup_gemv_lds_kernel(const uint16_t* __restrict__ x, int k,
+                                                                   moe_mxfp4_weights w,
+                                                                   const int32_t* __restrict__ offsets,
+                                                                   const int32_t* __restrict__ sorted_rows,
+                                                                   const int32_t* __restrict__ active,
+                                                                   float* __restrict__ h, int skip_upto) {
   extern __shared__ uint32_t s_x[];  // [MT][H/2] bf16 pairs
   const int slot = blockIdx.y;
   if (slot >= active[0]) return;
@@ -87,6 +94,7 @@ __global__ __launch_bounds__(kThreads) void gateup_gemv_kernel(const uint16_t* _
   const int e = active[1 + slot];
   const int p0 = offsets[e];
   const int cnt = offsets[e + 1] - p0;
+  if (cnt <= skip_upto) return;
   const int n0 = blockIdx.x * kRowsPerBlock;
   const int lane = threadIdx.x & (MOE_WAVE - 1), wave = threadIdx.x / MOE_WAVE;
   const int nb = H >> 5;
@@ -146,10 +154,10 @@ __global__ __launch_bounds__(kThreads) void gateup_gemv_kernel(const uint16_t* _
 }
 
 template <int MT>
-__global__ __launch_bounds__(kThreads) void down_gemv_kernel(const float* __restrict__ h, moe_mxfp4_weights w,
-                                                             const int32_t* __restrict__ offsets,
-                                                             const int32_t* __restrict__ active,
-                                                             float* __restrict__ y_rows) {
+__global__ __launch_bounds__(kThreads) void down_gemv_lds_kernel(const float* __restrict__ h, moe_mxfp4_weights w,
+                                                                 const int32_t* __restrict__ offsets,
+                                                                 const int32_t* __restrict__ active,
+                                                                 float* __restrict__ y_rows, int skip_upto) {
   extern __shared__ float s_h[];  // [MT][I]
   const int slot = blockIdx.y;
   if (slot >= active[0]) return;
@@ -157,6 +165,7 @@ __global__ __launch_bounds__(kThreads) void down_gemv_kernel(const float* __rest
   const int e = active[1 + slot];
   const int p0 = offsets[e];
   const int cnt = offsets[e + 1] - p0;
+  if (cnt <= skip_upto) return;
   const int n0 = blockIdx.x * kRowsPerBlock;
   const int lane = threadIdx.x & (MOE_WAVE - 1), wave = threadIdx.x / MOE_WAVE;
   const int nb = I >> 5;
@@ -201,12 +210,346 @@ __global__ __launch_bounds__(kThreads) void down_gemv_kernel(const float* __rest
   }
 }
 
+// ---------------------------------------------------------------------------
+// Register-resident GEMV (the decode path).  A wave owns P consecutive weight
+// rows per iteration, P*nb = 64*J chunks (nb = 32-value blocks per row): lane
+// l takes chunks c = 64j + l, i.e. row c / nb and block c % nb.  That block
+// index is the same in every iteration, so the lane keeps the J activation
+// blocks it needs in registers for the whole kernel and only weight bytes
+// stream from HBM; all of an iteration's loads are issued before any math.
+// Each row's partial sums are gathered by a wavefront butterfly.
+
+// 32 bf16 activations (4 x 16 B) against a dequantized chunk
+__device__ __forceinline__ float chunk_dot_bf16_reg(const bf16x2_t (&wv)[16], const uint4 (&xr)[4]) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc = dot2_bf16(wv[4 * i + 0], as_bf16x2(xr[i].x), acc);
+    acc = dot2_bf16(wv[4 * i + 1], as_bf16x2(xr[i].y), acc);
+    acc = dot2_bf16(wv[4 * i + 2], as_bf16x2(xr[i].z), acc);
+    acc = dot2_bf16(wv[4 * i + 3], as_bf16x2(xr[i].w), acc);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ float chunk_dot_f32_reg(const f32x2_t (&wv)[16], const float4 (&hr)[8]) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    acc += wv[2 * i].x * hr[i].x;
+    acc += wv[2 * i].y * hr[i].y;
+    acc += wv[2 * i + 1].x * hr[i].z;
+    acc += wv[2 * i + 1].y * hr[i].w;
+  }
+  return acc;
+}
+
+// Buffer resource over one expert matrix: loads past `bytes` return zero,
+// which masks the rows beyond the last one of a partial iteration.
+// log2 of the largest power of two (at most 64) dividing n
+__host__ __device__ constexpr int ctz_const(int n) {
+  return (n % 64 == 0) ? 6 : (n % 32 == 0) ? 5 : (n % 16 == 0) ? 4 : (n % 8 == 0) ? 3 : (n % 4 == 0) ? 2 : (n % 2 == 0) ? 1 : 0;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+__device__ __forceinline__ uint32_t load1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
+}
+
+// Lane layout: G = 2^lg lanes share one weight row (G divides nb, the row's
+// count of 32-value blocks) and lane l takes blocks (l % G) + G*j, j < J = nb/G,
+// of row l / G; a wave instruction covers 64/G rows and an iteration U such
+// row groups.  A row's partial sums then meet in log2(G) DPP steps, in the
+// group's last lane.
+// The activation row sits in LDS as planes of 16-byte sub-chunks (sub-chunk q
+// of block b at [q][b]), so consecutive lanes read consecutive 16 bytes, and
+// every block read from LDS serves all U rows of the iteration.
+//
+// grid: max_active * blocks_per_expert blocks of 4 waves; wave w of block b
+// of an expert runs row-iterations [(4b + w) * ipw, (4b + w + 1) * ipw).
+
+
+// Experts whose row count lies in [cnt_lo, cnt_hi] run here, MT rows at a
+// time: a weight chunk is loaded and dequantized once and applied to each of
+// the MT rows with exactly the arithmetic a single row gets, so a token's
+// result does not depend on how many other tokens share its experts.
+template <int J, int U, int MT, int NB>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void gateup_gemv_reg_kernel(
+    const uint16_t* __restrict__ x, int k, moe_mxfp4_weights w, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_rows, const int32_t* __restrict__ active, float* __restrict__ h, int lg_rt,
+    int ipw, int blocks_per_expert, int cnt_lo, int cnt_hi) {
+  extern __shared__ uint4 s_x4[];  // [MT][4][nb]
+  const int slot = blockIdx.x / blocks_per_expert;
+  if (slot >= active[0]) return;
+  const int e = active[1 + slot];
+  const int p0 = offsets[e];
+  const int cnt = offsets[e + 1] - p0;
+  if (cnt < cnt_lo || cnt > cnt_hi) return;
+  // NB > 0: the row's block count is a compile-time constant (so are the LDS
+  // and buffer offsets); NB == 0: taken from the weights at run time
+  const int I = w.inter, nb = NB > 0 ? NB : (w.hidden >> 5), H = 32 * nb;
+  const int lg = NB > 0 ? ctz_const(NB) : lg_rt;
+  const int lane = threadIdx.x & (MOE_WAVE - 1), wave = threadIdx.x / MOE_WAVE;
+  const int G = 1 << lg, rpi = MOE_WAVE >> lg, rows_it = rpi * U;
+  const int li = lane & (G - 1), gi = lane >> lg;
+  const int total_iters = (I + rows_it - 1) / rows_it;
+  const int it0 = ((blockIdx.x - slot * blocks_per_expert) * kWaves + wave) * ipw;
+  const int it1 = min(total_iters, it0 + ipw);
+  const uint32_t qrow = (uint32_t)H >> 1;
+  const int64_t eo = (int64_t)e * w.expert_stride;
+  const __amdgpu_buffer_rsrc_t rgq = make_rsrc(w.gate_q + eo, (uint32_t)I * qrow);
+  const __amdgpu_buffer_rsrc_t ruq = make_rsrc(w.up_q + eo, (uint32_t)I * qrow);
+  const __amdgpu_buffer_rsrc_t rgs = make_rsrc(w.gate_s + eo, (uint32_t)(I * nb));
+  const __amdgpu_buffer_rsrc_t rus = make_rsrc(w.up_s + eo, (uint32_t)(I * nb));
+  const uint32_t vq0 = (uint32_t)gi * qrow + 16u * li, vs0 = (uint32_t)(gi * nb + li);
+  const int plane = 4 * nb;  // uint4 per staged row
+  uint4 qg[U][J], qu[U][J];
+  uint32_t sg[U][J], su[U][J];
+  auto load_iter = [&](int it) {
+    const int n0 = it * rows_it;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t bq = (uint32_t)(n0 + u * rpi) * qrow, bs = (uint32_t)((n0 + u * rpi) * nb);
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        qg[u][j] = load16(rgq, vq0 + bq + 16u * G * j);
+        qu[u][j] = load16(ruq, vq0 + bq + 16u * G * j);
+        sg[u][j] = load1(rgs, vs0 + bs + G * j);
+        su[u][j] = load1(rus, vs0 + bs + G * j);
+      }
+    }
+  };
+  for (int m0 = 0; m0 < cnt; m0 += MT) {
+    const int mt = min(MT, cnt - m0);
+    __syncthreads();
+    for (int i = threadIdx.x; i < mt * plane; i += kThreads) {
+      const int m = i / plane, c = i - m * plane;
+      const int64_t t = sorted_rows[p0 + m0 + m] / k;
+      s_x4[m * plane + (c & 3) * nb + (c >> 2)] = ((const uint4*)(x + t * H))[c];
+    }
+    __syncthreads();
+    for (int it = it0; it < it1; ++it) {
+      const int n0 = it * rows_it;
+      load_iter(it);
+      float ag[U][MT], au[U][MT];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) ag[u][m] = au[u][m] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        if (MT == 1) {
+          // one row: one activation block read, gate and up chunks in turn
+          uint4 xr[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) xr[q] = s_x4[q * nb + li + G * j];
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            bf16x2_t wv[16];
+            dequant_bf16(qg[u][j], wv);
+            ag[u][0] += chunk_dot_bf16_reg(wv, xr) * e8m0_to_f32(sg[u][j]);
+            dequant_bf16(qu[u][j], wv);
+            au[u][0] += chunk_dot_bf16_reg(wv, xr) * e8m0_to_f32(su[u][j]);
+          }
+        } else {
+          // several rows: each chunk is dequantized once and serves every row
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            bf16x2_t wg[16], wu[16];
+            dequant_bf16(qg[u][j], wg);
+            dequant_bf16(qu[u][j], wu);
+            const float fg = e8m0_to_f32(sg[u][j]), fu = e8m0_to_f32(su[u][j]);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+              if (m < mt) {
+                uint4 xr[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) xr[q] = s_x4[m * plane + q * nb + li + G * j];
+                ag[u][m] += chunk_dot_bf16_reg(wg, xr) * fg;
+                au[u][m] += chunk_dot_bf16_reg(wu, xr) * fu;
+              }
+            }
+          }
+        }
+        // keeps the scheduler from hoisting every LDS read (and its registers)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int n = n0 + u * rpi + gi;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          if (m < mt) {
+            const float g = group_sum_last(ag[u][m], G);
+            const float uu = group_sum_last(au[u][m], G);
+            if (li == G - 1 && n < I) h[(int64_t)(p0 + m0 + m) * I + n] = silu_mul(g, uu);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int J, int U, int MT, int NB>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void down_gemv_reg_kernel(
+    const float* __restrict__ h, moe_mxfp4_weights w, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ active, float* __restrict__ y_rows, int lg_rt, int ipw, int blocks_per_expert,
+    int cnt_lo, int cnt_hi) {
+  extern __shared__ float4 s_h4[];  // [MT][8][nb]
+  const int slot = blockIdx.x / blocks_per_expert;
+  if (slot >= active[0]) return;
+  const int e = active[1 + slot];
+  const int p0 = offsets[e];
+  const int cnt = offsets[e + 1] - p0;
+  if (cnt < cnt_lo || cnt > cnt_hi) return;
+  const int H = w.hidden, nb = NB > 0 ? NB : (w.inter >> 5), I = 32 * nb;
+  const int lg = NB > 0 ? ctz_const(NB) : lg_rt;
+  const int lane = threadIdx.x & (MOE_WAVE - 1), wave = threadIdx.x / MOE_WAVE;
+  const int G = 1 << lg, rpi = MOE_WAVE >> lg, rows_it = rpi * U;
+  const int li = lane & (G - 1), gi = lane >> lg;
+  const int total_iters = (H + rows_it - 1) / rows_it;
+  const int it0 = ((blockIdx.x - slot * blocks_per_expert) * kWaves + wave) * ipw;
+  const int it1 = min(total_iters, it0 + ipw);
+  const uint32_t qrow = (uint32_t)I >> 1;
+  const int64_t eo = (int64_t)e * w.expert_stride;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(w.down_q + eo, (uint32_t)H * qrow);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(w.down_s + eo, (uint32_t)(H * nb));
+  const uint32_t vq0 = (uint32_t)gi * qrow + 16u * li, vs0 = (uint32_t)(gi * nb + li);
+  const int plane = 8 * nb;  // float4 per staged row
+  uint4 q[U][J];
+  uint32_t sc[U][J];
+  auto load_iter = [&](int it) {
+    const int n0 = it * rows_it;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t bq = (uint32_t)(n0 + u * rpi) * qrow, bs = (uint32_t)((n0 + u * rpi) * nb);
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        q[u][j] = load16(rq, vq0 + bq + 16u * G * j);
+        sc[u][j] = load1(rs, vs0 + bs + G * j);
+      }
+    }
+  };
+  for (int m0 = 0; m0 < cnt; m0 += MT) {
+    const int mt = min(MT, cnt - m0);
+    __syncthreads();
+    for (int i = threadIdx.x; i < mt * plane; i += kThreads) {
+      const int m = i / plane, c = i - m * plane;
+      s_h4[m * plane + (c & 7) * nb + (c >> 3)] = ((const float4*)(h + (int64_t)(p0 + m0 + m) * I))[c];
+    }
+    __syncthreads();
+    for (int it = it0; it < it1; ++it) {
+      const int n0 = it * rows_it;
+      load_iter(it);
+      float acc[U][MT];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[u][m] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        if (MT == 1) {
+          // one row: each h block read from LDS serves all U weight rows
+          float4 hr[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) hr[i] = s_h4[i * nb + li + G * j];
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            f32x2_t wv[16];
+            dequant_f32(q[u][j], wv);
+            acc[u][0] += chunk_dot_f32_reg(wv, hr) * e8m0_to_f32(sc[u][j]);
+            __builtin_amdgcn_sched_barrier(0);  // one dequantized chunk live at a time
+          }
+        } else {
+          // several rows: each chunk is dequantized once and serves every row
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            f32x2_t wv[16];
+            dequant_f32(q[u][j], wv);
+            const float f = e8m0_to_f32(sc[u][j]);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+              if (m < mt) {
+                float4 hr[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) hr[i] = s_h4[m * plane + i * nb + li + G * j];
+                acc[u][m] += chunk_dot_f32_reg(wv, hr) * f;
+              }
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int n = n0 + u * rpi + gi;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          if (m < mt) {
+            const float v = group_sum_last(acc[u][m], G);
+            if (li == G - 1 && n < H) y_rows[(int64_t)(p0 + m0 + m) * H + n] = v;
+          }
+        }
+      }
+    }
+  }
+}
+
 constexpr size_t kMaxLds = 65536;
 
 int pick_mt(size_t bytes_per_row) {
   if (4 * bytes_per_row <= kMaxLds) return 4;
   if (2 * bytes_per_row <= kMaxLds) return 2;
   return 1;
+}
+
+// Lane layout of the register GEMV for rows of nb blocks: G = 2^lg lanes per
+// row with G the largest power of two (at most 64) dividing nb, J = nb / G
+// blocks per lane, U row groups per iteration (loads in flight per lane =
+// U * J for down, 2 * U * J for gate/up).  J above 8 takes the LDS path.
+struct GemvShape {
+  bool ok;
+  int lg, J, U;
+};
+
+GemvShape gemv_shape(int nb, bool gateup) {
+  int lg = 0;
+  while (lg < 6 && (nb % (2 << lg)) == 0) ++lg;
+  const int J = nb >> lg;
+  if (J > 8) return {false, 0, 0, 0};
+  if (gateup && nb == 224) return {true, lg, J, kGateU224};
+  if (!gateup && nb == 48) return {true, lg, J, kDownU48};
+  int U;
+  if (gateup)
+    U = J == 1 ? 4 : (J <= 3 ? 2 : 1);
+  else
+    U = J == 1 ? 8 : (J == 2 ? 4 : (J == 3 ? 4 : (J == 4 ? 2 : 1)));
+  return {true, lg, J, U};
+}
+
+struct GemvGrid {
+  int ipw;                // row-iterations per wave
+  int blocks_per_expert;  // blocks of 4 waves per active-expert slot
+};
+
+// About 8 waves per CU (two per SIMD, one round) over 256 CUs for the upper
+// bound of active experts, and at least 8 blocks per expert so that a few
+// busy experts still spread.
+GemvGrid gemv_grid(int iters_per_expert, int max_active) {
+  const long total = (long)iters_per_expert * max_active;
+  int ipw = (int)((total + 2047) / 2048);
+  const int cap = (iters_per_expert + 31) / 32;
+  if (ipw > cap) ipw = cap;
+  if (ipw < 1) ipw = 1;
+  const int bpe = (iters_per_expert + kWaves * ipw - 1) / (kWaves * ipw);
+  return {ipw, bpe};
 }
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -228,32 +571,117 @@ hipError_t launch_expert_ffn(const uint16_t* x, int T, int k, const moe_mxfp4_we
   const int R = T * k, E = w.num_experts, H = w.hidden, I = w.inter;
   const int max_active = R < E ? R : E;
   float* hbuf = (float*)ws;
+  // One token: every expert runs on the register path (its token loop also
+  // covers an id repeated within the token).  Several tokens: single-row
+  // experts take the register path, the others the LDS path.
+  const GemvShape sg = gemv_shape(H >> 5, true), sd = gemv_shape(I >> 5, false);
+  const bool reg_g = sg.ok, reg_d = sd.ok;
+  // Register path: experts with one row (MT = 1) and with 2..kRegRows rows
+  // (MT = kRegRows, same per-row arithmetic); a single token sends every
+  // expert through MT = 1 (its row loop covers an id repeated in the token).
+  // Experts with more rows take the LDS path.
 
-  const int mt_g = pick_mt((size_t)H * 2);
-  dim3 grid_g((I + kRowsPerBlock - 1) / kRowsPerBlock, max_active);
-  const size_t lds_g = (size_t)mt_g * H * 2;
-  if (mt_g == 4)
-    hipLaunchKernelGGL(gateup_gemv_kernel<4>, grid_g, dim3(kThreads), lds_g, s, x, k, w, offsets, sorted_rows,
-                       active, hbuf);
-  else if (mt_g == 2)
-    hipLaunchKernelGGL(gateup_gemv_kernel<2>, grid_g, dim3(kThreads), lds_g, s, x, k, w, offsets, sorted_rows,
-                       active, hbuf);
-  else
-    hipLaunchKernelGGL(gateup_gemv_kernel<1>, grid_g, dim3(kThreads), lds_g, s, x, k, w, offsets, sorted_rows,
-                       active, hbuf);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  hipError_t err = hipSuccess;
+  if (reg_g) {
+    const int rows_it = (64 >> sg.lg) * sg.U;
+    GemvGrid gg = gemv_grid((I + rows_it - 1) / rows_it, max_active);
+    const dim3 g(max_active * gg.blocks_per_expert), b(kThreads);
+#define GU_REG(JJ, UU, MM, LO, HI)                                                                                \
+  hipLaunchKernelGGL((gateup_gemv_reg_kernel<JJ, UU, MM, 0>), g, b, (size_t)MM * H * 2, s, x, k, w, offsets,     \
+                     sorted_rows, active, hbuf, sg.lg, gg.ipw, gg.blocks_per_expert, LO, HI)
+#define GU_ALL(MM, LO, HI)                                                                                    \
+  if (H == 7168) {                                                                                            \
+    hipLaunchKernelGGL((gateup_gemv_reg_kernel<7, kGateU224, MM, 224>), g, b, (size_t)MM * H * 2, s, x, k, w, offsets, \
+                       sorted_rows, active, hbuf, sg.lg, gg.ipw, gg.blocks_per_expert, LO, HI);               \
+  } else                                    \
+  switch (sg.J) {                           \
+    case 1: GU_REG(1, 4, MM, LO, HI); break; \
+    case 2: GU_REG(2, 2, MM, LO, HI); break; \
+    case 3: GU_REG(3, 2, MM, LO, HI); break; \
+    case 4: GU_REG(4, 1, MM, LO, HI); break; \
+    case 5: GU_REG(5, 1, MM, LO, HI); break; \
+    case 6: GU_REG(6, 1, MM, LO, HI); break; \
+    case 7: GU_REG(7, 1, MM, LO, HI); break; \
+    default: GU_REG(8, 1, MM, LO, HI); break; \
+  }
+    if (T == 1) {
+      GU_ALL(1, 1, INT32_MAX)
+    } else {
+      GU_ALL(1, 1, 1)
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+      GU_ALL(kRegRows, 2, kRegRows)
+    }
+#undef GU_ALL
+#undef GU_REG
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (!reg_g || T > 1) {
+    const int mt_g = pick_mt((size_t)H * 2);
+    dim3 grid_g((I + kRowsPerBlock - 1) / kRowsPerBlock, max_active);
+    const size_t lds_g = (size_t)mt_g * H * 2;
+    const int skip = reg_g ? kRegRows : 0;
+    if (mt_g == 4)
+      hipLaunchKernelGGL(gateup_gemv_lds_kernel<4>, grid_g, dim3(kThreads), lds_g, s, x, k, w, offsets, sorted_rows,
+                         active, hbuf, skip);
+    else if (mt_g == 2)
+      hipLaunchKernelGGL(gateup_gemv_lds_kernel<2>, grid_g, dim3(kThreads), lds_g, s, x, k, w, offsets, sorted_rows,
+                         active, hbuf, skip);
+    else
+      hipLaunchKernelGGL(gateup_gemv_lds_kernel<1>, grid_g, dim3(kThreads), lds_g, s, x, k, w, offsets, sorted_rows,
+                         active, hbuf, skip);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
 
-  const int mt_d = pick_mt((size_t)I * 4);
-  dim3 grid_d((H + kRowsPerBlock - 1) / kRowsPerBlock, max_active);
-  const size_t lds_d = (size_t)mt_d * I * 4;
-  if (mt_d == 4)
-    hipLaunchKernelGGL(down_gemv_kernel<4>, grid_d, dim3(kThreads), lds_d, s, hbuf, w, offsets, active, y_rows);
-  else if (mt_d == 2)
-    hipLaunchKernelGGL(down_gemv_kernel<2>, grid_d, dim3(kThreads), lds_d, s, hbuf, w, offsets, active, y_rows);
-  else
-    hipLaunchKernelGGL(down_gemv_kernel<1>, grid_d, dim3(kThreads), lds_d, s, hbuf, w, offsets, active, y_rows);
-  return hipGetLastError();
+  if (reg_d) {
+    const int rows_it = (64 >> sd.lg) * sd.U;
+    GemvGrid gd = gemv_grid((H + rows_it - 1) / rows_it, max_active);
+    const dim3 g(max_active * gd.blocks_per_expert), b(kThreads);
+#define DN_REG(JJ, UU, MM, LO, HI)                                                                                  \
+  hipLaunchKernelGGL((down_gemv_reg_kernel<JJ, UU, MM, 0>), g, b, (size_t)MM * I * 4, s, hbuf, w, offsets, active, \
+                     y_rows, sd.lg, gd.ipw, gd.blocks_per_expert, LO, HI)
+#define DN_ALL(MM, LO, HI)                                                                                          \
+  if (I == 1536) {                                                                                                  \
+    hipLaunchKernelGGL((down_gemv_reg_kernel<3, kDownU48, MM, 48>), g, b, (size_t)MM * I * 4, s, hbuf, w, offsets, active, \
+                       y_rows, sd.lg, gd.ipw, gd.blocks_per_expert, LO, HI);                                        \
+  } else                                    \
+  switch (sd.J) {                           \
+    case 1: DN_REG(1, 8, MM, LO, HI); break; \
+    case 2: DN_REG(2, 4, MM, LO, HI); break; \
+    case 3: DN_REG(3, 4, MM, LO, HI); break; \
+    case 4: DN_REG(4, 2, MM, LO, HI); break; \
+    case 5: DN_REG(5, 1, MM, LO, HI); break; \
+    case 6: DN_REG(6, 1, MM, LO, HI); break; \
+    case 7: DN_REG(7, 1, MM, LO, HI); break; \
+    default: DN_REG(8, 1, MM, LO, HI); break; \
+  }
+    if (T == 1) {
+      DN_ALL(1, 1, INT32_MAX)
+    } else {
+      DN_ALL(1, 1, 1)
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+      DN_ALL(kRegRows, 2, kRegRows)
+    }
+#undef DN_ALL
+#undef DN_REG
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (!reg_d || T > 1) {
+    const int mt_d = pick_mt((size_t)I * 4);
+    dim3 grid_d((H + kRowsPerBlock - 1) / kRowsPerBlock, max_active);
+    const size_t lds_d = (size_t)mt_d * I * 4;
+    const int skip = reg_d ? kRegRows : 0;
+    if (mt_d == 4)
+      hipLaunchKernelGGL(down_gemv_lds_kernel<4>, grid_d, dim3(kThreads), lds_d, s, hbuf, w, offsets, active, y_rows,
+                         skip);
+    else if (mt_d == 2)
+      hipLaunchKernelGGL(down_gemv_lds_kernel<2>, grid_d, dim3(kThreads), lds_d, s, hbuf, w, offsets, active, y_rows,
+                         skip);
+    else
+      hipLaunchKernelGGL(down_gemv_lds_kernel<1>, grid_d, dim3(kThreads), lds_d, s, hbuf, w, offsets, active, y_rows,
+                         skip);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 }  // namespace moe

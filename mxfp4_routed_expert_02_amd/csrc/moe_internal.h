@@ -46,6 +46,40 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// DPP lane moves (GFX9 encodings): row_shr:n = 0x110 + n, row_bcast:15 =
+// 0x142, row_bcast:31 = 0x143.  Lanes without a source read 0.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Sum over each aligned group of G lanes (G a power of two, 1..64, uniform);
+// the total lands in the last lane of the group (other lanes hold partials).
+__device__ __forceinline__ float group_sum_last(float v, int G) {
+  if (G >= 2) v += dpp_f32<0x111>(v);
+  if (G >= 4) v += dpp_f32<0x112>(v);
+  if (G >= 8) v += dpp_f32<0x114>(v);
+  if (G >= 16) v += dpp_f32<0x118>(v);
+  if (G >= 32) v += dpp_f32<0x142, 0xA>(v);
+  if (G >= 64) v += dpp_f32<0x143, 0xC>(v);
+  return v;
+}
+
+// Maximum over the wave (unsigned), valid in lane 63.
+__device__ __forceinline__ uint32_t wave_max_u32_last(uint32_t v) {
+  v = max(v, dpp_u32<0x111>(v));
+  v = max(v, dpp_u32<0x112>(v));
+  v = max(v, dpp_u32<0x114>(v));
+  v = max(v, dpp_u32<0x118>(v));
+  v = max(v, dpp_u32<0x142, 0xA>(v));
+  v = max(v, dpp_u32<0x143, 0xC>(v));
+  return v;
+}
+
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne_dev(float f) {

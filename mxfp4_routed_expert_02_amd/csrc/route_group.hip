@@ -1,10 +1,11 @@
 // route_group.hip - router top-k and expert-major row grouping (gfx950).
 //
-// Top-k: one wavefront per token.  The token's logits sit in LDS; each of
-// the k rounds is a wavefront arg-max over the experts not yet taken (lane
-// scan, then a butterfly of (value, id) pairs: larger value wins, equal
-// values go to the lower id), so the ids come out in rank order.  The
-// softmax over the k picked logits runs in one lane in rank order.
+// Top-k: one wavefront per token; each of the k rounds is a wavefront
+// arg-max over the experts not yet taken (larger value wins, equal values go
+// to the lower id), so the ids come out in rank order.  Up to 2048 experts
+// the logits stay in registers (ordered keys, wave max + ballot); beyond
+// that they sit in LDS.  The softmax over the k picked logits runs in one
+// lane in rank order.
 //
 // Grouping: a stable counting sort of the flat rows r = t*k + j by expert.
 // Counts and OR-ed bitmaps are the only LDS atomics (both order-free), so
@@ -63,6 +64,66 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float* 
     float S = 0.0f;
     for (int j = 0; j < k; ++j) {
       const float ex = expf(s_val[j] - m);
+      s_val[j] = ex;
+      S += ex;
+    }
+    for (int j = 0; j < k; ++j) weights[(int64_t)t * k + j] = s_val[j] / S;
+  }
+}
+
+// Register variant: lane l holds the C logits of experts l*C .. l*C+C-1 as
+// order-preserving unsigned keys (0 = taken or absent), so the lowest lane
+// holding the wave maximum also holds the lowest id among equal values.
+__device__ __forceinline__ uint32_t order_key(float v) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;  // -0 ranks equal to +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int C>
+__global__ __launch_bounds__(kRouteThreads) void route_topk_reg_kernel(const float* __restrict__ logits, int E,
+                                                                       int k, int32_t* __restrict__ ids,
+                                                                       float* __restrict__ weights) {
+  __shared__ float s_val[MOE_MAX_TOPK];
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x;
+  const float* row = logits + (int64_t)t * E;
+  uint32_t key[C];
+#pragma unroll
+  for (int i = 0; i < C; ++i) {
+    const int e = lane * C + i;
+    key[i] = e < E ? order_key(row[e]) : 0u;
+  }
+  for (int j = 0; j < k; ++j) {
+    uint32_t bk = 0u;
+    int bi = 0;
+#pragma unroll
+    for (int i = 0; i < C; ++i)
+      if (key[i] > bk) {  // strict: the lowest slot wins a tie inside the lane
+        bk = key[i];
+        bi = i;
+      }
+    const uint32_t m = (uint32_t)__builtin_amdgcn_readlane((int)wave_max_u32_last(bk), 63);
+    const uint64_t hit = __ballot(bk == m);
+    const int win = __ffsll((unsigned long long)hit) - 1;
+    const int slot = __builtin_amdgcn_readlane(bi, win);
+    const int id = win * C + slot;
+    if (lane == win) {
+#pragma unroll
+      for (int i = 0; i < C; ++i)
+        if (i == slot) key[i] = 0u;
+    }
+    if (lane == 0) {
+      ids[(int64_t)t * k + j] = id;
+      s_val[j] = __uint_as_float((m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m);  // key -> value
+    }
+  }
+  __syncthreads();
+  if (lane == 0) {
+    const float mx = s_val[0];
+    float S = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const float ex = expf(s_val[j] - mx);
       s_val[j] = ex;
       S += ex;
     }
@@ -194,14 +255,101 @@ __global__ __launch_bounds__(kGroupThreads) void group_rows_kernel(const int32_t
   }
 }
 
+// Grouping for few rows (R <= kSmallRows): one block; counts by LDS
+// histogram, one scan of (flag << 32 | count) pairs, and each row's rank
+// among the earlier rows of its expert by direct comparison.
+constexpr int kSmallRows = 512;
+constexpr int kSmallThreads = 512;
+
+__global__ __launch_bounds__(kSmallThreads) void group_rows_small_kernel(const int32_t* __restrict__ ids, int R,
+                                                                         int E, int32_t* __restrict__ offsets,
+                                                                         int32_t* __restrict__ sorted_rows,
+                                                                         int32_t* __restrict__ row_pos,
+                                                                         int32_t* __restrict__ active) {
+  extern __shared__ uint64_t s_pair[];  // [E] (flag << 32) | count, then their exclusive scan
+  __shared__ int s_ids[kSmallRows];
+  __shared__ uint64_t s_wave[kSmallThreads / 64 + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < E; e += kSmallThreads) s_pair[e] = 0ull;
+  int my = -1;
+  if (tid < R) {
+    my = ids[tid];
+    s_ids[tid] = my;
+  }
+  __syncthreads();
+  if ((unsigned)my < (unsigned)E) atomicAdd((unsigned long long*)&s_pair[my], 1ull);
+  __syncthreads();
+  const int per = (E + kSmallThreads - 1) / kSmallThreads;
+  const int beg = min(E, tid * per), end = min(E, beg + per);
+  uint64_t local = 0;
+  for (int i = beg; i < end; ++i) {
+    const uint64_t c = s_pair[i];
+    local += (c ? (1ull << 32) : 0ull) + c;
+  }
+  uint64_t v = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint64_t u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  if (lane == 63) s_wave[wave] = v;
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t acc = 0;
+    for (int w = 0; w < kSmallThreads / 64; ++w) {
+      const uint64_t c = s_wave[w];
+      s_wave[w] = acc;
+      acc += c;
+    }
+    s_wave[kSmallThreads / 64] = acc;
+  }
+  __syncthreads();
+  uint64_t run = s_wave[wave] + v - local;
+  for (int i = beg; i < end; ++i) {
+    const uint64_t c = s_pair[i];
+    offsets[i] = (int32_t)(run & 0xFFFFFFFFull);
+    if (c) active[1 + (int)(run >> 32)] = i;
+    s_pair[i] = run;
+    run += (c ? (1ull << 32) : 0ull) + c;
+  }
+  if (tid == 0) {
+    const uint64_t tot = s_wave[kSmallThreads / 64];
+    offsets[E] = (int32_t)(tot & 0xFFFFFFFFull);
+    active[0] = (int32_t)(tot >> 32);
+  }
+  __syncthreads();
+  if ((unsigned)my < (unsigned)E) {
+    int rank = 0;
+    for (int r = 0; r < tid; ++r) rank += (s_ids[r] == my);
+    const int pos = (int)(s_pair[my] & 0xFFFFFFFFull) + rank;
+    sorted_rows[pos] = tid;
+    row_pos[tid] = pos;
+  }
+}
+
 }  // namespace
 
 namespace moe {
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const size_t lds = (size_t)E * sizeof(float) + (size_t)((E + 31) / 32) * sizeof(uint32_t);
-  hipLaunchKernelGGL(route_topk_kernel, dim3(T), dim3(kRouteThreads), lds, s, logits, E, k, ids, w);
+  const dim3 g(T), b(kRouteThreads);
+  if (E <= 64 * 1)
+    hipLaunchKernelGGL(route_topk_reg_kernel<1>, g, b, 0, s, logits, E, k, ids, w);
+  else if (E <= 64 * 2)
+    hipLaunchKernelGGL(route_topk_reg_kernel<2>, g, b, 0, s, logits, E, k, ids, w);
+  else if (E <= 64 * 4)
+    hipLaunchKernelGGL(route_topk_reg_kernel<4>, g, b, 0, s, logits, E, k, ids, w);
+  else if (E <= 64 * 8)
+    hipLaunchKernelGGL(route_topk_reg_kernel<8>, g, b, 0, s, logits, E, k, ids, w);
+  else if (E <= 64 * 16)
+    hipLaunchKernelGGL(route_topk_reg_kernel<16>, g, b, 0, s, logits, E, k, ids, w);
+  else if (E <= 64 * 32)
+    hipLaunchKernelGGL(route_topk_reg_kernel<32>, g, b, 0, s, logits, E, k, ids, w);
+  else {
+    const size_t lds = (size_t)E * sizeof(float) + (size_t)((E + 31) / 32) * sizeof(uint32_t);
+    hipLaunchKernelGGL(route_topk_kernel, g, b, lds, s, logits, E, k, ids, w);
+  }
   return hipGetLastError();
 }
 
@@ -216,6 +364,11 @@ hipError_t launch_group_rows(const int32_t* ids, int T, int k, int E, int32_t* o
                              int32_t* row_pos, int32_t* active, void* ws, hipStream_t s) {
   (void)ws;
   const int R = T * k;
+  if (R <= kSmallRows) {
+    hipLaunchKernelGGL(group_rows_small_kernel, dim3(1), dim3(kSmallThreads), (size_t)8 * E, s, ids, R, E, offsets,
+                       sorted_rows, row_pos, active);
+    return hipGetLastError();
+  }
   const size_t lds = (size_t)8 * E + (size_t)4 * E * group_words(E);
   hipLaunchKernelGGL(group_rows_kernel, dim3(1), dim3(kGroupThreads), lds, s, ids, R, E, offsets, sorted_rows,
                      row_pos, active);
