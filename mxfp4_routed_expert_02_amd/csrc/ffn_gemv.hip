@@ -539,12 +539,13 @@ struct GemvGrid {
   int blocks_per_expert;  // blocks of 4 waves per active-expert slot
 };
 
-// About 8 waves per CU (two per SIMD, one round) over 256 CUs for the upper
-// bound of active experts, and at least 8 blocks per expert so that a few
-// busy experts still spread.
-GemvGrid gemv_grid(int iters_per_expert, int max_active) {
+// One round of resident waves (waves_per_simd on each of the 1024 SIMDs) for
+// the upper bound of active experts, and at least 8 blocks per expert so that
+// a few busy experts still spread.
+GemvGrid gemv_grid(int iters_per_expert, int max_active, int waves_per_simd) {
   const long total = (long)iters_per_expert * max_active;
-  int ipw = (int)((total + 2047) / 2048);
+  const long slots = 1024L * waves_per_simd;
+  int ipw = (int)((total + slots - 1) / slots);
   const int cap = (iters_per_expert + 31) / 32;
   if (ipw > cap) ipw = cap;
   if (ipw < 1) ipw = 1;
@@ -584,7 +585,7 @@ hipError_t launch_expert_ffn(const uint16_t* x, int T, int k, const moe_mxfp4_we
   hipError_t err = hipSuccess;
   if (reg_g) {
     const int rows_it = (64 >> sg.lg) * sg.U;
-    GemvGrid gg = gemv_grid((I + rows_it - 1) / rows_it, max_active);
+    GemvGrid gg = gemv_grid((I + rows_it - 1) / rows_it, max_active, H == 7168 ? 4 : 2);
     const dim3 g(max_active * gg.blocks_per_expert), b(kThreads);
 #define GU_REG(JJ, UU, MM, LO, HI)                                                                                \
   hipLaunchKernelGGL((gateup_gemv_reg_kernel<JJ, UU, MM, 0>), g, b, (size_t)MM * H * 2, s, x, k, w, offsets,     \
@@ -634,7 +635,7 @@ hipError_t launch_expert_ffn(const uint16_t* x, int T, int k, const moe_mxfp4_we
 
   if (reg_d) {
     const int rows_it = (64 >> sd.lg) * sd.U;
-    GemvGrid gd = gemv_grid((H + rows_it - 1) / rows_it, max_active);
+    GemvGrid gd = gemv_grid((H + rows_it - 1) / rows_it, max_active, I == 1536 ? 3 : 2);
     const dim3 g(max_active * gd.blocks_per_expert), b(kThreads);
 #define DN_REG(JJ, UU, MM, LO, HI)                                                                                  \
   hipLaunchKernelGGL((down_gemv_reg_kernel<JJ, UU, MM, 0>), g, b, (size_t)MM * I * 4, s, hbuf, w, offsets, active, \

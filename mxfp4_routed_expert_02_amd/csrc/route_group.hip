@@ -84,7 +84,6 @@ template <int C>
 __global__ __launch_bounds__(kRouteThreads) void route_topk_reg_kernel(const float* __restrict__ logits, int E,
                                                                        int k, int32_t* __restrict__ ids,
                                                                        float* __restrict__ weights) {
-  __shared__ float s_val[MOE_MAX_TOPK];
   const int t = blockIdx.x;
   const int lane = threadIdx.x;
   const float* row = logits + (int64_t)t * E;
@@ -94,6 +93,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_reg_kernel(const flo
     const int e = lane * C + i;
     key[i] = e < E ? order_key(row[e]) : 0u;
   }
+  // round j leaves the pick's id and logit in lane j
+  int my_id = 0;
+  float my_val = 0.0f;
   for (int j = 0; j < k; ++j) {
     uint32_t bk = 0u;
     int bi = 0;
@@ -107,27 +109,24 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_reg_kernel(const flo
     const uint64_t hit = __ballot(bk == m);
     const int win = __ffsll((unsigned long long)hit) - 1;
     const int slot = __builtin_amdgcn_readlane(bi, win);
-    const int id = win * C + slot;
     if (lane == win) {
 #pragma unroll
       for (int i = 0; i < C; ++i)
         if (i == slot) key[i] = 0u;
     }
-    if (lane == 0) {
-      ids[(int64_t)t * k + j] = id;
-      s_val[j] = __uint_as_float((m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m);  // key -> value
+    if (lane == j) {
+      my_id = win * C + slot;
+      my_val = __uint_as_float((m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m);  // key -> value
     }
   }
-  __syncthreads();
-  if (lane == 0) {
-    const float mx = s_val[0];
-    float S = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const float ex = expf(s_val[j] - mx);
-      s_val[j] = ex;
-      S += ex;
-    }
-    for (int j = 0; j < k; ++j) weights[(int64_t)t * k + j] = s_val[j] / S;
+  // softmax over the k picks: exponentials in parallel, the sum in rank order
+  const float mx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_val), 0));
+  const float ex = lane < k ? expf(my_val - mx) : 0.0f;
+  float S = 0.0f;
+  for (int j = 0; j < k; ++j) S += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
+  if (lane < k) {
+    ids[(int64_t)t * k + lane] = my_id;
+    weights[(int64_t)t * k + lane] = ex / S;
   }
 }
 
