@@ -43,7 +43,45 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="bounded oracle sample (0 = skip)")
     p.add_argument("--cpu-threads", type=int, default=16)
     p.add_argument("--prefill-reps", type=int, default=10, help="prefill512 side measurement (0 = skip)")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="only run a plain device copy of this many MiB 5 times (calibrates HBM byte counters)")
     return p.parse_args()
+
+
+def profiled_traffic():
+    """HBM bytes per expert-FFN call from the committed counter summary, or
+    None when the kernel sources changed since those counters were taken."""
+    import glob
+    import hashlib
+    import re
+
+    path = os.path.join(ROOT, "profiles", "decode896_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"sources_sha256: ([0-9a-f]{64})", text)
+    m_bytes = re.search(r"ffn_call_traffic_bytes: (\d+)", text)
+    if not (m_sha and m_bytes):
+        return None
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "mxfp4_routed_expert_02_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return int(m_bytes.group(1)) if h.hexdigest() == m_sha.group(1) else None
+
+
+def copy_probe(mib):
+    """A plain copy kernel of known size: FETCH_SIZE / WRITE_SIZE read for it
+    give the counters' scale against true bytes."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copy probe: 5 copies of {mib} MiB ({n * 4} bytes read and written each)")
 
 
 def main():
@@ -53,6 +91,10 @@ def main():
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}, "
               f"WORLD_SIZE {world})", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_probe_mib > 0:
+        copy_probe(args.copy_probe_mib)
+        return
 
     import numpy as np
     import torch
@@ -131,7 +173,8 @@ def main():
                    "tokens": wl.T, "variants": V, "weight_bytes_per_step": weight_bytes},
         "roofline": {"bound": "hbm", "kernel": "moe_expert_ffn_mxfp4 call", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "launch_us": round(ffn_us, 2), "algorithmic_bytes": ffn_bytes},
+                     "traffic": profiled_traffic(), "launch_us": round(ffn_us, 2),
+                     "algorithmic_bytes": ffn_bytes},
     }
 
     if args.prefill_reps > 0:
