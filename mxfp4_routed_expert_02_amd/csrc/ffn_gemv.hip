@@ -22,7 +22,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / MOE_WAVE;
 constexpr int kRowsPerBlock = 16;
-constexpr int kRegRows = 4;  // rows per expert the register path takes at once
 // row-group unroll of the kernels specialized for 224-block (H = 7168) and
 // 48-block (I = 1536) rows; the host grid uses the same constants
 constexpr int kGateU224 = 1;
@@ -560,9 +559,9 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 namespace moe {
 
 size_t expert_ffn_workspace(int T, int k, int E, int H, int I) {
-  (void)E;
-  (void)H;
-  return align_up((size_t)T * k * I * sizeof(float), 256);  // h[R][I]
+  size_t b = align_up((size_t)T * k * I * sizeof(float), 256);  // h[R][I]
+  if (T > 1 && mfma_shape_ok(H, I)) b += mfma_workspace(T, k, E, H, I);
+  return b;
 }
 
 hipError_t launch_expert_ffn(const uint16_t* x, int T, int k, const moe_mxfp4_weights& w, const int32_t* offsets,
@@ -616,7 +615,12 @@ hipError_t launch_expert_ffn(const uint16_t* x, int T, int k, const moe_mxfp4_we
 #undef GU_REG
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  if (!reg_g || T > 1) {
+  const bool use_mfma = T > 1 && reg_g && reg_d && mfma_shape_ok(H, I);
+  uint8_t* mfma_ws = (uint8_t*)ws + align_up((size_t)R * I * sizeof(float), 256);
+  if (use_mfma) {
+    if ((err = launch_mfma_gateup(x, T, k, w, offsets, sorted_rows, active, hbuf, mfma_ws, s)) != hipSuccess)
+      return err;
+  } else if (!reg_g || T > 1) {
     const int mt_g = pick_mt((size_t)H * 2);
     dim3 grid_g((I + kRowsPerBlock - 1) / kRowsPerBlock, max_active);
     const size_t lds_g = (size_t)mt_g * H * 2;
@@ -666,7 +670,10 @@ hipError_t launch_expert_ffn(const uint16_t* x, int T, int k, const moe_mxfp4_we
 #undef DN_REG
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  if (!reg_d || T > 1) {
+  if (use_mfma) {
+    if ((err = launch_mfma_down(T, k, w, offsets, sorted_rows, active, hbuf, y_rows, mfma_ws, s)) != hipSuccess)
+      return err;
+  } else if (!reg_d || T > 1) {
     const int mt_d = pick_mt((size_t)I * 4);
     dim3 grid_d((H + kRowsPerBlock - 1) / kRowsPerBlock, max_active);
     const size_t lds_d = (size_t)mt_d * I * 4;

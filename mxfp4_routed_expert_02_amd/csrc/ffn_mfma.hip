@@ -1,0 +1,461 @@
+// ffn_mfma.hip - expert-major grouped GEMM of the expert FFN on the CDNA4
+// scaled MFMA (v_mfma_scale_f32_32x32x64_f8f6f4), for experts whose routed
+// rows make the product a dense contraction (more than kRegRows rows).
+//
+// A operand = the expert's MXFP4 weights exactly as stored (E2M1 codes with
+// their own E8M0 scale per 32 values); B operand = the activations split in
+// two E4M3 terms, each with an E8M0 scale per 32 values:
+//     a = q1 * 2^e1 + q2 * 2^e2,   q1 = rne_e4m3(a / 2^e1), q2 = rne_e4m3((a - q1 2^e1) / 2^e2)
+// with e = ceil(log2(amax / 448)) per block and term.  A bf16 value has 8
+// significant bits and each E4M3 term carries 4, so for x the two terms are
+// exact; for the fp32 h they carry the leading ~8 bits.  D accumulates both
+// terms in fp32.
+//
+// Operand layout of one 32x32x64 step (64 K values; lane-group h = lane / 32
+// of the FP4 operand holds K values 32h .. 32h+31 and lane l gives the E8M0
+// scale of 32-block l / 32 of its operand):
+//   A lane (m, h): weight row m, the 16 bytes (32 E2M1 codes) of block h of
+//                  the step, exactly as stored; that block's scale byte.
+//   B lane (n, h): token n, 32 E4M3 bytes holding K values 16h .. 16h+15 and
+//                  32 + 16h .. 32 + 16h + 15 (the FP8 operand's lane-groups
+//                  split K in 16-value halves); the scale byte of K values
+//                  32h .. 32h+31.  The quantizer stores the terms with the
+//                  middle two 16-value quarters of every 64 values swapped, so
+//                  that these 32 bytes are contiguous.
+//   D lane l, register r: token l % 32, weight row 8*(r/4) + 4*(l/32) + r%4.
+//
+// Tiles: 128 weight rows x 128 tokens per block of 4 waves (32 tokens per
+// wave, 4 row blocks of 32 each).  For gate/up the 128 rows are gate rows
+// i0..i0+63 followed by the same up rows, so SiLU(g)*u is formed in
+// registers.  The A tile of each 256-value K stage is staged in LDS
+// (double-buffered, 16-byte pieces XOR-swizzled by row) and shared by the
+// 4 waves; each wave streams its own B directly into registers.  Tiles are
+// numbered weight-tile-major within (expert, token tile) and spread so that
+// each XCD takes a contiguous range of tiles: tiles sharing a token tile
+// and neighbouring weight tiles run on the same L2.
+#include <climits>
+
+#include "moe_internal.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTileRows = 128;    // weight rows per block
+constexpr int kTileTok = 128;     // tokens per block
+constexpr int kStageK = 256;      // K values per LDS stage
+constexpr int kStageBytes = 128;  // FP4 bytes per row per stage
+
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+typedef float v16f_t __attribute__((ext_vector_type(16)));
+
+// ------------------------------------------------------------ E4M3 terms --
+// Round |a| <= 448 to E4M3 (ties to even); returns the code and the rounded
+// value (in the same units as a).
+__device__ __forceinline__ uint32_t e4m3_rne(float a, float& qv) {
+  const float x = fabsf(a);
+  uint32_t code;
+  if (x < 0.015625f) {  // below 2^-6: the subnormal grid m * 2^-9 (m = 8 is 2^-6)
+    const float m = rintf(x * 512.0f);
+    code = (uint32_t)m;
+    qv = m * (1.0f / 512.0f);
+  } else {
+    uint32_t b = __float_as_uint(x);
+    b += 0x7FFFFu + ((b >> 20) & 1u);  // keep 3 mantissa bits
+    b &= 0xFFF00000u;
+    code = (b >> 20) - (120u << 3);    // exponent bias 127 -> 7
+    if (code > 0x7Eu) {
+      code = 0x7Eu;
+      b = 0x43E00000u;  // 448
+    }
+    qv = __uint_as_float(b);
+  }
+  if (a < 0.0f) {
+    code |= 0x80u;
+    qv = -qv;
+  }
+  return code;
+}
+
+// E8M0 exponent e with amax / 2^e <= 448, e = ceil(log2(amax / 448)); 0 for amax = 0
+__device__ __forceinline__ int e4m3_block_exp(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  const uint32_t b = __float_as_uint(amax);
+  const int E = (int)((b >> 23) & 0xFF) - 127;
+  int e = ((b & 0x7FFFFFu) <= 0x600000u) ? E - 8 : E - 7;  // 448 = 1.75 * 2^8
+  return e < -126 ? -126 : (e > 126 ? 126 : e);  // 2^e and 2^-e stay normal floats
+}
+
+// Quantizes rows of a [rows][K] matrix (bf16 bits or fp32) into two E4M3
+// terms: q[row][2][K] bytes (quarters of each 64 values in the order
+// 0,2,1,3), s[row][2][K/256][2][4] scale bytes where the scale of 32-block
+// j = 8*stage + 2*step + half sits at [stage][half][step].
+// One thread per (row, 32-block).
+template <bool BF16_IN>
+__device__ __forceinline__ void quantize_block(const void* src, int row, int blk, int K, uint8_t* __restrict__ q,
+                                               uint8_t* __restrict__ s) {
+  float v[32];
+  if (BF16_IN) {
+    const uint4* p = (const uint4*)((const uint16_t*)src + (int64_t)row * K + 32 * blk);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 w = p[i];
+      const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * i + 2 * j] = __uint_as_float(d[j] << 16);
+        v[8 * i + 2 * j + 1] = __uint_as_float(d[j] & 0xFFFF0000u);
+      }
+    }
+  } else {
+    const float4* p = (const float4*)((const float*)src + (int64_t)row * K + 32 * blk);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 w = p[i];
+      v[4 * i] = w.x;
+      v[4 * i + 1] = w.y;
+      v[4 * i + 2] = w.z;
+      v[4 * i + 3] = w.w;
+    }
+  }
+  const int sidx = (blk >> 3) * 8 + (blk & 1) * 4 + ((blk >> 1) & 3);
+#pragma unroll
+  for (int term = 0; term < 2; ++term) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    const int e = e4m3_block_exp(amax);
+    const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e
+    const float scl = __uint_as_float((uint32_t)(127 + e) << 23);  // 2^e
+    uint32_t packed[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) packed[i] = 0u;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      float qv;
+      const uint32_t c = e4m3_rne(v[i] * inv, qv);
+      packed[i >> 2] |= c << (8 * (i & 3));
+      v[i] -= qv * scl;  // residual for the next term (exact)
+    }
+    // quarters 0,1,2,3 of each 64 values are stored in the order 0,2,1,3
+    uint8_t* g64 = q + ((int64_t)row * 2 + term) * K + 64 * (blk >> 1);
+    *(uint4*)(g64 + 16 * (blk & 1)) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    *(uint4*)(g64 + 32 + 16 * (blk & 1)) = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+    s[((int64_t)row * 2 + term) * (K / 32) + sidx] = (uint8_t)(e + 127);
+  }
+}
+
+// x [T][H] bf16 -> two E4M3 terms; block 0 also writes the tile plan: one
+// (slot, token tile) pair per token tile of every active expert with more
+// than kRegRows rows, in active-list order, and the pair count in plan[0].
+__global__ __launch_bounds__(kThreads) void mfma_prep_kernel(const uint16_t* __restrict__ x, int T, int H,
+                                                            const int32_t* __restrict__ offsets,
+                                                            const int32_t* __restrict__ active,
+                                                            uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
+                                                            int32_t* __restrict__ plan) {
+  if (blockIdx.x == 0) {
+    __shared__ int s_wave[kThreads / 64];
+    const int na = active[0];
+    int base = 0;
+    for (int a0 = 0; a0 < na; a0 += kThreads) {
+      const int a = a0 + threadIdx.x;
+      int nt = 0, e = 0;
+      if (a < na) {
+        e = active[1 + a];
+        const int cnt = offsets[e + 1] - offsets[e];
+        nt = cnt > kRegRows ? (cnt + kTileTok - 1) / kTileTok : 0;
+      }
+      // block-wide exclusive scan of nt
+      int v = nt;
+      const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(v, o, 64);
+        if (lane >= o) v += u;
+      }
+      if (lane == 63) s_wave[wave] = v;
+      __syncthreads();
+      int before = base;
+      for (int w = 0; w < wave; ++w) before += s_wave[w];
+      int total = 0;
+      for (int w = 0; w < kThreads / 64; ++w) total += s_wave[w];
+      before += v - nt;
+      for (int j = 0; j < nt; ++j) {
+        plan[1 + 2 * (before + j)] = a;
+        plan[2 + 2 * (before + j)] = j;
+      }
+      base += total;
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) plan[0] = base;
+    return;
+  }
+  const int nblk = H >> 5;
+  const int64_t i = (int64_t)(blockIdx.x - 1) * kThreads + threadIdx.x;
+  if (i >= (int64_t)T * nblk) return;
+  quantize_block<true>(x, (int)(i / nblk), (int)(i % nblk), H, xq, xs);
+}
+
+// h [R][I] fp32 -> two E4M3 terms, for every row
+__global__ __launch_bounds__(kThreads) void quantize_h_kernel(const float* __restrict__ h, int R, int I,
+                                                             uint8_t* __restrict__ hq, uint8_t* __restrict__ hs) {
+  const int nblk = I >> 5;
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= (int64_t)R * nblk) return;
+  quantize_block<false>(h, (int)(i / nblk), (int)(i % nblk), I, hq, hs);
+}
+
+// ------------------------------------------------------------------ GEMM --
+
+// 8 scale bytes of a row (natural order j = 2*step + half) -> [half][step]
+__device__ __forceinline__ uint2 scales_by_half(uint2 v) {
+  // bytes b0..b7 -> (b0, b2, b4, b6), (b1, b3, b5, b7)
+  const uint32_t lo = __builtin_amdgcn_perm(v.y, v.x, 0x06040200u);
+  const uint32_t hi = __builtin_amdgcn_perm(v.y, v.x, 0x07050301u);
+  return make_uint2(lo, hi);
+}
+
+template <bool GATEUP>
+__global__ __launch_bounds__(kThreads) void mfma_ffn_kernel(moe_mxfp4_weights w, int k,
+                                                           const int32_t* __restrict__ offsets,
+                                                           const int32_t* __restrict__ sorted_rows,
+                                                           const int32_t* __restrict__ active,
+                                                           const int32_t* __restrict__ plan,
+                                                           const uint8_t* __restrict__ bq,  // B terms [rows][2][K]
+                                                           const uint8_t* __restrict__ bs,  // B scales [rows][2][K/32]
+                                                           float* __restrict__ out, int m_tiles) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][kTileRows * kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint32_t s_sc[2][kTileRows * 2];
+
+  const int H = w.hidden, I = w.inter;
+  const int K = GATEUP ? H : I;               // reduction length
+  const int out_cols = GATEUP ? I : H;        // columns of the output rows
+  const uint32_t qrow = (uint32_t)K >> 1;     // FP4 bytes per weight row
+  const int nsb = K >> 5;                     // scale bytes per weight row
+
+  // tile index: each XCD (blockIdx % 8) takes a contiguous range of tiles
+  const int W = plan[0] * m_tiles;
+  const int per_xcd = (W + 7) >> 3;
+  const int bx = blockIdx.x;
+  if ((bx >> 3) >= per_xcd) return;
+  const int wt = (bx & 7) * per_xcd + (bx >> 3);
+  if (wt >= W) return;
+  const int pair = wt / m_tiles, mt = wt - pair * m_tiles;
+  const int slot = plan[1 + 2 * pair], ntile = plan[2 + 2 * pair];
+  const int e = active[1 + slot];
+  const int p0 = offsets[e], cnt = offsets[e + 1] - p0;
+  const int tok0 = ntile * kTileTok;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t eo = (int64_t)e * w.expert_stride;
+  const uint8_t* wq_g = (GATEUP ? w.gate_q : w.down_q) + eo;
+  const uint8_t* ws_g = (GATEUP ? w.gate_s : w.down_s) + eo;
+  const uint8_t* wq_u = w.up_q + eo;
+  const uint8_t* ws_u = w.up_s + eo;
+  const int row0 = GATEUP ? mt * (kTileRows / 2) : mt * kTileRows;
+
+  // staging: thread t copies 16-byte pieces c = t + 256 i (row c/8, piece c%8)
+  auto a_src = [&](int r) -> const uint8_t* {
+    if (GATEUP) return r < 64 ? wq_g + (int64_t)(row0 + r) * qrow : wq_u + (int64_t)(row0 + r - 64) * qrow;
+    return wq_g + (int64_t)(row0 + r) * qrow;
+  };
+  auto s_src = [&](int r) -> const uint8_t* {
+    if (GATEUP) return r < 64 ? ws_g + (int64_t)(row0 + r) * nsb : ws_u + (int64_t)(row0 + r - 64) * nsb;
+    return ws_g + (int64_t)(row0 + r) * nsb;
+  };
+  uint4 stage_q[4];
+  uint2 stage_s;
+  auto load_stage = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + kThreads * i;
+      stage_q[i] = *(const uint4*)(a_src(c >> 3) + st * kStageBytes + 16 * (c & 7));
+    }
+    if (tid < kTileRows) stage_s = *(const uint2*)(s_src(tid) + st * 8);
+  };
+  auto store_stage = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + kThreads * i;
+      const int r = c >> 3, piece = c & 7;
+      *(uint4*)(&s_a[buf][r * kStageBytes + 16 * (piece ^ (r & 7))]) = stage_q[i];
+    }
+    if (tid < kTileRows) {
+      const uint2 hs = scales_by_half(stage_s);
+      s_sc[buf][2 * tid] = hs.x;
+      s_sc[buf][2 * tid + 1] = hs.y;
+    }
+  };
+
+  // this lane's B row (token); rows past the expert's count re-read its last row
+  const int n = lane & 31, half = lane >> 5;
+  const int tok = tok0 + wave * 32 + n;
+  const bool tok_ok = tok < cnt;
+  const int p = p0 + (tok_ok ? tok : cnt - 1);
+  const int64_t brow = GATEUP ? (int64_t)(sorted_rows[p] / k) : (int64_t)p;
+  const uint8_t* b0 = bq + (brow * 2 + 0) * K + 32 * half;
+  const uint8_t* b1 = bq + (brow * 2 + 1) * K + 32 * half;
+  const uint32_t* bs0 = (const uint32_t*)(bs + (brow * 2 + 0) * nsb) + half;
+  const uint32_t* bs1 = (const uint32_t*)(bs + (brow * 2 + 1) * nsb) + half;
+
+  v16f_t acc[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[rb][i] = 0.0f;
+
+  const int nst = K / kStageK;
+  load_stage(0);
+  store_stage(0);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nst) load_stage(st + 1);
+    const uint32_t sb0 = bs0[2 * st], sb1 = bs1[2 * st];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int koff = st * kStageK + 64 * s;
+      v8i_t B0, B1;
+      {
+        const uint4 u0 = *(const uint4*)(b0 + koff), u1 = *(const uint4*)(b0 + koff + 16);
+        const uint4 w0 = *(const uint4*)(b1 + koff), w1 = *(const uint4*)(b1 + koff + 16);
+        B0[0] = u0.x; B0[1] = u0.y; B0[2] = u0.z; B0[3] = u0.w;
+        B0[4] = u1.x; B0[5] = u1.y; B0[6] = u1.z; B0[7] = u1.w;
+        B1[0] = w0.x; B1[1] = w0.y; B1[2] = w0.z; B1[3] = w0.w;
+        B1[4] = w1.x; B1[5] = w1.y; B1[6] = w1.z; B1[7] = w1.w;
+      }
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const int r = 32 * rb + n;
+        // block (2s + half) of the stage row: 16-byte piece 2s + half
+        const uint4 wa = *(const uint4*)(&s_a[buf][r * kStageBytes + 16 * ((2 * s + half) ^ (r & 7))]);
+        v8i_t A;
+        A[0] = wa.x; A[1] = wa.y; A[2] = wa.z; A[3] = wa.w;
+        A[4] = 0; A[5] = 0; A[6] = 0; A[7] = 0;
+        const uint32_t sa = s_sc[buf][2 * r + half];
+        // format codes: A = 4 (FP4 E2M1), B = 0 (FP8 E4M3); byte s of each scale word
+        switch (s) {
+          case 0:
+            acc[rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B0, acc[rb], 4, 0, 0, sa, 0, sb0);
+            acc[rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B1, acc[rb], 4, 0, 0, sa, 0, sb1);
+            break;
+          case 1:
+            acc[rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B0, acc[rb], 4, 0, 1, sa, 1, sb0);
+            acc[rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B1, acc[rb], 4, 0, 1, sa, 1, sb1);
+            break;
+          case 2:
+            acc[rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B0, acc[rb], 4, 0, 2, sa, 2, sb0);
+            acc[rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B1, acc[rb], 4, 0, 2, sa, 2, sb1);
+            break;
+          default:
+            acc[rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B0, acc[rb], 4, 0, 3, sa, 3, sb0);
+            acc[rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B1, acc[rb], 4, 0, 3, sa, 3, sb1);
+            break;
+        }
+      }
+    }
+    if (st + 1 < nst) store_stage(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (!tok_ok) return;
+  float* orow = out + (int64_t)(p0 + tok) * out_cols;
+  if (GATEUP) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int m = row0 + 32 * rb + 8 * g + 4 * half;
+        float4 v;
+        v.x = silu_mul(acc[rb][4 * g + 0], acc[rb + 2][4 * g + 0]);
+        v.y = silu_mul(acc[rb][4 * g + 1], acc[rb + 2][4 * g + 1]);
+        v.z = silu_mul(acc[rb][4 * g + 2], acc[rb + 2][4 * g + 2]);
+        v.w = silu_mul(acc[rb][4 * g + 3], acc[rb + 2][4 * g + 3]);
+        *(float4*)(orow + m) = v;
+      }
+  } else {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int m = row0 + 32 * rb + 8 * g + 4 * half;
+        *(float4*)(orow + m) =
+            make_float4(acc[rb][4 * g + 0], acc[rb][4 * g + 1], acc[rb][4 * g + 2], acc[rb][4 * g + 3]);
+      }
+  }
+}
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+}  // namespace
+
+namespace moe {
+
+bool mfma_shape_ok(int H, int I) { return H % kStageK == 0 && I % kStageK == 0 && I % 64 == 0 && H % 128 == 0; }
+
+// Workspace of the MFMA path after the h buffer: x terms, x scales, h terms,
+// h scales, tile plan.
+size_t mfma_workspace(int T, int k, int E, int H, int I) {
+  const size_t R = (size_t)T * k;
+  const size_t mx = (size_t)(R < (size_t)E ? R : E);
+  const size_t pairs = R / kTileTok + (mx < R / (kRegRows + 1) ? mx : R / (kRegRows + 1)) + 1;
+  return align256((size_t)T * 2 * H) + align256((size_t)T * 2 * (H / 32)) + align256(R * 2 * I) +
+         align256(R * 2 * (I / 32)) + align256((1 + 2 * pairs) * sizeof(int32_t));
+}
+
+size_t mfma_max_pairs(int T, int k, int E) {
+  const size_t R = (size_t)T * k;
+  const size_t mx = (size_t)(R < (size_t)E ? R : E);
+  return R / kTileTok + (mx < R / (kRegRows + 1) ? mx : R / (kRegRows + 1)) + 1;
+}
+
+// Launches prep, gate/up GEMM (h for experts with more than kRegRows rows).
+hipError_t launch_mfma_gateup(const uint16_t* x, int T, int k, const moe_mxfp4_weights& w, const int32_t* offsets,
+                              const int32_t* sorted_rows, const int32_t* active, float* h, uint8_t* ws,
+                              hipStream_t s) {
+  const int H = w.hidden, I = w.inter;
+  const size_t R = (size_t)T * k;
+  uint8_t* xq = ws;
+  uint8_t* xs = xq + align256((size_t)T * 2 * H);
+  uint8_t* hq = xs + align256((size_t)T * 2 * (H / 32));
+  uint8_t* hs = hq + align256(R * 2 * I);
+  int32_t* plan = (int32_t*)(hs + align256(R * 2 * (I / 32)));
+  (void)hq;
+  (void)hs;
+  const int64_t nq = (int64_t)T * (H / 32);
+  hipLaunchKernelGGL(mfma_prep_kernel, dim3(1 + (unsigned)((nq + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
+                     x, T, H, offsets, active, xq, xs, plan);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int m_tiles = I / (kTileRows / 2);
+  const size_t max_tiles = mfma_max_pairs(T, k, w.num_experts) * m_tiles;
+  const unsigned grid = (unsigned)(8 * ((max_tiles + 7) / 8));
+  hipLaunchKernelGGL((mfma_ffn_kernel<true>), dim3(grid), dim3(kThreads), 0, s, w, k, offsets, sorted_rows, active,
+                     plan, xq, xs, h, m_tiles);
+  return hipGetLastError();
+}
+
+// Launches h quantization and the down GEMM (y_rows for the same experts).
+hipError_t launch_mfma_down(int T, int k, const moe_mxfp4_weights& w, const int32_t* offsets,
+                            const int32_t* sorted_rows, const int32_t* active, const float* h, float* y_rows,
+                            uint8_t* ws, hipStream_t s) {
+  const int H = w.hidden, I = w.inter;
+  const size_t R = (size_t)T * k;
+  uint8_t* xq = ws;
+  uint8_t* xs = xq + align256((size_t)T * 2 * H);
+  uint8_t* hq = xs + align256((size_t)T * 2 * (H / 32));
+  uint8_t* hs = hq + align256(R * 2 * I);
+  int32_t* plan = (int32_t*)(hs + align256(R * 2 * (I / 32)));
+  const int64_t nq = (int64_t)R * (I / 32);
+  hipLaunchKernelGGL(quantize_h_kernel, dim3((unsigned)((nq + kThreads - 1) / kThreads)), dim3(kThreads), 0, s, h,
+                     (int)R, I, hq, hs);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int m_tiles = H / kTileRows;
+  const size_t max_tiles = mfma_max_pairs(T, k, w.num_experts) * m_tiles;
+  const unsigned grid = (unsigned)(8 * ((max_tiles + 7) / 8));
+  hipLaunchKernelGGL((mfma_ffn_kernel<false>), dim3(grid), dim3(kThreads), 0, s, w, k, offsets, sorted_rows, active,
+                     plan, hq, hs, y_rows, m_tiles);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -13,6 +13,10 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 #define MOE_WAVE 64
 
+// experts with at most this many routed rows run on the GEMV kernels; more
+// rows per expert take the grouped GEMM (MFMA) path
+constexpr int kRegRows = 4;
+
 // ------------------------------------------------------------------ device --
 // E8M0 scale byte -> 2^(s-127) as fp32 (s = 0 is the subnormal 2^-127).
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
@@ -103,6 +107,16 @@ hipError_t launch_expert_ffn(const uint16_t* x, int T, int k, const moe_mxfp4_we
                              const int32_t* sorted_rows, const int32_t* active, float* y_rows, void* ws,
                              hipStream_t s);
 size_t expert_ffn_workspace(int T, int k, int E, int H, int I);
+
+// MFMA grouped-GEMM path (experts with more than 4 routed rows)
+bool mfma_shape_ok(int H, int I);
+size_t mfma_workspace(int T, int k, int E, int H, int I);
+hipError_t launch_mfma_gateup(const uint16_t* x, int T, int k, const moe_mxfp4_weights& w, const int32_t* offsets,
+                              const int32_t* sorted_rows, const int32_t* active, float* h, uint8_t* ws,
+                              hipStream_t s);
+hipError_t launch_mfma_down(int T, int k, const moe_mxfp4_weights& w, const int32_t* offsets,
+                            const int32_t* sorted_rows, const int32_t* active, const float* h, float* y_rows,
+                            uint8_t* ws, hipStream_t s);
 
 hipError_t launch_combine(const float* y_rows, const float* w, const int32_t* row_pos, int T, int k, int H,
                           float* out, hipStream_t s);

@@ -53,6 +53,11 @@ SMALL = [
     synth.Workload("many_rows_chunks", E=24, H=64, I=32, k=6, T=400, pool=26, sub=26),
     synth.Workload("wide_rows", E=4, H=4096, I=64, k=2, T=6, pool=27, sub=27),
     synth.Workload("long_rows_down", E=4, H=64, I=4096, k=2, T=6, pool=28, sub=28),
+    # grouped-GEMM (MFMA) path: experts with more than 4 rows, several K stages,
+    # weight tiles and ragged token tiles
+    synth.Workload("mfma_mid", E=8, H=512, I=256, k=2, T=300, pool=30, sub=30),
+    synth.Workload("mfma_ragged", E=12, H=768, I=512, k=3, T=97, logits="zipf", pool=31, sub=31),
+    synth.Workload("mfma_one_hot_expert", E=6, H=256, I=256, k=1, T=260, logits="dense16", pool=32, sub=32),
 ]
 
 
