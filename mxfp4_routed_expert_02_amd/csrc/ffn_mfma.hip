@@ -24,15 +24,17 @@
 //                  that these 32 bytes are contiguous.
 //   D lane l, register r: token l % 32, weight row 8*(r/4) + 4*(l/32) + r%4.
 //
-// Tiles: 128 weight rows x 128 tokens per block of 4 waves (32 tokens per
-// wave, 4 row blocks of 32 each).  For gate/up the 128 rows are gate rows
-// i0..i0+63 followed by the same up rows, so SiLU(g)*u is formed in
-// registers.  The A tile of each 256-value K stage is staged in LDS
-// (double-buffered, 16-byte pieces XOR-swizzled by row) and shared by the
-// 4 waves; each wave streams its own B directly into registers.  Tiles are
-// numbered weight-tile-major within (expert, token tile) and spread so that
-// each XCD takes a contiguous range of tiles: tiles sharing a token tile
-// and neighbouring weight tiles run on the same L2.
+// Tiles: 256 weight rows x 128 tokens per block of 4 waves, one block per
+// CU (32 tokens per wave, 8 row blocks of 32 each, accumulators in AGPRs).
+// For gate/up the 256 rows are gate rows i0..i0+127 followed by the same up
+// rows, so SiLU(g)*u is formed in registers.  The A tile of each 256-value K
+// stage is staged in LDS (double-buffered, rows padded against bank
+// conflicts) and shared by the 4 waves; each wave streams its own B into
+// registers one stage ahead.  256 rows per tile halve the B bytes per MFMA
+// against 128, which keeps the vector-memory path under the MFMA time.
+// Tiles are numbered weight-tile-major within (expert, token tile) and
+// spread so that each XCD takes a contiguous range of tiles: tiles sharing
+// a token tile and neighbouring weight tiles run on the same L2.
 #include <climits>
 
 #include "moe_internal.h"
@@ -40,7 +42,7 @@
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTileRows = 128;    // weight rows per block
+constexpr int kTileRows = 256;    // weight rows per block
 constexpr int kTileTok = 128;     // tokens per block
 constexpr int kStageK = 256;      // K values per LDS stage
 constexpr int kStageBytes = 128;  // FP4 bytes per row per stage
@@ -214,17 +216,30 @@ __device__ __forceinline__ uint2 scales_by_half(uint2 v) {
   return make_uint2(lo, hi);
 }
 
+// One 64-deep K step of a 32x32 block: FP4 weights (format 4) times the
+// two E4M3 activation terms (format 0); OPSEL picks byte OPSEL of each
+// packed scale word (the step's block scale).
+template <int OPSEL>
+__device__ __forceinline__ v16f_t mfma_step(const v8i_t& A, const v8i_t& B0, const v8i_t& B1, v16f_t acc,
+                                            uint32_t sa, uint32_t sb0, uint32_t sb1) {
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B0, acc, 4, 0, OPSEL, sa, OPSEL, sb0);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B1, acc, 4, 0, OPSEL, sa, OPSEL, sb1);
+}
+
 template <bool GATEUP>
-__global__ __launch_bounds__(kThreads) void mfma_ffn_kernel(moe_mxfp4_weights w, int k,
-                                                           const int32_t* __restrict__ offsets,
-                                                           const int32_t* __restrict__ sorted_rows,
-                                                           const int32_t* __restrict__ active,
-                                                           const int32_t* __restrict__ plan,
-                                                           const uint8_t* __restrict__ bq,  // B terms [rows][2][K]
-                                                           const uint8_t* __restrict__ bs,  // B scales [rows][2][K/32]
-                                                           float* __restrict__ out, int m_tiles) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][kTileRows * kStageBytes];
-  __shared__ __attribute__((aligned(16))) uint32_t s_sc[2][kTileRows * 2];
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void mfma_ffn_kernel(
+    moe_mxfp4_weights w, int k, const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_rows,
+    const int32_t* __restrict__ active, const int32_t* __restrict__ plan,
+    const uint8_t* __restrict__ bq,  // B terms [rows][2][K]
+    const uint8_t* __restrict__ bs,  // B scales [rows][2][K/32]
+    float* __restrict__ out, int m_tiles) {
+  // A stage: kTileRows rows of 128 bytes, rows padded to 144 bytes so that
+  // 16 consecutive rows read at the same column fall in distinct LDS banks
+  constexpr int kRowPitch = kStageBytes + 16;
+  constexpr int kRB = kTileRows / 32;  // 32-row blocks per wave
+  static_assert(kTileRows == kThreads, "one scale row per thread");
+  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][kTileRows * kRowPitch];
+  __shared__ __attribute__((aligned(16))) uint32_t s_sc[2][kTileRows * 2];  // [row][half] words by step
 
   const int H = w.hidden, I = w.inter;
   const int K = GATEUP ? H : I;               // reduction length
@@ -247,44 +262,55 @@ __global__ __launch_bounds__(kThreads) void mfma_ffn_kernel(moe_mxfp4_weights w,
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t eo = (int64_t)e * w.expert_stride;
-  const uint8_t* wq_g = (GATEUP ? w.gate_q : w.down_q) + eo;
-  const uint8_t* ws_g = (GATEUP ? w.gate_s : w.down_s) + eo;
-  const uint8_t* wq_u = w.up_q + eo;
-  const uint8_t* ws_u = w.up_s + eo;
+  // tile rows: gate/up = gate rows row0 .. row0+127 then the same up rows;
+  // down = rows row0 .. row0+255
   const int row0 = GATEUP ? mt * (kTileRows / 2) : mt * kTileRows;
 
-  // staging: thread t copies 16-byte pieces c = t + 256 i (row c/8, piece c%8)
-  auto a_src = [&](int r) -> const uint8_t* {
-    if (GATEUP) return r < 64 ? wq_g + (int64_t)(row0 + r) * qrow : wq_u + (int64_t)(row0 + r - 64) * qrow;
-    return wq_g + (int64_t)(row0 + r) * qrow;
-  };
-  auto s_src = [&](int r) -> const uint8_t* {
-    if (GATEUP) return r < 64 ? ws_g + (int64_t)(row0 + r) * nsb : ws_u + (int64_t)(row0 + r - 64) * nsb;
-    return ws_g + (int64_t)(row0 + r) * nsb;
-  };
-  uint4 stage_q[4];
-  uint2 stage_s;
-  auto load_stage = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + kThreads * i;
-      stage_q[i] = *(const uint4*)(a_src(c >> 3) + st * kStageBytes + 16 * (c & 7));
-    }
-    if (tid < kTileRows) stage_s = *(const uint2*)(s_src(tid) + st * 8);
-  };
-  auto store_stage = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + kThreads * i;
-      const int r = c >> 3, piece = c & 7;
-      *(uint4*)(&s_a[buf][r * kStageBytes + 16 * (piece ^ (r & 7))]) = stage_q[i];
-    }
-    if (tid < kTileRows) {
-      const uint2 hs = scales_by_half(stage_s);
-      s_sc[buf][2 * tid] = hs.x;
-      s_sc[buf][2 * tid + 1] = hs.y;
-    }
-  };
+  // A staging: thread t copies the 16-byte pieces (row (t/8) + 32 i, piece
+  // t%8), i = 0..7, and the 8 scale bytes of row t.  The pieces travel
+  // through named registers (no array, so they stay in VGPRs).
+  const int64_t rstride = (int64_t)32 * qrow;  // 32 rows
+  const uint8_t* a_lo;                         // pieces 0..3
+  const uint8_t* a_hi;                         // pieces 4..7
+  const uint8_t* s_row;
+  if (GATEUP) {
+    a_lo = w.gate_q + eo + (int64_t)(row0 + (tid >> 3)) * qrow + 16 * (tid & 7);
+    a_hi = w.up_q + eo + (int64_t)(row0 + (tid >> 3)) * qrow + 16 * (tid & 7);
+    s_row = tid < kTileRows / 2 ? w.gate_s + eo + (int64_t)(row0 + tid) * nsb
+                                : w.up_s + eo + (int64_t)(row0 + tid - kTileRows / 2) * nsb;
+  } else {
+    a_lo = w.down_q + eo + (int64_t)(row0 + (tid >> 3)) * qrow + 16 * (tid & 7);
+    a_hi = a_lo + 4 * rstride;
+    s_row = w.down_s + eo + (int64_t)(row0 + tid) * nsb;
+  }
+  uint4 aq0, aq1, aq2, aq3, aq4, aq5, aq6, aq7;
+  uint2 as2;
+#define MFMA_LOAD_A(ST)                                                  \
+  do {                                                                   \
+    const int so_ = (ST) * kStageBytes;                                  \
+    aq0 = *(const uint4*)(a_lo + so_);                                   \
+    aq1 = *(const uint4*)(a_lo + rstride + so_);                         \
+    aq2 = *(const uint4*)(a_lo + 2 * rstride + so_);                     \
+    aq3 = *(const uint4*)(a_lo + 3 * rstride + so_);                     \
+    aq4 = *(const uint4*)(a_hi + so_);                                   \
+    aq5 = *(const uint4*)(a_hi + rstride + so_);                         \
+    aq6 = *(const uint4*)(a_hi + 2 * rstride + so_);                     \
+    aq7 = *(const uint4*)(a_hi + 3 * rstride + so_);                     \
+    as2 = *(const uint2*)(s_row + (ST) * 8);                             \
+  } while (0)
+#define MFMA_STORE_A(BUF)                                                          \
+  do {                                                                             \
+    uint8_t* d_ = &s_a[BUF][(tid >> 3) * kRowPitch + 16 * (tid & 7)];              \
+    *(uint4*)(d_) = aq0;                                                           \
+    *(uint4*)(d_ + 32 * kRowPitch) = aq1;                                          \
+    *(uint4*)(d_ + 64 * kRowPitch) = aq2;                                          \
+    *(uint4*)(d_ + 96 * kRowPitch) = aq3;                                          \
+    *(uint4*)(d_ + 128 * kRowPitch) = aq4;                                         \
+    *(uint4*)(d_ + 160 * kRowPitch) = aq5;                                         \
+    *(uint4*)(d_ + 192 * kRowPitch) = aq6;                                         \
+    *(uint4*)(d_ + 224 * kRowPitch) = aq7;                                         \
+    *(uint2*)(&s_sc[BUF][2 * tid]) = scales_by_half(as2);                          \
+  } while (0)
 
   // this lane's B row (token); rows past the expert's count re-read its last row
   const int n = lane & 31, half = lane >> 5;
@@ -297,84 +323,110 @@ __global__ __launch_bounds__(kThreads) void mfma_ffn_kernel(moe_mxfp4_weights w,
   const uint32_t* bs0 = (const uint32_t*)(bs + (brow * 2 + 0) * nsb) + half;
   const uint32_t* bs1 = (const uint32_t*)(bs + (brow * 2 + 1) * nsb) + half;
 
-  v16f_t acc[4];
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[rb][i] = 0.0f;
-
-  const int nst = K / kStageK;
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nst) load_stage(st + 1);
-    const uint32_t sb0 = bs0[2 * st], sb1 = bs1[2 * st];
+  // B of one stage in two register sets used in turn: [step][piece]
+  // (pieces 0,1 = term 1, pieces 2,3 = term 2) and the two scale words
+  uint4 bp[16], bq2[16];
+  uint32_t sp0, sp1, sq0, sq1;
+  auto load_b = [&](int st, uint4 (&bb)[16], uint32_t& s0, uint32_t& s1) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int koff = st * kStageK + 64 * s;
-      v8i_t B0, B1;
-      {
-        const uint4 u0 = *(const uint4*)(b0 + koff), u1 = *(const uint4*)(b0 + koff + 16);
-        const uint4 w0 = *(const uint4*)(b1 + koff), w1 = *(const uint4*)(b1 + koff + 16);
-        B0[0] = u0.x; B0[1] = u0.y; B0[2] = u0.z; B0[3] = u0.w;
-        B0[4] = u1.x; B0[5] = u1.y; B0[6] = u1.z; B0[7] = u1.w;
-        B1[0] = w0.x; B1[1] = w0.y; B1[2] = w0.z; B1[3] = w0.w;
-        B1[4] = w1.x; B1[5] = w1.y; B1[6] = w1.z; B1[7] = w1.w;
-      }
+      bb[4 * s + 0] = *(const uint4*)(b0 + koff);
+      bb[4 * s + 1] = *(const uint4*)(b0 + koff + 16);
+      bb[4 * s + 2] = *(const uint4*)(b1 + koff);
+      bb[4 * s + 3] = *(const uint4*)(b1 + koff + 16);
+    }
+    s0 = bs0[2 * st];
+    s1 = bs1[2 * st];
+  };
+
+  v16f_t acc[kRB];
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
+  for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[rb][i] = 0.0f;
+
+  // the MFMAs of one stage: 4 steps x kRB row blocks x 2 terms
+  auto compute = [&](int buf, const uint4 (&bb)[16], uint32_t s0, uint32_t s1) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      v8i_t B0, B1;
+      B0[0] = bb[4 * s].x; B0[1] = bb[4 * s].y; B0[2] = bb[4 * s].z; B0[3] = bb[4 * s].w;
+      B0[4] = bb[4 * s + 1].x; B0[5] = bb[4 * s + 1].y; B0[6] = bb[4 * s + 1].z; B0[7] = bb[4 * s + 1].w;
+      B1[0] = bb[4 * s + 2].x; B1[1] = bb[4 * s + 2].y; B1[2] = bb[4 * s + 2].z; B1[3] = bb[4 * s + 2].w;
+      B1[4] = bb[4 * s + 3].x; B1[5] = bb[4 * s + 3].y; B1[6] = bb[4 * s + 3].z; B1[7] = bb[4 * s + 3].w;
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
         const int r = 32 * rb + n;
         // block (2s + half) of the stage row: 16-byte piece 2s + half
-        const uint4 wa = *(const uint4*)(&s_a[buf][r * kStageBytes + 16 * ((2 * s + half) ^ (r & 7))]);
+        const uint4 wa = *(const uint4*)(&s_a[buf][r * kRowPitch + 16 * (2 * s + half)]);
         v8i_t A;
         A[0] = wa.x; A[1] = wa.y; A[2] = wa.z; A[3] = wa.w;
         A[4] = 0; A[5] = 0; A[6] = 0; A[7] = 0;
         const uint32_t sa = s_sc[buf][2 * r + half];
-        // format codes: A = 4 (FP4 E2M1), B = 0 (FP8 E4M3); byte s of each scale word
-        switch (s) {
-          case 0:
-            acc[rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B0, acc[rb], 4, 0, 0, sa, 0, sb0);
-            acc[rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B1, acc[rb], 4, 0, 0, sa, 0, sb1);
-            break;
-          case 1:
-            acc[rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B0, acc[rb], 4, 0, 1, sa, 1, sb0);
-            acc[rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B1, acc[rb], 4, 0, 1, sa, 1, sb1);
-            break;
-          case 2:
-            acc[rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B0, acc[rb], 4, 0, 2, sa, 2, sb0);
-            acc[rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B1, acc[rb], 4, 0, 2, sa, 2, sb1);
-            break;
-          default:
-            acc[rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B0, acc[rb], 4, 0, 3, sa, 3, sb0);
-            acc[rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B1, acc[rb], 4, 0, 3, sa, 3, sb1);
-            break;
-        }
+        if (s == 0) acc[rb] = mfma_step<0>(A, B0, B1, acc[rb], sa, s0, s1);
+        else if (s == 1) acc[rb] = mfma_step<1>(A, B0, B1, acc[rb], sa, s0, s1);
+        else if (s == 2) acc[rb] = mfma_step<2>(A, B0, B1, acc[rb], sa, s0, s1);
+        else acc[rb] = mfma_step<3>(A, B0, B1, acc[rb], sa, s0, s1);
       }
     }
-    if (st + 1 < nst) store_stage(buf ^ 1);
+  };
+
+  // Pipeline: while the MFMAs of stage st run on LDS buffer st&1 and B
+  // register set st&1, the A pieces of stage st+1 (registers, stored to the
+  // other buffer after the MFMAs) and its B (the other register set) are in
+  // flight.  Both halves of a loop iteration are single basic blocks whose
+  // prefetches are used unconditionally (the odd half of the last pair
+  // re-loads the last stage), and the scheduling barriers keep the loads
+  // ahead of the MFMAs and the waits for them behind.
+  const int nst = K / kStageK;
+  load_b(0, bp, sp0, sp1);
+  MFMA_LOAD_A(0);
+  MFMA_STORE_A(0);
+  __syncthreads();
+  int st = 0;
+  for (; st + 1 < nst; st += 2) {
+    // even stage: LDS buffer 0, register set bp; stage st+1 -> buffer 1 / bq2
+    MFMA_LOAD_A(st + 1);
+    load_b(st + 1, bq2, sq0, sq1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(0, bp, sp0, sp1);
+    __builtin_amdgcn_sched_barrier(0);
+    MFMA_STORE_A(1);
+    __syncthreads();
+    // odd stage: LDS buffer 1, register set bq2; stage st+2 -> buffer 0 / bp
+    const int nx = min(st + 2, nst - 1);
+    MFMA_LOAD_A(nx);
+    load_b(nx, bp, sp0, sp1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(1, bq2, sq0, sq1);
+    __builtin_amdgcn_sched_barrier(0);
+    MFMA_STORE_A(0);
     __syncthreads();
   }
+  if (st < nst) compute(0, bp, sp0, sp1);  // odd stage count: the last stage
+#undef MFMA_LOAD_A
+#undef MFMA_STORE_A
 
   if (!tok_ok) return;
   float* orow = out + (int64_t)(p0 + tok) * out_cols;
   if (GATEUP) {
+    // row blocks 0..kRB/2-1 are gate rows, the next kRB/2 the matching up rows
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < kRB / 2; ++rb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int m = row0 + 32 * rb + 8 * g + 4 * half;
         float4 v;
-        v.x = silu_mul(acc[rb][4 * g + 0], acc[rb + 2][4 * g + 0]);
-        v.y = silu_mul(acc[rb][4 * g + 1], acc[rb + 2][4 * g + 1]);
-        v.z = silu_mul(acc[rb][4 * g + 2], acc[rb + 2][4 * g + 2]);
-        v.w = silu_mul(acc[rb][4 * g + 3], acc[rb + 2][4 * g + 3]);
+        v.x = silu_mul(acc[rb][4 * g + 0], acc[rb + kRB / 2][4 * g + 0]);
+        v.y = silu_mul(acc[rb][4 * g + 1], acc[rb + kRB / 2][4 * g + 1]);
+        v.z = silu_mul(acc[rb][4 * g + 2], acc[rb + kRB / 2][4 * g + 2]);
+        v.w = silu_mul(acc[rb][4 * g + 3], acc[rb + kRB / 2][4 * g + 3]);
         *(float4*)(orow + m) = v;
       }
   } else {
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
+    for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int m = row0 + 32 * rb + 8 * g + 4 * half;
@@ -390,7 +442,11 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 namespace moe {
 
-bool mfma_shape_ok(int H, int I) { return H % kStageK == 0 && I % kStageK == 0 && I % 64 == 0 && H % 128 == 0; }
+// K of both products in whole stages, whole row tiles (gate/up: I/128 tiles
+// of 128 gate + 128 up rows; down: H/256 tiles)
+bool mfma_shape_ok(int H, int I) {
+  return H % kStageK == 0 && I % kStageK == 0 && I % (kTileRows / 2) == 0 && H % kTileRows == 0;
+}
 
 // Workspace of the MFMA path after the h buffer: x terms, x scales, h terms,
 // h scales, tile plan.
