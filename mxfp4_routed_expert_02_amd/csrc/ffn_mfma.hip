@@ -346,30 +346,59 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[rb][i] = 0.0f;
 
-  // the MFMAs of one stage: 4 steps x kRB row blocks x 2 terms
+  // the MFMAs of one stage: 4 steps x kRB row blocks x 2 terms.  Each A
+  // fragment (16 bytes per lane from LDS) feeds two MFMAs (128 cycles), less
+  // than the LDS latency under load, so the reads run kAhead fragments ahead
+  // of their use in a rotating set of registers.
+  constexpr int kAhead = 3;
+  constexpr int kFrags = 4 * kRB;  // (step, row block), step-major
   auto compute = [&](int buf, const uint4 (&bb)[16], uint32_t s0, uint32_t s1) {
+    const uint8_t* a_base = &s_a[buf][n * kRowPitch + 16 * half];
+    uint32_t sa[kRB];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int rb = 0; rb < kRB; ++rb) sa[rb] = s_sc[buf][2 * (32 * rb + n) + half];
+    // fragment f = (s, rb): row 32 rb + n, 16-byte piece 2 s + half (block 2s+half of the stage row)
+    auto frag = [&](int f) { return *(const uint4*)(a_base + (32 * (f % kRB)) * kRowPitch + 32 * (f / kRB)); };
+    uint4 fr[kAhead + 1];
+#pragma unroll
+    for (int f = 0; f < kAhead; ++f) fr[f] = frag(f);
+#pragma unroll
+    for (int f = 0; f < kFrags; ++f) {
+      if (f + kAhead < kFrags) fr[(f + kAhead) % (kAhead + 1)] = frag(f + kAhead);
+      const int s = f / kRB, rb = f % kRB;
       v8i_t B0, B1;
       B0[0] = bb[4 * s].x; B0[1] = bb[4 * s].y; B0[2] = bb[4 * s].z; B0[3] = bb[4 * s].w;
       B0[4] = bb[4 * s + 1].x; B0[5] = bb[4 * s + 1].y; B0[6] = bb[4 * s + 1].z; B0[7] = bb[4 * s + 1].w;
       B1[0] = bb[4 * s + 2].x; B1[1] = bb[4 * s + 2].y; B1[2] = bb[4 * s + 2].z; B1[3] = bb[4 * s + 2].w;
       B1[4] = bb[4 * s + 3].x; B1[5] = bb[4 * s + 3].y; B1[6] = bb[4 * s + 3].z; B1[7] = bb[4 * s + 3].w;
-#pragma unroll
-      for (int rb = 0; rb < kRB; ++rb) {
-        const int r = 32 * rb + n;
-        // block (2s + half) of the stage row: 16-byte piece 2s + half
-        const uint4 wa = *(const uint4*)(&s_a[buf][r * kRowPitch + 16 * (2 * s + half)]);
-        v8i_t A;
-        A[0] = wa.x; A[1] = wa.y; A[2] = wa.z; A[3] = wa.w;
-        A[4] = 0; A[5] = 0; A[6] = 0; A[7] = 0;
-        const uint32_t sa = s_sc[buf][2 * r + half];
-        if (s == 0) acc[rb] = mfma_step<0>(A, B0, B1, acc[rb], sa, s0, s1);
-        else if (s == 1) acc[rb] = mfma_step<1>(A, B0, B1, acc[rb], sa, s0, s1);
-        else if (s == 2) acc[rb] = mfma_step<2>(A, B0, B1, acc[rb], sa, s0, s1);
-        else acc[rb] = mfma_step<3>(A, B0, B1, acc[rb], sa, s0, s1);
-      }
+      const uint4 wa = fr[f % (kAhead + 1)];
+      v8i_t A;
+      A[0] = wa.x; A[1] = wa.y; A[2] = wa.z; A[3] = wa.w;
+      A[4] = 0; A[5] = 0; A[6] = 0; A[7] = 0;
+      if (s == 0) acc[rb] = mfma_step<0>(A, B0, B1, acc[rb], sa[rb], s0, s1);
+      else if (s == 1) acc[rb] = mfma_step<1>(A, B0, B1, acc[rb], sa[rb], s0, s1);
+      else if (s == 2) acc[rb] = mfma_step<2>(A, B0, B1, acc[rb], sa[rb], s0, s1);
+      else acc[rb] = mfma_step<3>(A, B0, B1, acc[rb], sa[rb], s0, s1);
     }
+  };
+
+  // Issue order of one stage (masks: 0x100 LDS read, 0x008 MFMA, 0x020
+  // global read, 0x200 LDS write): the scale reads and the first kAhead
+  // fragments, then two MFMAs, one fragment read and one of the next
+  // stage's global loads at a time, and the A stores last.  Spreading the
+  // 27 global loads over the MFMAs keeps the wave from stalling on the
+  // address path with its MFMAs queued behind them.
+  constexpr int kLoads = 9 + 18;  // A pieces + scales, B pieces + scale words
+  auto stage_schedule = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x100, kRB / 2 + kAhead, 0);
+#pragma unroll
+    for (int f = 0; f + kAhead < kFrags; ++f) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (f < kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kAhead, 0);
+    __builtin_amdgcn_sched_group_barrier(0x200, 9, 0);
   };
 
   // Pipeline: while the MFMAs of stage st run on LDS buffer st&1 and B
@@ -377,8 +406,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // other buffer after the MFMAs) and its B (the other register set) are in
   // flight.  Both halves of a loop iteration are single basic blocks whose
   // prefetches are used unconditionally (the odd half of the last pair
-  // re-loads the last stage), and the scheduling barriers keep the loads
-  // ahead of the MFMAs and the waits for them behind.
+  // re-loads the last stage), so the stage schedule above applies to each.
   const int nst = K / kStageK;
   load_b(0, bp, sp0, sp1);
   MFMA_LOAD_A(0);
@@ -389,19 +417,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // even stage: LDS buffer 0, register set bp; stage st+1 -> buffer 1 / bq2
     MFMA_LOAD_A(st + 1);
     load_b(st + 1, bq2, sq0, sq1);
-    __builtin_amdgcn_sched_barrier(0);
     compute(0, bp, sp0, sp1);
-    __builtin_amdgcn_sched_barrier(0);
     MFMA_STORE_A(1);
+    stage_schedule();
     __syncthreads();
     // odd stage: LDS buffer 1, register set bq2; stage st+2 -> buffer 0 / bp
     const int nx = min(st + 2, nst - 1);
     MFMA_LOAD_A(nx);
     load_b(nx, bp, sp0, sp1);
-    __builtin_amdgcn_sched_barrier(0);
     compute(1, bq2, sq0, sq1);
-    __builtin_amdgcn_sched_barrier(0);
     MFMA_STORE_A(0);
+    stage_schedule();
     __syncthreads();
   }
   if (st < nst) compute(0, bp, sp0, sp1);  // odd stage count: the last stage
