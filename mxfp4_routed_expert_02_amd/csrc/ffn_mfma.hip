@@ -32,10 +32,15 @@
 // conflicts) and shared by the 4 waves; each wave streams its own B into
 // registers one stage ahead.  256 rows per tile halve the B bytes per MFMA
 // against 128, which keeps the vector-memory path under the MFMA time.
-// Tiles are numbered weight-tile-major within (expert, token tile) and
-// spread so that each XCD takes a contiguous range of tiles: tiles sharing
-// a token tile and neighbouring weight tiles run on the same L2.
+// A tile's 128 token slots form 4 groups of 32; a tile whose expert rows
+// fill only 1 or 2 groups runs with the 4 waves splitting the row blocks
+// instead (2 or 4 blocks each, gate blocks kept with their up blocks), so
+// MFMA work follows the routed rows rather than the padded tile.  The plan
+// orders (expert, token tile) pairs heaviest first and deals them to the 8
+// XCDs in turn; each XCD runs its pairs' weight tiles consecutively, so
+// tiles sharing a token tile share that XCD's L2.
 #include <climits>
+#include <type_traits>
 
 #include "moe_internal.h"
 
@@ -155,40 +160,82 @@ __global__ __launch_bounds__(kThreads) void mfma_prep_kernel(const uint16_t* __r
                                                             uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
                                                             int32_t* __restrict__ plan) {
   if (blockIdx.x == 0) {
-    __shared__ int s_wave[kThreads / 64];
+    // Tile plan: the (slot, token tile) pairs of experts with more than
+    // kRegRows rows, heaviest first: tiles with 4 token groups (65..128
+    // rows), then 2 (33..64), then 1 (5..32).  The GEMM deals pair g to XCD
+    // g % 8, so every XCD gets a near-equal share of each class and starts
+    // with its heaviest tiles.  Within a class pairs keep slot order, so
+    // the plan is deterministic.
+    __shared__ int s_part[3][kThreads / 64];
     const int na = active[0];
-    int base = 0;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // pairs of slot a by class: c[0] (4 groups), c[1] (2 groups), c[2] (1 group)
+    auto classes = [&](int a, int (&c)[3]) {
+      c[0] = c[1] = c[2] = 0;
+      if (a >= na) return;
+      const int e = active[1 + a];
+      const int cnt = offsets[e + 1] - offsets[e];
+      if (cnt <= kRegRows) return;
+      const int nt = (cnt + kTileTok - 1) / kTileTok;
+      const int last = cnt - (nt - 1) * kTileTok;
+      c[0] = nt - 1 + (last > 64);
+      c[1] = (last > 32 && last <= 64);
+      c[2] = (last <= 32);
+    };
+    // block-wide exclusive scan of three counters; returns the block totals
+    auto scan3 = [&](int (&c)[3], int (&before)[3], int (&total)[3]) {
+#pragma unroll
+      for (int q = 0; q < 3; ++q) {
+        int v = c[q];
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int u = __shfl_up(v, o, 64);
+          if (lane >= o) v += u;
+        }
+        if (lane == 63) s_part[q][wave] = v;
+        before[q] = v - c[q];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 3; ++q) {
+        total[q] = 0;
+        for (int w2 = 0; w2 < kThreads / 64; ++w2) {
+          if (w2 < wave) before[q] += s_part[q][w2];
+          total[q] += s_part[q][w2];
+        }
+      }
+      __syncthreads();
+    };
+    // pass 1: class totals
+    int tot[3] = {0, 0, 0};
+    for (int a0 = 0; a0 < na; a0 += kThreads) {
+      int c[3], bf[3], t[3];
+      classes(a0 + threadIdx.x, c);
+      scan3(c, bf, t);
+      for (int q = 0; q < 3; ++q) tot[q] += t[q];
+    }
+    // pass 2: positions
+    int base[3] = {0, tot[0], tot[0] + tot[1]};
     for (int a0 = 0; a0 < na; a0 += kThreads) {
       const int a = a0 + threadIdx.x;
-      int nt = 0, e = 0;
-      if (a < na) {
-        e = active[1 + a];
+      int c[3], bf[3], t[3];
+      classes(a, c);
+      scan3(c, bf, t);
+      if (c[0] + c[1] + c[2] > 0) {
+        const int e = active[1 + a];
         const int cnt = offsets[e + 1] - offsets[e];
-        nt = cnt > kRegRows ? (cnt + kTileTok - 1) / kTileTok : 0;
+        const int nt = (cnt + kTileTok - 1) / kTileTok;
+        for (int j = 0; j < nt; ++j) {
+          const int r = min(cnt - j * kTileTok, kTileTok);
+          const int q = r > 64 ? 0 : r > 32 ? 1 : 2;
+          const int g = base[q] + bf[q]++;
+          plan[1 + 2 * g] = a;
+          plan[2 + 2 * g] = j;
+        }
       }
-      // block-wide exclusive scan of nt
-      int v = nt;
-      const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int u = __shfl_up(v, o, 64);
-        if (lane >= o) v += u;
-      }
-      if (lane == 63) s_wave[wave] = v;
-      __syncthreads();
-      int before = base;
-      for (int w = 0; w < wave; ++w) before += s_wave[w];
-      int total = 0;
-      for (int w = 0; w < kThreads / 64; ++w) total += s_wave[w];
-      before += v - nt;
-      for (int j = 0; j < nt; ++j) {
-        plan[1 + 2 * (before + j)] = a;
-        plan[2 + 2 * (before + j)] = j;
-      }
-      base += total;
-      __syncthreads();
+      for (int q = 0; q < 3; ++q) base[q] += t[q];
     }
-    if (threadIdx.x == 0) plan[0] = base;
+    if (threadIdx.x == 0) plan[0] = tot[0] + tot[1] + tot[2];
     return;
   }
   const int nblk = H >> 5;
@@ -247,14 +294,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const uint32_t qrow = (uint32_t)K >> 1;     // FP4 bytes per weight row
   const int nsb = K >> 5;                     // scale bytes per weight row
 
-  // tile index: each XCD (blockIdx % 8) takes a contiguous range of tiles
-  const int W = plan[0] * m_tiles;
-  const int per_xcd = (W + 7) >> 3;
+  // tile: XCD x = blockIdx % 8 runs pairs g = x, x + 8, ... of the plan
+  // (heaviest first), each as m_tiles consecutive weight tiles
   const int bx = blockIdx.x;
-  if ((bx >> 3) >= per_xcd) return;
-  const int wt = (bx & 7) * per_xcd + (bx >> 3);
-  if (wt >= W) return;
-  const int pair = wt / m_tiles, mt = wt - pair * m_tiles;
+  const int q8 = (bx >> 3) / m_tiles, mt = (bx >> 3) - q8 * m_tiles;
+  const int pair = (bx & 7) + 8 * q8;
+  if (pair >= plan[0]) return;
   const int slot = plan[1 + 2 * pair], ntile = plan[2 + 2 * pair];
   const int e = active[1 + slot];
   const int p0 = offsets[e], cnt = offsets[e + 1] - p0;
@@ -312,154 +357,181 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     *(uint2*)(&s_sc[BUF][2 * tid]) = scales_by_half(as2);                          \
   } while (0)
 
-  // this lane's B row (token); rows past the expert's count re-read its last row
-  const int n = lane & 31, half = lane >> 5;
-  const int tok = tok0 + wave * 32 + n;
-  const bool tok_ok = tok < cnt;
-  const int p = p0 + (tok_ok ? tok : cnt - 1);
-  const int64_t brow = GATEUP ? (int64_t)(sorted_rows[p] / k) : (int64_t)p;
-  const uint8_t* b0 = bq + (brow * 2 + 0) * K + 32 * half;
-  const uint8_t* b1 = bq + (brow * 2 + 1) * K + 32 * half;
-  const uint32_t* bs0 = (const uint32_t*)(bs + (brow * 2 + 0) * nsb) + half;
-  const uint32_t* bs1 = (const uint32_t*)(bs + (brow * 2 + 1) * nsb) + half;
+  // Token groups of 32 that hold routed rows: 1, 2 or 4 (3 runs as 4).
+  // With tg groups, wave w takes token group w % tg and 2*tg of the 8 row
+  // blocks: gate/up keeps each gate block with its up block (b and b+4).
+  const int rows_in_tile = min(cnt - tok0, kTileTok);
+  const int tg = rows_in_tile <= 32 ? 1 : rows_in_tile <= 64 ? 2 : 4;
 
-  // B of one stage in two register sets used in turn: [step][piece]
-  // (pieces 0,1 = term 1, pieces 2,3 = term 2) and the two scale words
-  uint4 bp[16], bq2[16];
-  uint32_t sp0, sp1, sq0, sq1;
-  auto load_b = [&](int st, uint4 (&bb)[16], uint32_t& s0, uint32_t& s1) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int koff = st * kStageK + 64 * s;
-      bb[4 * s + 0] = *(const uint4*)(b0 + koff);
-      bb[4 * s + 1] = *(const uint4*)(b0 + koff + 16);
-      bb[4 * s + 2] = *(const uint4*)(b1 + koff);
-      bb[4 * s + 3] = *(const uint4*)(b1 + koff + 16);
-    }
-    s0 = bs0[2 * st];
-    s1 = bs1[2 * st];
-  };
+  auto body = [&](auto rbw_c) {
+    constexpr int RBW = decltype(rbw_c)::value;  // row blocks of this wave
+    constexpr int TG = RBW / 2;                  // token groups of the tile
+    // row block of slot j is rb_base + rel(j); rel(j) is a compile-time
+    // offset so LDS addresses fold to immediates (rb_base = 0 with 8 blocks)
+    const int rb_base = RBW == kRB ? 0 : (wave / TG) * (RBW / 2);
+    auto rel = [](int j) { return j < RBW / 2 ? j : kRB / 2 + (j - RBW / 2); };
+    auto rb_of = [&](int j) { return rb_base + rel(j); };
 
-  v16f_t acc[kRB];
-#pragma unroll
-  for (int rb = 0; rb < kRB; ++rb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[rb][i] = 0.0f;
+    // this lane's B row (token); rows past the expert's count re-read its last row
+    const int n = lane & 31, half = lane >> 5;
+    const int tok = tok0 + (wave % TG) * 32 + n;
+    const bool tok_ok = tok < cnt;
+    const int p = p0 + (tok_ok ? tok : cnt - 1);
+    const int64_t brow = GATEUP ? (int64_t)(sorted_rows[p] / k) : (int64_t)p;
+    const uint8_t* b0 = bq + (brow * 2 + 0) * K + 32 * half;
+    const uint8_t* b1 = bq + (brow * 2 + 1) * K + 32 * half;
+    const uint32_t* bs0 = (const uint32_t*)(bs + (brow * 2 + 0) * nsb) + half;
+    const uint32_t* bs1 = (const uint32_t*)(bs + (brow * 2 + 1) * nsb) + half;
 
-  // the MFMAs of one stage: 4 steps x kRB row blocks x 2 terms.  Each A
-  // fragment (16 bytes per lane from LDS) feeds two MFMAs (128 cycles), less
-  // than the LDS latency under load, so the reads run kAhead fragments ahead
-  // of their use in a rotating set of registers.
-  constexpr int kAhead = 3;
-  constexpr int kFrags = 4 * kRB;  // (step, row block), step-major
-  auto compute = [&](int buf, const uint4 (&bb)[16], uint32_t s0, uint32_t s1) {
-    const uint8_t* a_base = &s_a[buf][n * kRowPitch + 16 * half];
-    uint32_t sa[kRB];
+    // B of one stage in two register sets used in turn: [step][piece]
+    // (pieces 0,1 = term 1, pieces 2,3 = term 2) and the two scale words
+    uint4 bp[16], bq2[16];
+    uint32_t sp0, sp1, sq0, sq1;
+    auto load_b = [&](int st, uint4 (&bb)[16], uint32_t& s0, uint32_t& s1) {
 #pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) sa[rb] = s_sc[buf][2 * (32 * rb + n) + half];
-    // fragment f = (s, rb): row 32 rb + n, 16-byte piece 2 s + half (block 2s+half of the stage row)
-    auto frag = [&](int f) { return *(const uint4*)(a_base + (32 * (f % kRB)) * kRowPitch + 32 * (f / kRB)); };
-    uint4 fr[kAhead + 1];
-#pragma unroll
-    for (int f = 0; f < kAhead; ++f) fr[f] = frag(f);
-#pragma unroll
-    for (int f = 0; f < kFrags; ++f) {
-      if (f + kAhead < kFrags) fr[(f + kAhead) % (kAhead + 1)] = frag(f + kAhead);
-      const int s = f / kRB, rb = f % kRB;
-      v8i_t B0, B1;
-      B0[0] = bb[4 * s].x; B0[1] = bb[4 * s].y; B0[2] = bb[4 * s].z; B0[3] = bb[4 * s].w;
-      B0[4] = bb[4 * s + 1].x; B0[5] = bb[4 * s + 1].y; B0[6] = bb[4 * s + 1].z; B0[7] = bb[4 * s + 1].w;
-      B1[0] = bb[4 * s + 2].x; B1[1] = bb[4 * s + 2].y; B1[2] = bb[4 * s + 2].z; B1[3] = bb[4 * s + 2].w;
-      B1[4] = bb[4 * s + 3].x; B1[5] = bb[4 * s + 3].y; B1[6] = bb[4 * s + 3].z; B1[7] = bb[4 * s + 3].w;
-      const uint4 wa = fr[f % (kAhead + 1)];
-      v8i_t A;
-      A[0] = wa.x; A[1] = wa.y; A[2] = wa.z; A[3] = wa.w;
-      A[4] = 0; A[5] = 0; A[6] = 0; A[7] = 0;
-      if (s == 0) acc[rb] = mfma_step<0>(A, B0, B1, acc[rb], sa[rb], s0, s1);
-      else if (s == 1) acc[rb] = mfma_step<1>(A, B0, B1, acc[rb], sa[rb], s0, s1);
-      else if (s == 2) acc[rb] = mfma_step<2>(A, B0, B1, acc[rb], sa[rb], s0, s1);
-      else acc[rb] = mfma_step<3>(A, B0, B1, acc[rb], sa[rb], s0, s1);
-    }
-  };
+      for (int s = 0; s < 4; ++s) {
+        const int koff = st * kStageK + 64 * s;
+        bb[4 * s + 0] = *(const uint4*)(b0 + koff);
+        bb[4 * s + 1] = *(const uint4*)(b0 + koff + 16);
+        bb[4 * s + 2] = *(const uint4*)(b1 + koff);
+        bb[4 * s + 3] = *(const uint4*)(b1 + koff + 16);
+      }
+      s0 = bs0[2 * st];
+      s1 = bs1[2 * st];
+    };
 
-  // Issue order of one stage (masks: 0x100 LDS read, 0x008 MFMA, 0x020
-  // global read, 0x200 LDS write): the scale reads and the first kAhead
-  // fragments, then two MFMAs, one fragment read and one of the next
-  // stage's global loads at a time, and the A stores last.  Spreading the
-  // 27 global loads over the MFMAs keeps the wave from stalling on the
-  // address path with its MFMAs queued behind them.
-  constexpr int kLoads = 9 + 18;  // A pieces + scales, B pieces + scale words
-  auto stage_schedule = [&]() {
-    __builtin_amdgcn_sched_group_barrier(0x100, kRB / 2 + kAhead, 0);
+    v16f_t acc[RBW];
 #pragma unroll
-    for (int f = 0; f + kAhead < kFrags; ++f) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (f < kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kAhead, 0);
-    __builtin_amdgcn_sched_group_barrier(0x200, 9, 0);
-  };
+    for (int j = 0; j < RBW; ++j)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[j][i] = 0.0f;
 
-  // Pipeline: while the MFMAs of stage st run on LDS buffer st&1 and B
-  // register set st&1, the A pieces of stage st+1 (registers, stored to the
-  // other buffer after the MFMAs) and its B (the other register set) are in
-  // flight.  Both halves of a loop iteration are single basic blocks whose
-  // prefetches are used unconditionally (the odd half of the last pair
-  // re-loads the last stage), so the stage schedule above applies to each.
-  const int nst = K / kStageK;
-  load_b(0, bp, sp0, sp1);
-  MFMA_LOAD_A(0);
-  MFMA_STORE_A(0);
-  __syncthreads();
-  int st = 0;
-  for (; st + 1 < nst; st += 2) {
-    // even stage: LDS buffer 0, register set bp; stage st+1 -> buffer 1 / bq2
-    MFMA_LOAD_A(st + 1);
-    load_b(st + 1, bq2, sq0, sq1);
-    compute(0, bp, sp0, sp1);
-    MFMA_STORE_A(1);
-    stage_schedule();
-    __syncthreads();
-    // odd stage: LDS buffer 1, register set bq2; stage st+2 -> buffer 0 / bp
-    const int nx = min(st + 2, nst - 1);
-    MFMA_LOAD_A(nx);
-    load_b(nx, bp, sp0, sp1);
-    compute(1, bq2, sq0, sq1);
+    // the MFMAs of one stage: 4 steps x RBW row blocks x 2 terms.  Each A
+    // fragment (16 bytes per lane from LDS) feeds two MFMAs (128 cycles),
+    // less than the LDS latency under load, so the reads run kAhead
+    // fragments ahead of their use in a rotating set of registers.
+    constexpr int kAhead = 3;
+    constexpr int kFrags = 4 * RBW;  // (step, row block), step-major
+    auto compute = [&](int buf, const uint4 (&bb)[16], uint32_t s0, uint32_t s1) {
+      const uint8_t* a_base = &s_a[buf][(32 * rb_base + n) * kRowPitch + 16 * half];
+      const uint32_t* sc_base = &s_sc[buf][2 * (32 * rb_base + n) + half];
+      uint32_t sa[RBW];
+#pragma unroll
+      for (int j = 0; j < RBW; ++j) sa[j] = sc_base[64 * rel(j)];
+      // fragment f = (s, j): row 32 rb_of(j) + n, 16-byte piece 2 s + half
+      // (block 2s+half of the stage row)
+      auto frag = [&](int f) {
+        return *(const uint4*)(a_base + (32 * rel(f % RBW)) * kRowPitch + 32 * (f / RBW));
+      };
+      uint4 fr[kAhead + 1];
+#pragma unroll
+      for (int f = 0; f < kAhead; ++f) fr[f] = frag(f);
+#pragma unroll
+      for (int f = 0; f < kFrags; ++f) {
+        if (f + kAhead < kFrags) fr[(f + kAhead) % (kAhead + 1)] = frag(f + kAhead);
+        const int s = f / RBW, j = f % RBW;
+        v8i_t B0, B1;
+        B0[0] = bb[4 * s].x; B0[1] = bb[4 * s].y; B0[2] = bb[4 * s].z; B0[3] = bb[4 * s].w;
+        B0[4] = bb[4 * s + 1].x; B0[5] = bb[4 * s + 1].y; B0[6] = bb[4 * s + 1].z; B0[7] = bb[4 * s + 1].w;
+        B1[0] = bb[4 * s + 2].x; B1[1] = bb[4 * s + 2].y; B1[2] = bb[4 * s + 2].z; B1[3] = bb[4 * s + 2].w;
+        B1[4] = bb[4 * s + 3].x; B1[5] = bb[4 * s + 3].y; B1[6] = bb[4 * s + 3].z; B1[7] = bb[4 * s + 3].w;
+        const uint4 wa = fr[f % (kAhead + 1)];
+        v8i_t A;
+        A[0] = wa.x; A[1] = wa.y; A[2] = wa.z; A[3] = wa.w;
+        A[4] = 0; A[5] = 0; A[6] = 0; A[7] = 0;
+        if (s == 0) acc[j] = mfma_step<0>(A, B0, B1, acc[j], sa[j], s0, s1);
+        else if (s == 1) acc[j] = mfma_step<1>(A, B0, B1, acc[j], sa[j], s0, s1);
+        else if (s == 2) acc[j] = mfma_step<2>(A, B0, B1, acc[j], sa[j], s0, s1);
+        else acc[j] = mfma_step<3>(A, B0, B1, acc[j], sa[j], s0, s1);
+      }
+    };
+
+    // Issue order of one stage (masks: 0x100 LDS read, 0x008 MFMA, 0x020
+    // global read, 0x200 LDS write): the scale reads and the first kAhead
+    // fragments, then two MFMAs, one fragment read and the next share of
+    // the next stage's global loads at a time, and the A stores last.
+    // Spreading the 27 global loads over the MFMAs keeps the wave from
+    // stalling on the address path with its MFMAs queued behind them.
+    constexpr int kLoads = 9 + 18;  // A pieces + scales, B pieces + scale words
+    constexpr int kSlots = kFrags - kAhead;
+    constexpr int kPer = (kLoads + kSlots - 1) / kSlots;
+    auto stage_schedule = [&]() {
+      __builtin_amdgcn_sched_group_barrier(0x100, (RBW + 1) / 2 + kAhead, 0);
+#pragma unroll
+      for (int f = 0; f < kSlots; ++f) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (f * kPer < kLoads) __builtin_amdgcn_sched_group_barrier(0x020, kPer, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * kAhead, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 9, 0);
+    };
+
+    // Pipeline: while the MFMAs of stage st run on LDS buffer st&1 and B
+    // register set st&1, the A pieces of stage st+1 (registers, stored to
+    // the other buffer after the MFMAs) and its B (the other register set)
+    // are in flight.  Both halves of a loop iteration are single basic
+    // blocks whose prefetches are used unconditionally (the odd half of the
+    // last pair re-loads the last stage), so the stage schedule applies to
+    // each.
+    const int nst = K / kStageK;
+    load_b(0, bp, sp0, sp1);
+    MFMA_LOAD_A(0);
     MFMA_STORE_A(0);
-    stage_schedule();
     __syncthreads();
-  }
-  if (st < nst) compute(0, bp, sp0, sp1);  // odd stage count: the last stage
+    int st = 0;
+    for (; st + 1 < nst; st += 2) {
+      // even stage: LDS buffer 0, register set bp; stage st+1 -> buffer 1 / bq2
+      MFMA_LOAD_A(st + 1);
+      load_b(st + 1, bq2, sq0, sq1);
+      compute(0, bp, sp0, sp1);
+      MFMA_STORE_A(1);
+      stage_schedule();
+      __syncthreads();
+      // odd stage: LDS buffer 1, register set bq2; stage st+2 -> buffer 0 / bp
+      const int nx = min(st + 2, nst - 1);
+      MFMA_LOAD_A(nx);
+      load_b(nx, bp, sp0, sp1);
+      compute(1, bq2, sq0, sq1);
+      MFMA_STORE_A(0);
+      stage_schedule();
+      __syncthreads();
+    }
+    if (st < nst) compute(0, bp, sp0, sp1);  // odd stage count: the last stage
+
+    if (!tok_ok) return;
+    float* orow = out + (int64_t)(p0 + tok) * out_cols;
+    if (GATEUP) {
+      // j < RBW/2: gate block rb_of(j); j + RBW/2: the matching up block
+#pragma unroll
+      for (int j = 0; j < RBW / 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int m = row0 + 32 * rb_of(j) + 8 * g + 4 * half;
+          float4 v;
+          v.x = silu_mul(acc[j][4 * g + 0], acc[j + RBW / 2][4 * g + 0]);
+          v.y = silu_mul(acc[j][4 * g + 1], acc[j + RBW / 2][4 * g + 1]);
+          v.z = silu_mul(acc[j][4 * g + 2], acc[j + RBW / 2][4 * g + 2]);
+          v.w = silu_mul(acc[j][4 * g + 3], acc[j + RBW / 2][4 * g + 3]);
+          *(float4*)(orow + m) = v;
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < RBW; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int m = row0 + 32 * rb_of(j) + 8 * g + 4 * half;
+          *(float4*)(orow + m) =
+              make_float4(acc[j][4 * g + 0], acc[j][4 * g + 1], acc[j][4 * g + 2], acc[j][4 * g + 3]);
+        }
+      }
+    }
+  };
+  if (tg == 1) body(std::integral_constant<int, 2>());
+  else if (tg == 2) body(std::integral_constant<int, 4>());
+  else body(std::integral_constant<int, 8>());
 #undef MFMA_LOAD_A
 #undef MFMA_STORE_A
-
-  if (!tok_ok) return;
-  float* orow = out + (int64_t)(p0 + tok) * out_cols;
-  if (GATEUP) {
-    // row blocks 0..kRB/2-1 are gate rows, the next kRB/2 the matching up rows
-#pragma unroll
-    for (int rb = 0; rb < kRB / 2; ++rb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int m = row0 + 32 * rb + 8 * g + 4 * half;
-        float4 v;
-        v.x = silu_mul(acc[rb][4 * g + 0], acc[rb + kRB / 2][4 * g + 0]);
-        v.y = silu_mul(acc[rb][4 * g + 1], acc[rb + kRB / 2][4 * g + 1]);
-        v.z = silu_mul(acc[rb][4 * g + 2], acc[rb + kRB / 2][4 * g + 2]);
-        v.w = silu_mul(acc[rb][4 * g + 3], acc[rb + kRB / 2][4 * g + 3]);
-        *(float4*)(orow + m) = v;
-      }
-  } else {
-#pragma unroll
-    for (int rb = 0; rb < kRB; ++rb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int m = row0 + 32 * rb + 8 * g + 4 * half;
-        *(float4*)(orow + m) =
-            make_float4(acc[rb][4 * g + 0], acc[rb][4 * g + 1], acc[rb][4 * g + 2], acc[rb][4 * g + 3]);
-      }
-  }
 }
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
@@ -509,8 +581,7 @@ hipError_t launch_mfma_gateup(const uint16_t* x, int T, int k, const moe_mxfp4_w
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int m_tiles = I / (kTileRows / 2);
-  const size_t max_tiles = mfma_max_pairs(T, k, w.num_experts) * m_tiles;
-  const unsigned grid = (unsigned)(8 * ((max_tiles + 7) / 8));
+  const unsigned grid = (unsigned)(8 * ((mfma_max_pairs(T, k, w.num_experts) + 7) / 8) * m_tiles);
   hipLaunchKernelGGL((mfma_ffn_kernel<true>), dim3(grid), dim3(kThreads), 0, s, w, k, offsets, sorted_rows, active,
                      plan, xq, xs, h, m_tiles);
   return hipGetLastError();
@@ -533,8 +604,7 @@ hipError_t launch_mfma_down(int T, int k, const moe_mxfp4_weights& w, const int3
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int m_tiles = H / kTileRows;
-  const size_t max_tiles = mfma_max_pairs(T, k, w.num_experts) * m_tiles;
-  const unsigned grid = (unsigned)(8 * ((max_tiles + 7) / 8));
+  const unsigned grid = (unsigned)(8 * ((mfma_max_pairs(T, k, w.num_experts) + 7) / 8) * m_tiles);
   hipLaunchKernelGGL((mfma_ffn_kernel<false>), dim3(grid), dim3(kThreads), 0, s, w, k, offsets, sorted_rows, active,
                      plan, hq, hs, y_rows, m_tiles);
   return hipGetLastError();

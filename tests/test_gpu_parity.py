@@ -66,6 +66,29 @@ def test_small_shapes(wl):
     _small_case(wl)
 
 
+def test_mfma_row_count_edges():
+    """Per-expert row counts at the edges of the GEMV/MFMA split (4, 5 rows) and
+    of the MFMA tile's 32-token groups and 128-token tiles: with k = 1, a +40
+    boost on one logit per token routes it, so every count is exact."""
+    counts = [1, 4, 5, 31, 32, 33, 64, 65, 97, 128, 129, 200]
+    E = len(counts)
+    T = sum(counts)
+    wl = synth.Workload("row_count_edges", E=E, H=512, I=256, k=1, T=T, pool=33, sub=33)
+    say(f"case {wl.name}: counts {counts}")
+    first = np.random.default_rng(1).permutation(np.repeat(np.arange(E), counts))
+    logits = synth.router_logits(0, wl)
+    logits[np.arange(T), first] += 40.0
+    assert np.array_equal(np.bincount(first, minlength=E), counts)
+    x = synth.activations_bf16(0, wl)
+    pool = device_pool(wl)
+    hpool = oracle.Pool(synth.expert_slabs(0, wl.pool, 0, 0, wl.E, wl.H, wl.I), wl.H, wl.I)
+    ref = oracle.layer(x, logits, wl.k, hpool, nthreads=NTH)
+    gpu = run_gpu_layer(wl, pool, x, logits)
+    check_routing(gpu, ref, wl.E)
+    assert_close(gpu["y_rows"], ref["y_rows"], "y_rows")
+    assert_close(gpu["out"], ref["out"], "out")
+
+
 def test_empty_batch_is_a_no_op():
     wl = synth.Workload("empty", E=8, H=64, I=32, k=2, T=0, pool=29, sub=29)
     pool = device_pool(wl)
