@@ -271,8 +271,66 @@ __device__ __forceinline__ uint32_t load1(__amdgpu_buffer_rsrc_t r, uint32_t off
 // of block b at [q][b]), so consecutive lanes read consecutive 16 bytes, and
 // every block read from LDS serves all U rows of the iteration.
 //
-// grid: max_active * blocks_per_expert blocks of 4 waves; wave w of block b
-// of an expert runs row-iterations [(4b + w) * ipw, (4b + w + 1) * ipw).
+// Work items are (expert slot, block b of the expert); wave w of item b runs
+// row-iterations [(4b + w) * ipw, (4b + w + 1) * ipw).  One token: one block
+// per item, slot = blockIdx / blocks_per_expert over the active list.
+// Several tokens: `list` holds the slots of this kernel's row-count class,
+// and a grid sized to the machine strides over list[0] * blocks_per_expert
+// items, so the work spreads over the experts that exist, not the upper
+// bound of them.
+
+// Slots of the experts with exactly one routed row (l1) and with 2 ..
+// kRegRows rows (l4), in slot order: l[0] = count, l[1..] = slots.  One block.
+__global__ __launch_bounds__(kThreads) void small_lists_kernel(const int32_t* __restrict__ offsets,
+                                                              const int32_t* __restrict__ active,
+                                                              int32_t* __restrict__ l1, int32_t* __restrict__ l4) {
+  __shared__ int s_part[2][kWaves];
+  const int na = active[0];
+  const int lane = threadIdx.x & (MOE_WAVE - 1), wave = threadIdx.x / MOE_WAVE;
+  int base1 = 0, base4 = 0;
+  for (int a0 = 0; a0 < na; a0 += kThreads) {
+    const int a = a0 + threadIdx.x;
+    int f1 = 0, f4 = 0;
+    if (a < na) {
+      const int e = active[1 + a];
+      const int cnt = offsets[e + 1] - offsets[e];
+      f1 = cnt == 1;
+      f4 = cnt >= 2 && cnt <= kRegRows;
+    }
+    int v1 = f1, v4 = f4;
+#pragma unroll
+    for (int o = 1; o < MOE_WAVE; o <<= 1) {
+      const int u1 = __shfl_up(v1, o, MOE_WAVE), u4 = __shfl_up(v4, o, MOE_WAVE);
+      if (lane >= o) {
+        v1 += u1;
+        v4 += u4;
+      }
+    }
+    if (lane == MOE_WAVE - 1) {
+      s_part[0][wave] = v1;
+      s_part[1][wave] = v4;
+    }
+    __syncthreads();
+    int b1 = base1 + v1 - f1, b4 = base4 + v4 - f4, t1 = 0, t4 = 0;
+    for (int w2 = 0; w2 < kWaves; ++w2) {
+      if (w2 < wave) {
+        b1 += s_part[0][w2];
+        b4 += s_part[1][w2];
+      }
+      t1 += s_part[0][w2];
+      t4 += s_part[1][w2];
+    }
+    if (f1) l1[1 + b1] = a;
+    if (f4) l4[1 + b4] = a;
+    base1 += t1;
+    base4 += t4;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    l1[0] = base1;
+    l4[0] = base4;
+  }
+}
 
 
 // Experts whose row count lies in [cnt_lo, cnt_hi] run here, MT rows at a
@@ -282,15 +340,17 @@ __device__ __forceinline__ uint32_t load1(__amdgpu_buffer_rsrc_t r, uint32_t off
 template <int J, int U, int MT, int NB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void gateup_gemv_reg_kernel(
     const uint16_t* __restrict__ x, int k, moe_mxfp4_weights w, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ sorted_rows, const int32_t* __restrict__ active, float* __restrict__ h, int lg_rt,
-    int ipw, int blocks_per_expert, int cnt_lo, int cnt_hi) {
+    const int32_t* __restrict__ sorted_rows, const int32_t* __restrict__ active, const int32_t* __restrict__ list,
+    float* __restrict__ h, int lg_rt, int ipw, int blocks_per_expert, int cnt_lo, int cnt_hi) {
   extern __shared__ uint4 s_x4[];  // [MT][4][nb]
-  const int slot = blockIdx.x / blocks_per_expert;
+  const int n_items = list ? list[0] * blocks_per_expert : (int)gridDim.x;
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+  const int slot = list ? list[1 + item / blocks_per_expert] : item / blocks_per_expert;
   if (slot >= active[0]) return;
   const int e = active[1 + slot];
   const int p0 = offsets[e];
   const int cnt = offsets[e + 1] - p0;
-  if (cnt < cnt_lo || cnt > cnt_hi) return;
+  if (cnt < cnt_lo || cnt > cnt_hi) continue;
   // NB > 0: the row's block count is a compile-time constant (so are the LDS
   // and buffer offsets); NB == 0: taken from the weights at run time
   const int I = w.inter, nb = NB > 0 ? NB : (w.hidden >> 5), H = 32 * nb;
@@ -299,7 +359,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int G = 1 << lg, rpi = MOE_WAVE >> lg, rows_it = rpi * U;
   const int li = lane & (G - 1), gi = lane >> lg;
   const int total_iters = (I + rows_it - 1) / rows_it;
-  const int it0 = ((blockIdx.x - slot * blocks_per_expert) * kWaves + wave) * ipw;
+  const int it0 = ((item % blocks_per_expert) * kWaves + wave) * ipw;
   const int it1 = min(total_iters, it0 + ipw);
   const uint32_t qrow = (uint32_t)H >> 1;
   const int64_t eo = (int64_t)e * w.expert_stride;
@@ -394,27 +454,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       }
     }
   }
+  }
 }
 
 template <int J, int U, int MT, int NB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void down_gemv_reg_kernel(
     const float* __restrict__ h, moe_mxfp4_weights w, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ active, float* __restrict__ y_rows, int lg_rt, int ipw, int blocks_per_expert,
-    int cnt_lo, int cnt_hi) {
+    const int32_t* __restrict__ active, const int32_t* __restrict__ list, float* __restrict__ y_rows, int lg_rt,
+    int ipw, int blocks_per_expert, int cnt_lo, int cnt_hi) {
   extern __shared__ float4 s_h4[];  // [MT][8][nb]
-  const int slot = blockIdx.x / blocks_per_expert;
+  const int n_items = list ? list[0] * blocks_per_expert : (int)gridDim.x;
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+  const int slot = list ? list[1 + item / blocks_per_expert] : item / blocks_per_expert;
   if (slot >= active[0]) return;
   const int e = active[1 + slot];
   const int p0 = offsets[e];
   const int cnt = offsets[e + 1] - p0;
-  if (cnt < cnt_lo || cnt > cnt_hi) return;
+  if (cnt < cnt_lo || cnt > cnt_hi) continue;
   const int H = w.hidden, nb = NB > 0 ? NB : (w.inter >> 5), I = 32 * nb;
   const int lg = NB > 0 ? ctz_const(NB) : lg_rt;
   const int lane = threadIdx.x & (MOE_WAVE - 1), wave = threadIdx.x / MOE_WAVE;
   const int G = 1 << lg, rpi = MOE_WAVE >> lg, rows_it = rpi * U;
   const int li = lane & (G - 1), gi = lane >> lg;
   const int total_iters = (H + rows_it - 1) / rows_it;
-  const int it0 = ((blockIdx.x - slot * blocks_per_expert) * kWaves + wave) * ipw;
+  const int it0 = ((item % blocks_per_expert) * kWaves + wave) * ipw;
   const int it1 = min(total_iters, it0 + ipw);
   const uint32_t qrow = (uint32_t)I >> 1;
   const int64_t eo = (int64_t)e * w.expert_stride;
@@ -499,6 +562,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       }
     }
   }
+  }
 }
 
 constexpr size_t kMaxLds = 65536;
@@ -552,7 +616,82 @@ GemvGrid gemv_grid(int iters_per_expert, int max_active, int waves_per_simd) {
   return {ipw, bpe};
 }
 
+// Several tokens: about 32 blocks (128 waves) per expert, so a few dozen
+// small experts already fill the machine; the grid strides over the items.
+GemvGrid multi_grid(int iters_per_expert) {
+  const int ipw = max(1, (iters_per_expert + 127) / 128);
+  return {ipw, (iters_per_expert + kWaves * ipw - 1) / (kWaves * ipw)};
+}
+constexpr int kMultiGridCap = 2048;  // blocks of a grid-stride GEMV launch
+
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct GemvArgs {
+  const uint16_t* x;
+  int k;
+  const moe_mxfp4_weights* w;
+  const int32_t *offsets, *sorted_rows, *active;
+  float *h, *y_rows;
+  hipStream_t s;
+};
+
+// Register gate/up GEMV for experts with lo..hi rows, MT rows per weight pass.
+template <int MT>
+void gateup_reg(const GemvArgs& a, const GemvShape& sh, const GemvGrid& gg, dim3 grid, const int32_t* list, int lo,
+                int hi) {
+  const int H = a.w->hidden;
+  const size_t lds = (size_t)MT * H * 2;
+#define GU(JJ, UU, NB)                                                                                          \
+  hipLaunchKernelGGL((gateup_gemv_reg_kernel<JJ, UU, MT, NB>), grid, dim3(kThreads), lds, a.s, a.x, a.k, *a.w, \
+                     a.offsets, a.sorted_rows, a.active, list, a.h, sh.lg, gg.ipw, gg.blocks_per_expert, lo, hi)
+  if (H == 7168) {
+    GU(7, kGateU224, 224);
+    return;
+  }
+  switch (sh.J) {
+    case 1: GU(1, 4, 0); break;
+    case 2: GU(2, 2, 0); break;
+    case 3: GU(3, 2, 0); break;
+    case 4: GU(4, 1, 0); break;
+    case 5: GU(5, 1, 0); break;
+    case 6: GU(6, 1, 0); break;
+    case 7: GU(7, 1, 0); break;
+    default: GU(8, 1, 0); break;
+  }
+#undef GU
+}
+
+// Register down GEMV for experts with lo..hi rows, MT rows per weight pass.
+template <int MT>
+void down_reg(const GemvArgs& a, const GemvShape& sh, const GemvGrid& gg, dim3 grid, const int32_t* list, int lo,
+              int hi) {
+  const int I = a.w->inter;
+  const size_t lds = (size_t)MT * I * 4;
+#define DN(JJ, UU, NB)                                                                                              \
+  hipLaunchKernelGGL((down_gemv_reg_kernel<JJ, UU, MT, NB>), grid, dim3(kThreads), lds, a.s, a.h, *a.w, a.offsets, \
+                     a.active, list, a.y_rows, sh.lg, gg.ipw, gg.blocks_per_expert, lo, hi)
+  if (I == 1536) {
+    DN(3, kDownU48, 48);
+    return;
+  }
+  switch (sh.J) {
+    case 1: DN(1, 8, 0); break;
+    case 2: DN(2, 4, 0); break;
+    case 3: DN(3, 4, 0); break;
+    case 4: DN(4, 2, 0); break;
+    case 5: DN(5, 1, 0); break;
+    case 6: DN(6, 1, 0); break;
+    case 7: DN(7, 1, 0); break;
+    default: DN(8, 1, 0); break;
+  }
+#undef DN
+}
+
+// Class lists of the register GEMVs (several tokens): 2 x (1 + max_active).
+size_t lists_bytes(int T, int k, int E) {
+  const size_t R = (size_t)T * k, mx = R < (size_t)E ? R : (size_t)E;
+  return align_up(2 * (1 + mx) * sizeof(int32_t), 256);
+}
 
 }  // namespace
 
@@ -560,6 +699,7 @@ namespace moe {
 
 size_t expert_ffn_workspace(int T, int k, int E, int H, int I) {
   size_t b = align_up((size_t)T * k * I * sizeof(float), 256);  // h[R][I]
+  if (T > 1) b += lists_bytes(T, k, E);
   if (T > 1 && mfma_shape_ok(H, I)) b += mfma_workspace(T, k, E, H, I);
   return b;
 }
@@ -571,52 +711,50 @@ hipError_t launch_expert_ffn(const uint16_t* x, int T, int k, const moe_mxfp4_we
   const int R = T * k, E = w.num_experts, H = w.hidden, I = w.inter;
   const int max_active = R < E ? R : E;
   float* hbuf = (float*)ws;
-  // One token: every expert runs on the register path (its token loop also
-  // covers an id repeated within the token).  Several tokens: single-row
-  // experts take the register path, the others the LDS path.
-  const GemvShape sg = gemv_shape(H >> 5, true), sd = gemv_shape(I >> 5, false);
-  const bool reg_g = sg.ok, reg_d = sd.ok;
-  // Register path: experts with one row (MT = 1) and with 2..kRegRows rows
+  // Register GEMVs: experts with one row (MT = 1) and with 2..kRegRows rows
   // (MT = kRegRows, same per-row arithmetic); a single token sends every
   // expert through MT = 1 (its row loop covers an id repeated in the token).
-  // Experts with more rows take the LDS path.
+  // Experts with more rows take the grouped GEMM (MFMA) when the shape
+  // allows it, else the LDS GEMV.  Shapes the register layout cannot take
+  // (more than 8 blocks per lane) run on the LDS GEMV throughout.
+  const GemvShape sg = gemv_shape(H >> 5, true), sd = gemv_shape(I >> 5, false);
+  const bool reg_g = sg.ok, reg_d = sd.ok;
 
   hipError_t err = hipSuccess;
-  if (reg_g) {
-    const int rows_it = (64 >> sg.lg) * sg.U;
-    GemvGrid gg = gemv_grid((I + rows_it - 1) / rows_it, max_active, H == 7168 ? 4 : 2);
-    const dim3 g(max_active * gg.blocks_per_expert), b(kThreads);
-#define GU_REG(JJ, UU, MM, LO, HI)                                                                                \
-  hipLaunchKernelGGL((gateup_gemv_reg_kernel<JJ, UU, MM, 0>), g, b, (size_t)MM * H * 2, s, x, k, w, offsets,     \
-                     sorted_rows, active, hbuf, sg.lg, gg.ipw, gg.blocks_per_expert, LO, HI)
-#define GU_ALL(MM, LO, HI)                                                                                    \
-  if (H == 7168) {                                                                                            \
-    hipLaunchKernelGGL((gateup_gemv_reg_kernel<7, kGateU224, MM, 224>), g, b, (size_t)MM * H * 2, s, x, k, w, offsets, \
-                       sorted_rows, active, hbuf, sg.lg, gg.ipw, gg.blocks_per_expert, LO, HI);               \
-  } else                                    \
-  switch (sg.J) {                           \
-    case 1: GU_REG(1, 4, MM, LO, HI); break; \
-    case 2: GU_REG(2, 2, MM, LO, HI); break; \
-    case 3: GU_REG(3, 2, MM, LO, HI); break; \
-    case 4: GU_REG(4, 1, MM, LO, HI); break; \
-    case 5: GU_REG(5, 1, MM, LO, HI); break; \
-    case 6: GU_REG(6, 1, MM, LO, HI); break; \
-    case 7: GU_REG(7, 1, MM, LO, HI); break; \
-    default: GU_REG(8, 1, MM, LO, HI); break; \
-  }
-    if (T == 1) {
-      GU_ALL(1, 1, INT32_MAX)
-    } else {
-      GU_ALL(1, 1, 1)
+  const GemvArgs ga{x, k, &w, offsets, sorted_rows, active, hbuf, y_rows, s};
+  // several tokens: class lists of the register GEMVs (after h in the workspace)
+  size_t off = align_up((size_t)R * I * sizeof(float), 256);
+  int32_t *l1 = nullptr, *l4 = nullptr;
+  if (T > 1) {
+    l1 = (int32_t*)((uint8_t*)ws + off);
+    l4 = l1 + 1 + max_active;
+    off += lists_bytes(T, k, E);
+    if (reg_g || reg_d) {
+      hipLaunchKernelGGL(small_lists_kernel, dim3(1), dim3(kThreads), 0, s, offsets, active, l1, l4);
       if ((err = hipGetLastError()) != hipSuccess) return err;
-      GU_ALL(kRegRows, 2, kRegRows)
     }
-#undef GU_ALL
-#undef GU_REG
+  }
+  // grids of the class launches: n_max experts of the class at most
+  auto multi = [&](int n_max, const GemvGrid& gg) {
+    const long b = (long)n_max * gg.blocks_per_expert;
+    return dim3((unsigned)(b < kMultiGridCap ? b : kMultiGridCap));
+  };
+  const int n1_max = max_active, n4_max = R / 2 < max_active ? R / 2 : max_active;
+  if (reg_g) {
+    const int rows_it = (64 >> sg.lg) * sg.U, iters = (I + rows_it - 1) / rows_it;
+    if (T == 1) {
+      const GemvGrid gg = gemv_grid(iters, max_active, H == 7168 ? 4 : 2);
+      gateup_reg<1>(ga, sg, gg, dim3(max_active * gg.blocks_per_expert), nullptr, 1, INT32_MAX);
+    } else {
+      const GemvGrid gg = multi_grid(iters);
+      gateup_reg<1>(ga, sg, gg, multi(n1_max, gg), l1, 1, 1);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+      gateup_reg<kRegRows>(ga, sg, gg, multi(n4_max, gg), l4, 2, kRegRows);
+    }
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   const bool use_mfma = T > 1 && reg_g && reg_d && mfma_shape_ok(H, I);
-  uint8_t* mfma_ws = (uint8_t*)ws + align_up((size_t)R * I * sizeof(float), 256);
+  uint8_t* mfma_ws = (uint8_t*)ws + off;
   if (use_mfma) {
     if ((err = launch_mfma_gateup(x, T, k, w, offsets, sorted_rows, active, hbuf, mfma_ws, s)) != hipSuccess)
       return err;
@@ -638,36 +776,16 @@ hipError_t launch_expert_ffn(const uint16_t* x, int T, int k, const moe_mxfp4_we
   }
 
   if (reg_d) {
-    const int rows_it = (64 >> sd.lg) * sd.U;
-    GemvGrid gd = gemv_grid((H + rows_it - 1) / rows_it, max_active, I == 1536 ? 3 : 2);
-    const dim3 g(max_active * gd.blocks_per_expert), b(kThreads);
-#define DN_REG(JJ, UU, MM, LO, HI)                                                                                  \
-  hipLaunchKernelGGL((down_gemv_reg_kernel<JJ, UU, MM, 0>), g, b, (size_t)MM * I * 4, s, hbuf, w, offsets, active, \
-                     y_rows, sd.lg, gd.ipw, gd.blocks_per_expert, LO, HI)
-#define DN_ALL(MM, LO, HI)                                                                                          \
-  if (I == 1536) {                                                                                                  \
-    hipLaunchKernelGGL((down_gemv_reg_kernel<3, kDownU48, MM, 48>), g, b, (size_t)MM * I * 4, s, hbuf, w, offsets, active, \
-                       y_rows, sd.lg, gd.ipw, gd.blocks_per_expert, LO, HI);                                        \
-  } else                                    \
-  switch (sd.J) {                           \
-    case 1: DN_REG(1, 8, MM, LO, HI); break; \
-    case 2: DN_REG(2, 4, MM, LO, HI); break; \
-    case 3: DN_REG(3, 4, MM, LO, HI); break; \
-    case 4: DN_REG(4, 2, MM, LO, HI); break; \
-    case 5: DN_REG(5, 1, MM, LO, HI); break; \
-    case 6: DN_REG(6, 1, MM, LO, HI); break; \
-    case 7: DN_REG(7, 1, MM, LO, HI); break; \
-    default: DN_REG(8, 1, MM, LO, HI); break; \
-  }
+    const int rows_it = (64 >> sd.lg) * sd.U, iters = (H + rows_it - 1) / rows_it;
     if (T == 1) {
-      DN_ALL(1, 1, INT32_MAX)
+      const GemvGrid gd = gemv_grid(iters, max_active, I == 1536 ? 3 : 2);
+      down_reg<1>(ga, sd, gd, dim3(max_active * gd.blocks_per_expert), nullptr, 1, INT32_MAX);
     } else {
-      DN_ALL(1, 1, 1)
+      const GemvGrid gd = multi_grid(iters);
+      down_reg<1>(ga, sd, gd, multi(n1_max, gd), l1, 1, 1);
       if ((err = hipGetLastError()) != hipSuccess) return err;
-      DN_ALL(kRegRows, 2, kRegRows)
+      down_reg<kRegRows>(ga, sd, gd, multi(n4_max, gd), l4, 2, kRegRows);
     }
-#undef DN_ALL
-#undef DN_REG
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (use_mfma) {
