@@ -23,6 +23,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_synth.so")
+GPU_LIB_PATH = os.path.join(_HERE, "libmoe_synth_gpu.so")  # device twin of the slab generator
 
 # array ids of the tag field (weights use 1..6 inside moe_synth.c)
 ARR_X = 16
@@ -31,10 +32,12 @@ ARR_BIAS = 18
 ARR_TIES = 19
 
 _lib = None
+_gpu_lib = None
 
 
 def build(verbose: bool = False) -> str:
-    """Compile moe_synth.c into libmoe_synth.so with gcc (host code only)."""
+    """Compile moe_synth.c into libmoe_synth.so with gcc (host code) and
+    synth_gpu.hip into libmoe_synth_gpu.so with hipcc (gfx950)."""
     import subprocess
 
     cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC",
@@ -43,7 +46,29 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd))
     subprocess.check_call(cmd)
     os.replace(LIB_PATH + ".tmp", LIB_PATH)
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    cmd = [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-fvisibility=hidden",
+           os.path.join(_HERE, "synth_gpu.hip"), "-o", GPU_LIB_PATH + ".tmp"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.check_call(cmd)
+    os.replace(GPU_LIB_PATH + ".tmp", GPU_LIB_PATH)
     return LIB_PATH
+
+
+def gpu_lib():
+    global _gpu_lib
+    if _gpu_lib is None:
+        if not os.path.exists(GPU_LIB_PATH):
+            raise RuntimeError(f"{GPU_LIB_PATH} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(GPU_LIB_PATH)
+        L.synth_expert_slabs_gpu.restype = ctypes.c_int
+        L.synth_expert_slabs_gpu.argtypes = [ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                             ctypes.c_uint64, ctypes.c_void_p]
+        _gpu_lib = L
+    return _gpu_lib
 
 
 def lib():
@@ -197,6 +222,26 @@ def router_logits(seed: int, wl: Workload, layer: int = 0, variant: int = 0) -> 
         b[:16] = 64.0
         return (base + b[None, :]).astype(np.float32)
     raise ValueError(f"unknown logits recipe {wl.logits}")
+
+
+def device_pool_slabs(seed: int, pool: int, layer: int, E: int, H: int, I: int, device, out=None,
+                      first: int = 0):
+    """Experts first..first+E-1 of (pool, layer) generated on the device: a
+    uint8 tensor [E, slab] holding the same bytes as expert_slabs() /
+    upload_pool()."""
+    import torch
+
+    sb = slab_bytes(H, I)
+    dst = torch.empty((E, sb), dtype=torch.uint8, device=device) if out is None else out
+    assert dst.dtype == torch.uint8 and dst.is_contiguous() and dst.numel() >= E * sb
+    stream = torch.cuda.current_stream(dst.device).cuda_stream
+    for e0 in range(0, E, 65535):
+        n = min(65535, E - e0)
+        rc = gpu_lib().synth_expert_slabs_gpu(seed, pool, layer, first + e0, n, H, I, dst[e0].data_ptr(), sb,
+                                              stream)
+        if rc != 0:
+            raise RuntimeError(f"synth_expert_slabs_gpu failed ({rc})")
+    return dst
 
 
 def upload_pool(seed: int, pool: int, layer: int, E: int, H: int, I: int, device, nthreads: int = 16,

@@ -31,8 +31,11 @@ def assert_close(got: np.ndarray, ref: np.ndarray, what: str):
 
 
 def device_pool(wl, layer=0, seed=0):
+    """The workload's pool generated on the device (the same bytes as the
+    host generator, which test_gpu_synth checks)."""
     dev = torch.device("cuda", 0)
-    slabs = synth.upload_pool(seed, wl.pool, layer, wl.E, wl.H, wl.I, dev)
+    slabs = synth.device_pool_slabs(seed, wl.pool, layer, wl.E, wl.H, wl.I, dev)
+    torch.cuda.synchronize()
     return ExpertPool(slabs, wl.H, wl.I)
 
 
