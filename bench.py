@@ -42,7 +42,9 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="bounded oracle sample (0 = skip)")
     p.add_argument("--cpu-threads", type=int, default=16)
-    p.add_argument("--prefill-reps", type=int, default=10, help="prefill512 side measurement (0 = skip)")
+    p.add_argument("--prefill-reps", type=int, default=20, help="prefill512 / dense side measures (0 = skip)")
+    p.add_argument("--side-reps", type=int, default=100, help="verify8 side measure (0 = skip)")
+    p.add_argument("--stack-reps", type=int, default=20, help="92-layer stack side measure (0 = skip)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="only run a plain device copy of this many MiB 5 times (calibrates HBM byte counters)")
     return p.parse_args()
@@ -107,7 +109,8 @@ def main():
     wl = synth.WORKLOADS["decode896"]
     V = args.variants
     t0 = time.time()
-    slabs = synth.upload_pool(args.seed, wl.pool, 0, wl.E, wl.H, wl.I, dev)
+    slabs = synth.device_pool_slabs(args.seed, wl.pool, 0, wl.E, wl.H, wl.I, dev)
+    torch.cuda.synchronize()
     pool = ExpertPool(slabs, wl.H, wl.I)
     log(f"pool: {wl.E} experts, {slabs.numel() / 1e9:.2f} GB resident ({time.time() - t0:.1f} s)")
     xs = torch.stack([torch.from_numpy(synth.activations_bf16(args.seed, wl, variant=v).view(np.int16))
@@ -161,9 +164,11 @@ def main():
         expert_ffn_mxfp4(xs[i % V], wl.k, pool, gobjs[i % V], layer.workspace, y_rows)
         b.record(stream)
     torch.cuda.synchronize()
-    ffn_us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    ffn_each = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
+    ffn_us = float(np.mean(ffn_each))
     achieved = ffn_bytes / (ffn_us * 1e-6) / 1e9
     log(f"expert FFN call: {ffn_us:.1f} us, {achieved:.0f} GB/s of {ffn_bytes} algorithmic bytes")
+    layer_each = per_call_us(lambda i: step(i), K, stream)
 
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -175,25 +180,82 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": profiled_traffic(), "launch_us": round(ffn_us, 2),
                      "algorithmic_bytes": ffn_bytes},
+        "decode896_us": {"ffn_call": pct(ffn_each), "layer": pct(layer_each),
+                         "ffn_call_gbs_at_median": round(ffn_bytes / (np.median(ffn_each) * 1e-6) / 1e9, 1)},
     }
 
+    if args.side_reps > 0:
+        res["verify8"] = verify_side(dev, pool, args.seed, args.side_reps)
     if args.prefill_reps > 0:
-        res["prefill512"] = prefill_side(dev, pool, args.seed, args.prefill_reps)
+        res["prefill512"] = prefill_side(dev, pool, args.seed, args.prefill_reps, "prefill512")
+        res["prefill_dense"] = prefill_side(dev, pool, args.seed, args.prefill_reps, "prefill_dense")
+    if args.stack_reps > 0:
+        res["stack92"] = stack_side(dev, args.seed, args.stack_reps)
 
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(args, wl)
     print(json.dumps(res), flush=True)
 
 
-def prefill_side(dev, pool, seed, reps):
-    """512-token expert-major prefill on the same pool: algorithmic TFLOP/s."""
+def per_call_us(fn, reps, stream):
+    """Durations (us) of reps calls of fn(i), one event pair around each."""
+    import numpy as np
+    import torch
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        evs[i][0].record(stream)
+        fn(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
+
+
+def pct(v):
+    import numpy as np
+
+    return {"p10": round(float(np.percentile(v, 10)), 2), "median": round(float(np.median(v)), 2),
+            "p90": round(float(np.percentile(v, 90)), 2)}
+
+
+def verify_side(dev, pool, seed, reps):
+    """8-token speculative-verify batch on the same pool: weight GB/s over
+    the unique experts the batch reads."""
     import numpy as np
     import torch
 
     from mxfp4_routed_expert_02_amd import synth
     from mxfp4_routed_expert_02_amd.layer import RoutedExpertLayer
 
-    wl = synth.WORKLOADS["prefill512"]
+    wl = synth.WORKLOADS["verify8"]
+    V = 16  # rotate over variants like decode, against the last-level cache
+    xs = [torch.from_numpy(synth.activations_bf16(seed, wl, variant=v).view(np.int16)).to(dev).view(torch.bfloat16)
+          for v in range(V)]
+    ls = [torch.from_numpy(synth.router_logits(seed, wl, variant=v)).to(dev) for v in range(V)]
+    layer = RoutedExpertLayer(wl.E, wl.H, wl.I, wl.k, wl.T, dev)
+    uniq = []
+    for v in range(V):
+        layer(xs[v], ls[v], pool)
+        uniq.append(int(layer.grp.active[0].item()))
+    stream = torch.cuda.current_stream(dev)
+    each = per_call_us(lambda i: layer(xs[i % V], ls[i % V], pool), reps, stream)
+    per_call_bytes = np.array([uniq[i % V] for i in range(reps)]) * synth.slab_bytes(wl.H, wl.I)
+    gbs = float(per_call_bytes.sum() / (each.sum() * 1e-6) / 1e9)
+    log(f"verify8: {np.median(each):.1f} us/layer (median), {gbs:.0f} GB/s over {np.mean(uniq):.1f} unique experts")
+    return {"us_per_layer": pct(each), "weight_gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "unique_experts_mean": round(float(np.mean(uniq)), 2), "variants": V}
+
+
+def prefill_side(dev, pool, seed, reps, name):
+    """512-token expert-major prefill on the same pool: algorithmic TFLOP/s
+    (2 * R * 3 * H * I per layer) against the FP4 peak and the binding roofline."""
+    import numpy as np
+    import torch
+
+    from mxfp4_routed_expert_02_amd import synth
+    from mxfp4_routed_expert_02_amd.layer import RoutedExpertLayer
+
+    wl = synth.WORKLOADS[name]
     x = torch.from_numpy(synth.activations_bf16(seed, wl).view(np.int16)).to(dev).view(torch.bfloat16)
     logits = torch.from_numpy(synth.router_logits(seed, wl)).to(dev)
     layer = RoutedExpertLayer(wl.E, wl.H, wl.I, wl.k, wl.T, dev)
@@ -203,21 +265,65 @@ def prefill_side(dev, pool, seed, reps):
     offs = layer.grp.expert_offsets.cpu().numpy()
     touched = int((np.diff(offs) > 0).sum())
     stream = torch.cuda.current_stream(dev)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(reps):
-        layer(x, logits, pool)
-    b.record(stream)
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / reps
+    each = per_call_us(lambda i: layer(x, logits, pool), reps, stream)
+    ms = float(np.median(each)) * 1e-3
     flops = 2.0 * wl.R * 3 * wl.H * wl.I
     tflops = flops / (ms * 1e-3) / 1e12
     bytes_touched = touched * synth.slab_bytes(wl.H, wl.I)
     floor_ms = max(bytes_touched / (HBM_PEAK_GBS * 1e9), flops / (FP4_PEAK_TFLOPS * 1e12)) * 1e3
-    log(f"prefill512: {ms:.3f} ms/layer, {tflops:.1f} TFLOP/s, {touched} experts touched")
-    return {"ms_per_layer": round(ms, 4), "tflops": round(tflops, 2), "frac_fp4_peak": round(tflops / FP4_PEAK_TFLOPS, 4),
-            "experts_touched": touched, "binding_floor_ms": round(floor_ms, 4),
-            "frac_binding_roofline": round(floor_ms / ms, 4)}
+    log(f"{name}: {ms:.3f} ms/layer (median), {tflops:.1f} TFLOP/s, {touched} experts touched")
+    return {"ms_per_layer": round(ms, 4), "us_per_layer": pct(each), "tflops": round(tflops, 2),
+            "frac_fp4_peak": round(tflops / FP4_PEAK_TFLOPS, 4), "experts_touched": touched,
+            "binding_floor_ms": round(floor_ms, 4), "frac_binding_roofline": round(floor_ms / ms, 4)}
+
+
+def stack_side(dev, seed, reps):
+    """Batch-1 decode through the 92-layer stack (96 experts per layer, 155 GB
+    resident), RMS rescale between layers; the token step (92 x 5 calls) is
+    captured once in a HIP graph and replayed."""
+    import numpy as np
+    import torch
+
+    from mxfp4_routed_expert_02_amd import ExpertPool, rms_rescale_bf16, synth
+    from mxfp4_routed_expert_02_amd.layer import RoutedExpertLayer
+
+    wl = synth.WORKLOADS["stack92"]
+    t0 = time.time()
+    pools = [ExpertPool(synth.device_pool_slabs(seed, wl.pool, l, wl.E, wl.H, wl.I, dev), wl.H, wl.I)
+             for l in range(wl.layers)]
+    torch.cuda.synchronize()
+    log(f"stack92: {wl.layers} pools generated on the device in {time.time() - t0:.1f} s")
+    layer = RoutedExpertLayer(wl.E, wl.H, wl.I, wl.k, 1, dev)
+    x0 = torch.from_numpy(synth.activations_bf16(seed, wl).view(np.int16)).to(dev).view(torch.bfloat16)
+    logits = torch.stack([torch.from_numpy(synth.router_logits(seed, wl, layer=l)) for l in range(wl.layers)]).to(dev)
+    xbuf = torch.empty((2, 1, wl.H), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((1, wl.H), dtype=torch.float32, device=dev)
+
+    def token():
+        x = x0
+        for l in range(wl.layers):
+            layer(x, logits[l], pools[l], out)
+            x = rms_rescale_bf16(out, 1e-6, out=xbuf[l & 1])
+
+    token()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    eager = per_call_us(lambda i: token(), 3, stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        token()
+    g.replay()
+    torch.cuda.synchronize()
+    each = per_call_us(lambda i: g.replay(), reps, stream)
+    bytes_token = wl.layers * wl.k * synth.slab_bytes(wl.H, wl.I)
+    ms = float(np.median(each)) * 1e-3
+    gbs = bytes_token / (ms * 1e-3) / 1e9
+    log(f"stack92: {ms:.3f} ms/token in a graph (median), {gbs:.0f} GB/s; eager {np.median(eager) * 1e-3:.3f} ms")
+    del g, pools
+    torch.cuda.empty_cache()
+    return {"ms_per_token": round(ms, 4), "us_per_token": pct(each), "weight_gbs": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "weight_bytes_per_token": bytes_token,
+            "eager_ms_per_token": round(float(np.median(eager)) * 1e-3, 4), "graph": True}
 
 
 def cpu_baseline(args, wl):
