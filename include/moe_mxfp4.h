@@ -174,7 +174,9 @@ MOE_API const char* moe_status_string(moe_status s);
  * moe_rms_rescale_bf16 - glue between stacked layers (not one of the four
  * calls of a layer): x_next[t] = bf16_rne(y[t] / sqrt(mean(y[t]^2) + eps)),
  * the weightless RMS rescaling that feeds layer l's output to layer l+1.
- *   y [T][H] fp32, x_next [T][H] bf16 out (raw bits); H >= 1, eps >= 0.
+ *   y [T][H] fp32, x_next [T][H] bf16 out (raw bits); H a multiple of 32 in
+ *   32..MOE_MAX_DIM, eps >= 0; y 16-byte and x_next 8-byte aligned
+ *   (MOE_ERR_INVALID_ARG otherwise).
  */
 MOE_API moe_status moe_rms_rescale_bf16(const float* y, int32_t T, int32_t H, float eps, uint16_t* x_next,
                                 moe_stream_t stream);

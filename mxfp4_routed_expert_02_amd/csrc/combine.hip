@@ -55,21 +55,44 @@ __global__ __launch_bounds__(kThreads) void combine_scalar_kernel(const float* _
 }
 
 // one block per token: sum of squares -> 1/sqrt(mean + eps) -> bf16 RNE
-__global__ __launch_bounds__(kThreads) void rms_rescale_kernel(const float* __restrict__ y, int H, float eps,
-                                                               uint16_t* __restrict__ x_next) {
-  __shared__ float s_part[kThreads / MOE_WAVE];
+// One block of 1024 threads per token: each thread keeps up to 4 float4 of
+// y in registers (H <= 16384), so y is read once; the sum of squares meets
+// in a wave butterfly and then across the 16 waves in LDS.
+constexpr int kRmsThreads = 1024;
+constexpr int kRmsVec = 4;  // float4 per thread
+
+__global__ __launch_bounds__(kRmsThreads) void rms_rescale_kernel(const float* __restrict__ y, int H, float eps,
+                                                                  uint16_t* __restrict__ x_next) {
+  __shared__ float s_part[kRmsThreads / MOE_WAVE];
   const int t = blockIdx.x;
-  const float* yr = y + (int64_t)t * H;
+  const int n4 = H >> 2;
+  const float4* yr = (const float4*)(y + (int64_t)t * H);
+  float4 v[kRmsVec];
   float ss = 0.0f;
-  for (int n = threadIdx.x; n < H; n += kThreads) ss += yr[n] * yr[n];
+#pragma unroll
+  for (int i = 0; i < kRmsVec; ++i) {
+    const int c = threadIdx.x + kRmsThreads * i;
+    v[i] = c < n4 ? yr[c] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  }
+#pragma unroll
+  for (int i = 0; i < kRmsVec; ++i) ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
   ss = wave_sum(ss);
   if ((threadIdx.x & (MOE_WAVE - 1)) == 0) s_part[threadIdx.x / MOE_WAVE] = ss;
   __syncthreads();
   float tot = 0.0f;
 #pragma unroll
-  for (int i = 0; i < kThreads / MOE_WAVE; ++i) tot += s_part[i];
+  for (int i = 0; i < kRmsThreads / MOE_WAVE; ++i) tot += s_part[i];
   const float r = 1.0f / sqrtf(tot / (float)H + eps);
-  for (int n = threadIdx.x; n < H; n += kThreads) x_next[(int64_t)t * H + n] = f32_to_bf16_rne_dev(yr[n] * r);
+  uint2* xo = (uint2*)(x_next + (int64_t)t * H);
+#pragma unroll
+  for (int i = 0; i < kRmsVec; ++i) {
+    const int c = threadIdx.x + kRmsThreads * i;
+    if (c < n4) {
+      const uint32_t lo = f32_to_bf16_rne_dev(v[i].x * r) | ((uint32_t)f32_to_bf16_rne_dev(v[i].y * r) << 16);
+      const uint32_t hi = f32_to_bf16_rne_dev(v[i].z * r) | ((uint32_t)f32_to_bf16_rne_dev(v[i].w * r) << 16);
+      xo[c] = make_uint2(lo, hi);
+    }
+  }
 }
 
 }  // namespace
@@ -93,7 +116,9 @@ hipError_t launch_combine(const float* y_rows, const float* w, const int32_t* ro
 
 hipError_t launch_rms_rescale(const float* y, int T, int H, float eps, uint16_t* x_next, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(rms_rescale_kernel, dim3(T), dim3(kThreads), 0, s, y, H, eps, x_next);
+  // H is a multiple of 32 and at most MOE_MAX_DIM = 16384 = 4 * 4 * 1024
+  static_assert(MOE_MAX_DIM <= 4 * kRmsVec * kRmsThreads, "one register tile per token");
+  hipLaunchKernelGGL(rms_rescale_kernel, dim3(T), dim3(kRmsThreads), 0, s, y, H, eps, x_next);
   return hipGetLastError();
 }
 

@@ -120,7 +120,9 @@ moe_status moe_combine(const float* y_rows, const float* topk_weights, const int
 
 moe_status moe_rms_rescale_bf16(const float* y, int32_t T, int32_t H, float eps, uint16_t* x_next,
                                 moe_stream_t stream) {
-  if ((T > 0 && (!y || !x_next)) || T < 0 || H < 1 || H > MOE_MAX_DIM || !(eps >= 0.0f)) return MOE_ERR_INVALID_ARG;
+  if ((T > 0 && (!y || !x_next)) || T < 0 || H < 32 || H > MOE_MAX_DIM || (H & 31) != 0 || !(eps >= 0.0f))
+    return MOE_ERR_INVALID_ARG;
+  if (((uintptr_t)y & 15) != 0 || ((uintptr_t)x_next & 7) != 0) return MOE_ERR_INVALID_ARG;
   const moe_status d = check_device();
   if (d != MOE_OK) return d;
   return from_hip(moe::launch_rms_rescale(y, T, H, eps, x_next, (hipStream_t)stream));

@@ -71,31 +71,26 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float* 
   }
 }
 
-// Register variant: lane l holds the C logits of experts l*C .. l*C+C-1 as
-// order-preserving unsigned keys (0 = taken or absent), so the lowest lane
-// holding the wave maximum also holds the lowest id among equal values.
+// Order-preserving unsigned key of a logit (0 is below every finite value
+// and marks taken or absent slots).
 __device__ __forceinline__ uint32_t order_key(float v) {
   uint32_t u = __float_as_uint(v);
   if (u == 0x80000000u) u = 0u;  // -0 ranks equal to +0
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Four-wave variant: wave w holds the keys of experts [w*Q, w*Q + Q),
+// Q = 64*C, lane l those of experts w*Q + l*C + i.  Each wave picks its own
+// top-k in k register rounds (cheap with C <= 8 keys per lane); the global
+// top-k lies among those 4k candidates, and wave 0 picks it from them with
+// the candidates in (wave, rank) order, so that the lowest lane and slot
+// among equal keys is still the lowest expert id.
+constexpr int kRoute4Threads = 256;
+
+// k rounds of arg-max over the wave's keys (0 = taken or absent); round j
+// leaves the pick's key and its position lane*C + slot in lane j.
 template <int C>
-__global__ __launch_bounds__(kRouteThreads) void route_topk_reg_kernel(const float* __restrict__ logits, int E,
-                                                                       int k, int32_t* __restrict__ ids,
-                                                                       float* __restrict__ weights) {
-  const int t = blockIdx.x;
-  const int lane = threadIdx.x;
-  const float* row = logits + (int64_t)t * E;
-  uint32_t key[C];
-#pragma unroll
-  for (int i = 0; i < C; ++i) {
-    const int e = lane * C + i;
-    key[i] = e < E ? order_key(row[e]) : 0u;
-  }
-  // round j leaves the pick's id and logit in lane j
-  int my_id = 0;
-  float my_val = 0.0f;
+__device__ __forceinline__ void wave_topk(uint32_t (&key)[C], int k, int lane, uint32_t& my_key, int& my_pos) {
   for (int j = 0; j < k; ++j) {
     uint32_t bk = 0u;
     int bi = 0;
@@ -115,9 +110,50 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_reg_kernel(const flo
         if (i == slot) key[i] = 0u;
     }
     if (lane == j) {
-      my_id = win * C + slot;
-      my_val = __uint_as_float((m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m);  // key -> value
+      my_key = m;
+      my_pos = win * C + slot;
     }
+  }
+}
+
+template <int C>
+__global__ __launch_bounds__(kRoute4Threads) void route_topk_4w_kernel(const float* __restrict__ logits, int E,
+                                                                      int k, int32_t* __restrict__ ids,
+                                                                      float* __restrict__ weights) {
+  constexpr int Q = MOE_WAVE * C;
+  __shared__ uint32_t s_key[4 * MOE_MAX_TOPK];
+  __shared__ int32_t s_id[4 * MOE_MAX_TOPK];
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x & (MOE_WAVE - 1), wave = threadIdx.x / MOE_WAVE;
+  const float* row = logits + (int64_t)t * E;
+  uint32_t key[C];
+#pragma unroll
+  for (int i = 0; i < C; ++i) {
+    const int e = wave * Q + lane * C + i;
+    key[i] = e < E ? order_key(row[e]) : 0u;
+  }
+  uint32_t mk = 0u;
+  int mp = 0;
+  wave_topk<C>(key, k, lane, mk, mp);
+  if (lane < k) {
+    s_key[wave * k + lane] = mk;
+    s_id[wave * k + lane] = wave * Q + mp;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  // candidate c = w*k + r in lane c/2, slot c%2
+  uint32_t ck[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = 2 * lane + i;
+    ck[i] = c < 4 * k ? s_key[c] : 0u;
+  }
+  wave_topk<2>(ck, k, lane, mk, mp);
+  int my_id = 0;
+  float my_val = 0.0f;
+  if (lane < k) {
+    my_id = s_id[mp];
+    my_val = __uint_as_float((mk & 0x80000000u) ? (mk & 0x7FFFFFFFu) : ~mk);  // key -> value
   }
   // softmax over the k picks: exponentials in parallel, the sum in rank order
   const float mx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_val), 0));
@@ -332,19 +368,15 @@ namespace moe {
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const dim3 g(T), b(kRouteThreads);
-  if (E <= 64 * 1)
-    hipLaunchKernelGGL(route_topk_reg_kernel<1>, g, b, 0, s, logits, E, k, ids, w);
-  else if (E <= 64 * 2)
-    hipLaunchKernelGGL(route_topk_reg_kernel<2>, g, b, 0, s, logits, E, k, ids, w);
-  else if (E <= 64 * 4)
-    hipLaunchKernelGGL(route_topk_reg_kernel<4>, g, b, 0, s, logits, E, k, ids, w);
-  else if (E <= 64 * 8)
-    hipLaunchKernelGGL(route_topk_reg_kernel<8>, g, b, 0, s, logits, E, k, ids, w);
-  else if (E <= 64 * 16)
-    hipLaunchKernelGGL(route_topk_reg_kernel<16>, g, b, 0, s, logits, E, k, ids, w);
-  else if (E <= 64 * 32)
-    hipLaunchKernelGGL(route_topk_reg_kernel<32>, g, b, 0, s, logits, E, k, ids, w);
+  const dim3 g(T), b(kRouteThreads), b4(kRoute4Threads);
+  if (E <= 4 * 64 * 1)
+    hipLaunchKernelGGL(route_topk_4w_kernel<1>, g, b4, 0, s, logits, E, k, ids, w);
+  else if (E <= 4 * 64 * 2)
+    hipLaunchKernelGGL(route_topk_4w_kernel<2>, g, b4, 0, s, logits, E, k, ids, w);
+  else if (E <= 4 * 64 * 4)
+    hipLaunchKernelGGL(route_topk_4w_kernel<4>, g, b4, 0, s, logits, E, k, ids, w);
+  else if (E <= 4 * 64 * 8)
+    hipLaunchKernelGGL(route_topk_4w_kernel<8>, g, b4, 0, s, logits, E, k, ids, w);
   else {
     const size_t lds = (size_t)E * sizeof(float) + (size_t)((E + 31) / 32) * sizeof(uint32_t);
     hipLaunchKernelGGL(route_topk_kernel, g, b, lds, s, logits, E, k, ids, w);

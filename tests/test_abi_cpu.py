@@ -101,6 +101,8 @@ def test_combine_and_rescale_reject_bad_arguments(L):
     assert L.moe_combine(FAKE, FAKE, FAKE, 1, 2, 0, FAKE, None) == INVALID
     assert L.moe_rms_rescale_bf16(FAKE, 1, 0, 1e-6, FAKE, None) == INVALID
     assert L.moe_rms_rescale_bf16(FAKE, 1, 64, -1.0, FAKE, None) == INVALID
+    assert L.moe_rms_rescale_bf16(FAKE, 1, 48, 1e-6, FAKE, None) == INVALID  # H not a multiple of 32
+    assert L.moe_rms_rescale_bf16(FAKE + 4, 1, 64, 1e-6, FAKE, None) == INVALID  # y not 16-byte aligned
 
 
 def test_valid_call_without_gpu_reports_hip_error(L):

@@ -109,7 +109,10 @@ def test_routing_max_experts_and_ties():
 
     for wl in (synth.Workload("E4096", E=4096, H=32, I=32, k=32, T=37, sub=30),
                synth.Workload("ties4096", E=4096, H=32, I=32, k=16, T=19, logits="ties", sub=31),
-               synth.Workload("E896_T2000", E=896, H=32, I=32, k=16, T=2000, logits="zipf", sub=32)):
+               synth.Workload("E896_T2000", E=896, H=32, I=32, k=16, T=2000, logits="zipf", sub=32),
+               synth.Workload("ties896", E=896, H=32, I=32, k=16, T=64, logits="ties", sub=33),
+               synth.Workload("ties2048_k32", E=2048, H=32, I=32, k=32, T=16, logits="ties", sub=34),
+               synth.Workload("E1000_k1", E=1000, H=32, I=32, k=1, T=40, sub=35)):
         say(f"case {wl.name}")
         logits = synth.router_logits(0, wl)
         ref = _ref_routing(wl, logits)
