@@ -122,7 +122,9 @@ MOE_API moe_status moe_route_topk(const float* logits, int32_t T, int32_t E, int
  *                   least one row, active[1..] = those experts ascending
  *                   (entries past the count are left unchanged)
  *   workspace       device scratch of at least
- *                   moe_workspace_bytes(T, k, E, H, I) bytes (any H, I)
+ *                   moe_workspace_bytes(T, k, E, H, I) bytes (any H, I),
+ *                   16-byte aligned (more than 512 rows use it; fewer may
+ *                   pass NULL)
  * Same ranges as moe_route_topk (k may exceed E here; ids may repeat).
  */
 MOE_API moe_status moe_group_rows(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t* expert_offsets,

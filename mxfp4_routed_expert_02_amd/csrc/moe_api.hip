@@ -85,7 +85,7 @@ moe_status moe_group_rows(const int32_t* topk_ids, int32_t T, int32_t k, int32_t
   if (T > 0 && (!topk_ids || !sorted_rows || !row_pos)) return MOE_ERR_INVALID_ARG;
   if (!rows_fit(T, k) || k > MOE_MAX_TOPK || E < 1 || E > MOE_MAX_EXPERTS) return MOE_ERR_INVALID_ARG;
   const size_t need = moe::group_rows_workspace(T, k, E);
-  if (need > 0 && !workspace) return MOE_ERR_INVALID_ARG;
+  if (need > 0 && (!workspace || !aligned16(workspace))) return MOE_ERR_INVALID_ARG;
   if (workspace_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
   const moe_status d = check_device();
   if (d != MOE_OK) return d;

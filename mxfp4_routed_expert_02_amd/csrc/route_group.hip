@@ -168,14 +168,6 @@ __global__ __launch_bounds__(kRoute4Threads) void route_topk_4w_kernel(const flo
 
 // ------------------------------------------------------------------ group --
 constexpr int kGroupThreads = 1024;
-constexpr int kGroupLds = 61440;  // bytes of dynamic LDS the grouping kernel may use
-
-// words of bitmap per expert per chunk (chunk = 32 * W rows)
-__host__ __device__ inline int group_words(int E) {
-  int words = (kGroupLds - 8 * E) / 4 / E;
-  return words > 32 ? 32 : (words < 1 ? 1 : words);
-}
-
 // In-place exclusive scan of a[0..n) in LDS by the whole block; returns total.
 __device__ int block_exclusive_scan(int* a, int n, int* s_wave) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -213,42 +205,80 @@ __device__ int block_exclusive_scan(int* a, int n, int* s_wave) {
   return total;
 }
 
-__global__ __launch_bounds__(kGroupThreads) void group_rows_kernel(const int32_t* __restrict__ ids, int R, int E,
-                                                                   int32_t* __restrict__ offsets,
-                                                                   int32_t* __restrict__ sorted_rows,
-                                                                   int32_t* __restrict__ row_pos,
-                                                                   int32_t* __restrict__ active) {
-  extern __shared__ int s_mem[];
-  int* s_count = s_mem;             // [E] counts, then running positions
-  int* s_flag = s_mem + E;          // [E] active flags, then their scan
-  uint32_t* s_bits = (uint32_t*)(s_mem + 2 * E);
-  __shared__ int s_wave[kGroupThreads / 64 + 1];
-  const int tid = threadIdx.x;
-  const int W = group_words(E);
-  const int CH = 32 * W;
+// Grouping for many rows: three kernels over chunks of kChunkRows rows.
+//   count:   per chunk, each expert's row count and each row's rank among
+//            the chunk's earlier rows of the same expert (many blocks)
+//   scan:    per expert, the chunks' counts become exclusive positions
+//            within the expert, and the totals become expert_offsets and the
+//            active list (one block)
+//   scatter: each row goes to expert offset + chunk position + rank (many
+//            blocks)
+// Positions follow (chunk, rank in chunk) = ascending row index within each
+// expert, the same stable order as a counting sort.  Workspace: cnt
+// [chunks][E] then rank [R] (int32).
+constexpr int kChunkRows = 256;
 
-  for (int e = tid; e < E; e += kGroupThreads) s_count[e] = 0;
+__global__ __launch_bounds__(kChunkRows) void group_count_kernel(const int32_t* __restrict__ ids, int R, int E,
+                                                                int32_t* __restrict__ cnt,
+                                                                int32_t* __restrict__ rank) {
+  extern __shared__ int s_cnt[];  // [E]
+  __shared__ int s_ids[kChunkRows];
+  const int c = blockIdx.x, tid = threadIdx.x, r = c * kChunkRows + tid;
+  for (int e = tid; e < E; e += kChunkRows) s_cnt[e] = 0;
+  const int e = r < R ? ids[r] : -1;
+  s_ids[tid] = e;
   __syncthreads();
   // ids outside [0, E) break the documented precondition; they are skipped so
-  // that no LDS access leaves the arrays
-  for (int r = tid; r < R; r += kGroupThreads) {
-    const int e = ids[r];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&s_count[e], 1);
+  // that no LDS access leaves the array
+  if ((unsigned)e < (unsigned)E) {
+    atomicAdd(&s_cnt[e], 1);
+    int k = 0;
+    for (int j = 0; j < tid; ++j) k += s_ids[j] == e;
+    rank[r] = k;
   }
   __syncthreads();
-  for (int e = tid; e < E; e += kGroupThreads) s_flag[e] = s_count[e] > 0 ? 1 : 0;
-  __syncthreads();
-  const int total = block_exclusive_scan(s_count, E, s_wave);  // s_count = offsets
-  for (int e = tid; e < E; e += kGroupThreads) offsets[e] = s_count[e];
-  if (tid == 0) offsets[E] = total;
-  // active list: experts whose offset range is non-empty, ascending
+  for (int x = tid; x < E; x += kChunkRows) cnt[(int64_t)c * E + x] = s_cnt[x];
+}
+
+__global__ __launch_bounds__(kGroupThreads) void group_scan_kernel(int nch, int E, int32_t* __restrict__ cnt,
+                                                                  int32_t* __restrict__ offsets,
+                                                                  int32_t* __restrict__ active) {
+  extern __shared__ int s_mem[];
+  int* s_tot = s_mem;       // [E] totals, then offsets
+  int* s_flag = s_mem + E;  // [E] active flags, then their scan
+  __shared__ int s_wave[kGroupThreads / 64 + 1];
+  const int tid = threadIdx.x;
   for (int e = tid; e < E; e += kGroupThreads) {
-    const int next = (e + 1 < E) ? s_count[e + 1] : total;
-    s_flag[e] = next > s_count[e] ? 1 : 0;
+    // counts of 8 chunks are loaded before any is rewritten
+    int run = 0;
+    int c0 = 0;
+    for (; c0 + 8 <= nch; c0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = cnt[(int64_t)(c0 + i) * E + e];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        cnt[(int64_t)(c0 + i) * E + e] = run;
+        run += v[i];
+      }
+    }
+    for (int c = c0; c < nch; ++c) {
+      const int v = cnt[(int64_t)c * E + e];
+      cnt[(int64_t)c * E + e] = run;
+      run += v;
+    }
+    s_tot[e] = run;
   }
+  __syncthreads();
+  const int total = block_exclusive_scan(s_tot, E, s_wave);  // s_tot = offsets
+  for (int e = tid; e < E; e += kGroupThreads) {
+    offsets[e] = s_tot[e];
+    const int next = (e + 1 < E) ? s_tot[e + 1] : total;
+    s_flag[e] = next > s_tot[e] ? 1 : 0;
+  }
+  if (tid == 0) offsets[E] = total;
   __syncthreads();
   {
-    // keep flags to know which slots to write: scan a copy held per thread
     const int per = (E + kGroupThreads - 1) / kGroupThreads;
     const int beg = min(E, tid * per), end = min(E, beg + per);
     int mine[MOE_MAX_EXPERTS / kGroupThreads];
@@ -259,35 +289,21 @@ __global__ __launch_bounds__(kGroupThreads) void group_rows_kernel(const int32_t
       if (mine[i - beg]) active[1 + s_flag[i]] = i;
     if (tid == 0) active[0] = na;
   }
+}
 
-  // stable placement, one chunk of CH rows at a time (s_count = running position)
-  for (int c0 = 0; c0 < R; c0 += CH) {
-    const int n = min(CH, R - c0);
-    for (int i = tid; i < E * W; i += kGroupThreads) s_bits[i] = 0u;
-    __syncthreads();
-    for (int p = tid; p < n; p += kGroupThreads) {
-      const int e = ids[c0 + p];
-      if ((unsigned)e < (unsigned)E) atomicOr(&s_bits[e * W + (p >> 5)], 1u << (p & 31));
-    }
-    __syncthreads();
-    for (int p = tid; p < n; p += kGroupThreads) {
-      const int e = ids[c0 + p];
-      if ((unsigned)e >= (unsigned)E) continue;
-      const uint32_t* b = s_bits + e * W;
-      int rank = __popc(b[p >> 5] & ((1u << (p & 31)) - 1u));
-      for (int w = 0; w < (p >> 5); ++w) rank += __popc(b[w]);
-      const int pos = s_count[e] + rank;
-      sorted_rows[pos] = c0 + p;
-      row_pos[c0 + p] = pos;
-    }
-    __syncthreads();
-    for (int e = tid; e < E; e += kGroupThreads) {
-      int c = 0;
-      for (int w = 0; w < W; ++w) c += __popc(s_bits[e * W + w]);
-      s_count[e] += c;
-    }
-    __syncthreads();
-  }
+__global__ __launch_bounds__(kChunkRows) void group_scatter_kernel(const int32_t* __restrict__ ids, int R, int E,
+                                                                  const int32_t* __restrict__ offsets,
+                                                                  const int32_t* __restrict__ cnt,
+                                                                  const int32_t* __restrict__ rank,
+                                                                  int32_t* __restrict__ sorted_rows,
+                                                                  int32_t* __restrict__ row_pos) {
+  const int c = blockIdx.x, r = c * kChunkRows + threadIdx.x;
+  if (r >= R) return;
+  const int e = ids[r];
+  if ((unsigned)e >= (unsigned)E) return;
+  const int pos = offsets[e] + cnt[(int64_t)c * E + e] + rank[r];
+  sorted_rows[pos] = r;
+  row_pos[r] = pos;
 }
 
 // Grouping for few rows (R <= kSmallRows): one block; counts by LDS
@@ -385,24 +401,30 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
 }
 
 size_t group_rows_workspace(int T, int k, int E) {
-  (void)T;
-  (void)k;
-  (void)E;
-  return 0;
+  const size_t R = (size_t)T * k;
+  if (R <= (size_t)kSmallRows) return 0;
+  const size_t nch = (R + kChunkRows - 1) / kChunkRows;
+  return (nch * (size_t)E + R) * sizeof(int32_t);
 }
 
 hipError_t launch_group_rows(const int32_t* ids, int T, int k, int E, int32_t* offsets, int32_t* sorted_rows,
                              int32_t* row_pos, int32_t* active, void* ws, hipStream_t s) {
-  (void)ws;
   const int R = T * k;
   if (R <= kSmallRows) {
     hipLaunchKernelGGL(group_rows_small_kernel, dim3(1), dim3(kSmallThreads), (size_t)8 * E, s, ids, R, E, offsets,
                        sorted_rows, row_pos, active);
     return hipGetLastError();
   }
-  const size_t lds = (size_t)8 * E + (size_t)4 * E * group_words(E);
-  hipLaunchKernelGGL(group_rows_kernel, dim3(1), dim3(kGroupThreads), lds, s, ids, R, E, offsets, sorted_rows,
-                     row_pos, active);
+  const int nch = (R + kChunkRows - 1) / kChunkRows;
+  int32_t* cnt = (int32_t*)ws;
+  int32_t* rank = cnt + (size_t)nch * E;
+  hipLaunchKernelGGL(group_count_kernel, dim3(nch), dim3(kChunkRows), (size_t)4 * E, s, ids, R, E, cnt, rank);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(kGroupThreads), (size_t)8 * E, s, nch, E, cnt, offsets, active);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(group_scatter_kernel, dim3(nch), dim3(kChunkRows), 0, s, ids, R, E, offsets, cnt, rank,
+                     sorted_rows, row_pos);
   return hipGetLastError();
 }
 

@@ -69,6 +69,12 @@ def test_group_rejects_bad_arguments(L):
     assert L.moe_group_rows(FAKE, 1, 2, 8, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == INVALID
     assert L.moe_group_rows(FAKE, 1, 0, 8, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == INVALID
     assert L.moe_group_rows(FAKE, 1, 2, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == INVALID
+    # more than 512 rows need the chunk counts in the workspace
+    need = L.moe_workspace_bytes(512, 16, 896, 7168, 1536)
+    assert need >= (32 * 896 + 8192) * 4
+    assert L.moe_group_rows(FAKE, 512, 16, 896, FAKE, FAKE, FAKE, FAKE, FAKE, 1024, None) == WS_SMALL
+    assert L.moe_group_rows(FAKE, 512, 16, 896, FAKE, FAKE, FAKE, FAKE, None, need, None) == INVALID
+    assert L.moe_group_rows(FAKE, 512, 16, 896, FAKE, FAKE, FAKE, FAKE, FAKE + 4, need, None) == INVALID
 
 
 def _weights(H=256, I=128, E=8, misalign=0, stride=None):
