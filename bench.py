@@ -53,8 +53,6 @@ def parse():
 def profiled_traffic():
     """HBM bytes per expert-FFN call from the committed counter summary, or
     None when the kernel sources changed since those counters were taken."""
-    import glob
-    import hashlib
     import re
 
     path = os.path.join(ROOT, "profiles", "decode896_hbm_traffic.md")
@@ -65,11 +63,20 @@ def profiled_traffic():
     m_bytes = re.search(r"ffn_call_traffic_bytes: (\d+)", text)
     if not (m_sha and m_bytes):
         return None
+    return int(m_bytes.group(1)) if ffn_sources_sha256() == m_sha.group(1) else None
+
+
+def ffn_sources_sha256():
+    """Fingerprint of the sources of the decode expert-FFN kernels (the
+    register GEMVs and the device helpers they include)."""
+    import hashlib
+
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "mxfp4_routed_expert_02_amd", "csrc", "*"))):
-        h.update(os.path.basename(f).encode())
+    for name in ("ffn_gemv.hip", "moe_internal.h"):
+        f = os.path.join(ROOT, "mxfp4_routed_expert_02_amd", "csrc", name)
+        h.update(name.encode())
         h.update(open(f, "rb").read())
-    return int(m_bytes.group(1)) if h.hexdigest() == m_sha.group(1) else None
+    return h.hexdigest()
 
 
 def copy_probe(mib):
@@ -189,6 +196,7 @@ def main():
     if args.prefill_reps > 0:
         res["prefill512"] = prefill_side(dev, pool, args.seed, args.prefill_reps, "prefill512")
         res["prefill_dense"] = prefill_side(dev, pool, args.seed, args.prefill_reps, "prefill_dense")
+        res["prefill4096"] = prefill_side(dev, pool, args.seed, max(2, args.prefill_reps // 4), "prefill4096")
     if args.stack_reps > 0:
         res["stack92"] = stack_side(dev, args.seed, args.stack_reps)
 

@@ -138,6 +138,8 @@ WORKLOADS: Dict[str, Workload] = {
     "stack92": Workload("stack92", E=96, H=7168, I=1536, k=16, T=1, layers=92, pool=3, sub=3),
     "verify8": Workload("verify8", E=896, H=7168, I=1536, k=16, T=8, logits="shared_bias", pool=0, sub=4),
     "prefill512": Workload("prefill512", E=896, H=7168, I=1536, k=16, T=512, logits="zipf", pool=0, sub=5),
+    # long prompt: hot experts reach thousands of rows (the grouped GEMM's MFMA-bound regime)
+    "prefill4096": Workload("prefill4096", E=896, H=7168, I=1536, k=16, T=4096, logits="zipf", pool=0, sub=7),
     # auxiliary dense case: every token routes to the same 16 experts (512 rows each)
     "prefill_dense": Workload("prefill_dense", E=896, H=7168, I=1536, k=16, T=512, logits="dense16", pool=0,
                               sub=6),

@@ -222,3 +222,14 @@ def test_prefill_dense(pool896):
     say("case prefill_dense")
     wl = synth.WORKLOADS["prefill_dense"]
     _full_case(wl, pool896, tokens=[0, 1, 255, 511])
+
+
+def test_prefill4096(pool896):
+    """A 4096-token prompt (65,536 routed rows): hot experts with thousands of
+    rows and many token tiles each; sampled tokens against the oracle."""
+    say("case prefill4096")
+    wl = synth.WORKLOADS["prefill4096"]
+    logits = synth.router_logits(0, wl)
+    ref = _ref_routing(wl, logits)
+    toks = _sample_tokens(ref, wl.T, wl.k)
+    _full_case(wl, pool896, tokens=toks)
