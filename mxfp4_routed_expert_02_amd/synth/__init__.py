@@ -30,6 +30,7 @@ ARR_X = 16
 ARR_LOGITS = 17
 ARR_BIAS = 18
 ARR_TIES = 19
+ARR_ROUTER = 20
 
 _lib = None
 _gpu_lib = None
@@ -144,6 +145,13 @@ WORKLOADS: Dict[str, Workload] = {
     "prefill_dense": Workload("prefill_dense", E=896, H=7168, I=1536, k=16, T=512, logits="dense16", pool=0,
                               sub=6),
 }
+
+
+def router_weights(seed: int, wl: Workload, layer: int = 0) -> np.ndarray:
+    """Router projection weights w_r[E][H] fp32 ~ N(0, 1/H), so that for
+    activations N(0, 1) the logits are about N(0, 1) like the logit recipes."""
+    return normal_f32(key(seed, ARR_ROUTER, wl.pool, layer), wl.E * wl.H,
+                      stddev=float(1.0 / np.sqrt(wl.H))).reshape(wl.E, wl.H)
 
 
 def slab_bytes(H: int, I: int) -> int:

@@ -56,9 +56,10 @@ def lib():
         L.oracle_token_layer.argtypes = [_P, _P, _P, _I32, W, _P]
         L.oracle_token_layer_f64.argtypes = [_P, _P, _P, _I32, W, _P]
         L.oracle_dense_token.argtypes = [_P, _P, _I32, _I32, W, _P]
+        L.oracle_router_logits.argtypes = [_P, _I32, _I32, _P, _I32, _P, _I32]
         for f in ("oracle_route_topk", "oracle_group_rows", "oracle_gateup", "oracle_down", "oracle_combine",
                   "oracle_rms_rescale_bf16", "oracle_token_layer", "oracle_token_layer_f64",
-                  "oracle_dense_token"):
+                  "oracle_dense_token", "oracle_router_logits"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -147,6 +148,18 @@ def rms_rescale_bf16(y: np.ndarray, eps: float = 1e-6) -> np.ndarray:
     x = np.zeros((T, H), np.uint16)
     lib().oracle_rms_rescale_bf16(y.ctypes.data, T, H, eps, x.ctypes.data)
     return x
+
+
+def router_logits(x: np.ndarray, w_router: np.ndarray, nthreads: int = 8) -> np.ndarray:
+    """logits[T][E] = x[T][H] (bf16 bits) . w_router[E][H]^T (fp32), fp32 sums in
+    ascending H (the router projection before the path)."""
+    x, wr = _c(x, np.uint16), _c(w_router, np.float32)
+    T, H = x.shape
+    E = wr.shape[0]
+    assert wr.shape[1] == H
+    out = np.zeros((T, E), np.float32)
+    lib().oracle_router_logits(x.ctypes.data, T, H, wr.ctypes.data, E, out.ctypes.data, nthreads)
+    return out
 
 
 def layer(x: np.ndarray, logits: np.ndarray, k: int, pool: Pool, nthreads: int = 8) -> Dict[str, np.ndarray]:

@@ -25,6 +25,9 @@
 //   down     y_n = sum_i h_i Wd[n][i] (fp32, i ascending)
 //   combine  out[t] = sum_j w[t][j] y(t, j) (fp32, j ascending)
 //   rescale  x_next = bf16_rne(y / sqrt(mean(y^2) + eps)) between stacked layers
+//   router   logits[t][e] = sum_c x[t][c] Wr[e][c] (fp32 weights, fp32, c
+//            ascending): the projection before the path that feeds route
+//            (page 1, section on how it works: the router picks the experts)
 //
 // Accumulation is fp32 in the stated order; the build uses -ffp-contract=off
 // so no product is fused into an add.  A double-accumulation variant of the
@@ -322,6 +325,24 @@ int oracle_dense_token(const uint16_t* x_t, const float* logits_t, int32_t E, in
     for (int j = 0; j < k; ++j) acc += (ex[j] / S) * yall[(int64_t)order[j] * H + n];
     out_t[n] = acc;
   }
+  return 0;
+}
+
+// Router projection: logits[t][e] = sum_{c=0}^{H-1} x[t][c] * wr[e][c], x bf16
+// (exact in fp32), wr fp32 [E][H], fp32 accumulation with c ascending.
+// Tokens are spread over nthreads host threads (each logit is one thread's
+// fixed-order sum, so the result does not depend on nthreads).
+int oracle_router_logits(const uint16_t* x, int32_t T, int32_t H, const float* wr, int32_t E, float* logits,
+                         int32_t nthreads) {
+  parallel_for(T, nthreads, [&](int64_t t) {
+    std::vector<float> xf(H);
+    for (int64_t c = 0; c < H; ++c) xf[c] = bf16_to_f32(x[t * H + c]);
+    for (int64_t e = 0; e < E; ++e) {
+      float acc = 0.0f;
+      for (int64_t c = 0; c < H; ++c) acc += xf[c] * wr[e * H + c];
+      logits[t * E + e] = acc;
+    }
+  });
   return 0;
 }
 

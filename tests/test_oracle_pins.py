@@ -324,3 +324,78 @@ def test_byte_model_matches_pages():
     assert abs(total / spec["pages_expert_total_bytes"] - 1) < spec["pages_expert_total_rel_tol"]
     assert abs(b / 1e6 / spec["pages_file_mb"] - 1) < spec["pages_file_rel_tol"]
     assert spec["experts_total"] % spec["layers"] == 0 and spec["experts_total"] // spec["layers"] == 896
+
+
+# ---------------------------------------------------------------- router --
+def _bf16_bits(a: np.ndarray) -> np.ndarray:
+    """float32 values that bf16 holds exactly -> their bf16 bit patterns."""
+    u = np.ascontiguousarray(a, np.float32).view(np.uint32)
+    assert np.all((u & 0xFFFF) == 0)
+    return (u >> 16).astype(np.uint16)
+
+
+def _bf16_values(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def test_router_one_hot_input_selects_a_weight_column():
+    wl = synth.Workload("r", E=40, H=96, I=32, k=4, T=3)
+    wr = synth.router_weights(3, wl)
+    x = np.zeros((3, wl.H), np.float32)
+    cols = [0, 17, 95]
+    for t, c in enumerate(cols):
+        x[t, c] = 1.0
+    got = oracle.router_logits(_bf16_bits(x), wr)
+    for t, c in enumerate(cols):
+        assert np.array_equal(got[t], wr[:, c])
+
+
+def test_router_power_of_two_scaling_is_exact():
+    wl = synth.Workload("r", E=24, H=256, I=32, k=4, T=5, sub=9)
+    wr = synth.router_weights(0, wl)
+    x = synth.activations_bf16(0, wl)
+    base = oracle.router_logits(x, wr)
+    x4 = _bf16_bits(_bf16_values(x) * 4.0)
+    assert np.array_equal(oracle.router_logits(x4, wr), base * 4.0)
+
+
+def test_router_expert_permutation_permutes_logits_exactly():
+    wl = synth.Workload("r", E=30, H=128, I=32, k=4, T=4, sub=10)
+    wr = synth.router_weights(1, wl)
+    x = synth.activations_bf16(1, wl)
+    perm = np.random.default_rng(5).permutation(wl.E)
+    assert np.array_equal(oracle.router_logits(x, wr[perm]), oracle.router_logits(x, wr)[:, perm])
+
+
+@pytest.mark.parametrize("E,H,T", [(896, 7168, 2), (64, 96, 7), (8, 256, 4)])
+def test_router_within_the_fp32_summation_bound_of_float64(E, H, T):
+    """|fp32 result - exact| <= g(H + 1) * sum |x w| with g(n) = n u / (1 - n u),
+    u = 2^-24 (recursive summation of H rounded products; Higham, Accuracy and
+    Stability of Numerical Algorithms, 2nd ed., section 3.1); exact = a float64
+    matmul of the same values (itself within 1e-12 relative here)."""
+    wl = synth.Workload("r", E=E, H=H, I=32, k=4, T=T, sub=11)
+    wr = synth.router_weights(2, wl)
+    x = synth.activations_bf16(2, wl)
+    got = oracle.router_logits(x, wr, nthreads=8).astype(np.float64)
+    xf = _bf16_values(x).astype(np.float64)
+    exact = xf @ wr.astype(np.float64).T
+    mag = np.abs(xf) @ np.abs(wr.astype(np.float64)).T
+    u = 2.0 ** -24
+    g = (H + 1) * u / (1 - (H + 1) * u)
+    assert np.all(np.abs(got - exact) <= g * mag)
+    # and the logits are about N(0, 1), as the logit recipes are
+    assert 0.5 < got.std() < 2.0
+
+
+def test_router_bound_test_catches_a_planted_error():
+    """The bound above is tight enough to see a single dropped term."""
+    wl = synth.Workload("r", E=16, H=256, I=32, k=4, T=3, sub=12)
+    wr = synth.router_weights(4, wl)
+    x = synth.activations_bf16(4, wl)
+    got = oracle.router_logits(x, wr).astype(np.float64)
+    xf = _bf16_values(x).astype(np.float64)
+    dropped = xf[:, 1:] @ wr[:, 1:].astype(np.float64).T  # the first term left out
+    mag = np.abs(xf) @ np.abs(wr.astype(np.float64)).T
+    u = 2.0 ** -24
+    g = (wl.H + 1) * u / (1 - (wl.H + 1) * u)
+    assert np.any(np.abs(got - dropped) > g * mag)
