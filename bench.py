@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 FP4_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4 MFMA
+FP32_PEAK_TFLOPS = 157.3  # MI355X fp32 (vector and MFMA)
 METRIC = "MoE MXFP4 expert layer: decode weight GB/s + prefill TFLOP/s, % of roofline"
 
 
@@ -197,6 +198,8 @@ def main():
         res["prefill512"] = prefill_side(dev, pool, args.seed, args.prefill_reps, "prefill512")
         res["prefill_dense"] = prefill_side(dev, pool, args.seed, args.prefill_reps, "prefill_dense")
         res["prefill4096"] = prefill_side(dev, pool, args.seed, max(2, args.prefill_reps // 4), "prefill4096")
+    if args.side_reps > 0:
+        res["router"] = router_side(dev, args.seed, args.side_reps)
     if args.stack_reps > 0:
         res["stack92"] = stack_side(dev, args.seed, args.stack_reps)
 
@@ -252,6 +255,38 @@ def verify_side(dev, pool, seed, reps):
     log(f"verify8: {np.median(each):.1f} us/layer (median), {gbs:.0f} GB/s over {np.mean(uniq):.1f} unique experts")
     return {"us_per_layer": pct(each), "weight_gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "unique_experts_mean": round(float(np.mean(uniq)), 2), "variants": V}
+
+
+def router_side(dev, seed, reps):
+    """The router projection before the path (x . W_r^T, fp32 weights
+    896 x 7168): one token streams W_r (25.7 MB, HBM-bound); 512 tokens are
+    2*T*E*H flops against the fp32 peak."""
+    import numpy as np
+    import torch
+
+    from mxfp4_routed_expert_02_amd import router_logits, synth
+
+    out = {}
+    for name, T in (("decode", 1), ("prefill512", 512)):
+        wl = synth.Workload("router", E=896, H=7168, I=1536, k=16, T=T, sub=8)
+        V = 4  # rotating weight matrices (103 MB) so the last-level cache does not serve W_r
+        wrs = [torch.from_numpy(synth.router_weights(seed, wl, layer=v)).to(dev) for v in range(V)]
+        x = torch.from_numpy(synth.activations_bf16(seed, wl).view(np.int16)).to(dev).view(torch.bfloat16)
+        logits = torch.empty((T, wl.E), dtype=torch.float32, device=dev)
+        for v in range(V):
+            router_logits(x, wrs[v], logits)
+        stream = torch.cuda.current_stream(dev)
+        each = per_call_us(lambda i: router_logits(x, wrs[i % V], logits), reps, stream)
+        us = float(np.median(each))
+        wbytes = wl.E * wl.H * 4
+        flops = 2.0 * T * wl.E * wl.H
+        out[name] = {"us": pct(each), "weight_gbs": round(wbytes / (us * 1e-6) / 1e9, 1),
+                     "tflops": round(flops / (us * 1e-6) / 1e12, 2),
+                     "frac_hbm_peak": round(wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "frac_fp32_peak": round(flops / (us * 1e-6) / 1e12 / FP32_PEAK_TFLOPS, 4)}
+        log(f"router {name}: {us:.1f} us (median), {out[name]['weight_gbs']} GB/s of W_r, "
+            f"{out[name]['tflops']} TFLOP/s")
+    return out
 
 
 def prefill_side(dev, pool, seed, reps, name):

@@ -173,6 +173,23 @@ MOE_API size_t moe_workspace_bytes(int32_t T, int32_t k, int32_t E, int32_t H, i
 MOE_API const char* moe_status_string(moe_status s);
 
 /*
+ * moe_router_logits - the router projection that feeds moe_route_topk (the
+ * step before the path; the router picks each token's experts from these
+ * logits: page "hn.213312.xyz/article/49090233", section on how it works;
+ * the pages give no router form, so this takes the plain linear one):
+ *   logits[t][e] = sum_{c=0}^{H-1} x[t][c] * w_router[e][c]
+ * with fp32 products and sums (the order of the sums is the library's; the
+ * result lies within the fp32 summation bound of the exact value).
+ *   x_bf16    [T][H] bf16 bits, 16-byte aligned
+ *   w_router  [E][H] fp32, 16-byte aligned
+ *   logits    [T][E] fp32 out
+ * E in 1..MOE_MAX_EXPERTS, H a multiple of 32 in 32..MOE_MAX_DIM,
+ * T*E <= INT32_MAX (MOE_ERR_INVALID_ARG otherwise).
+ */
+MOE_API moe_status moe_router_logits(const uint16_t* x_bf16, int32_t T, int32_t H, const float* w_router,
+                                     int32_t E, float* logits, moe_stream_t stream);
+
+/*
  * moe_rms_rescale_bf16 - glue between stacked layers (not one of the four
  * calls of a layer): x_next[t] = bf16_rne(y[t] / sqrt(mean(y[t]^2) + eps)),
  * the weightless RMS rescaling that feeds layer l's output to layer l+1.

@@ -9,6 +9,7 @@ calls raise.
 One layer (the routed experts of a Kimi K3 layer: 16 experts picked per
 token, MXFP4 weights, SwiGLU FFN, weighted combine):
 
+    logits = router_logits(x, w_router)      # the projection before the path
     ids, w = route_topk(logits, k)
     grp = group_rows(ids, E, workspace)
     y_rows = expert_ffn_mxfp4(x, k, pool, grp, workspace)
@@ -26,6 +27,7 @@ from ._binding import (  # noqa: F401
     lib,
     rms_rescale_bf16,
     route_topk,
+    router_logits,
     status_string,
     workspace_bytes,
     MAX_EXPERTS,

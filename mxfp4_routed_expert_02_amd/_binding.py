@@ -51,12 +51,13 @@ def lib():
         L.moe_expert_ffn_mxfp4.argtypes = [_P, _I32, _I32, W, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_combine.argtypes = [_P, _P, _P, _I32, _I32, _I32, _P, _P]
         L.moe_rms_rescale_bf16.argtypes = [_P, _I32, _I32, ctypes.c_float, _P, _P]
+        L.moe_router_logits.argtypes = [_P, _I32, _I32, _P, _I32, _P, _P]
         L.moe_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32, _I32]
         L.moe_workspace_bytes.restype = ctypes.c_size_t
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         for f in ("moe_route_topk", "moe_group_rows", "moe_expert_ffn_mxfp4", "moe_combine",
-                  "moe_rms_rescale_bf16"):
+                  "moe_rms_rescale_bf16", "moe_router_logits"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -186,4 +187,17 @@ def rms_rescale_bf16(y: torch.Tensor, eps: float = 1e-6, out: Optional[torch.Ten
     _check("moe_rms_rescale_bf16", lib().moe_rms_rescale_bf16(
         _dev(y, torch.float32, "y"), T, H, eps, _dev(out.view(torch.int16), torch.int16, "x_next"),
         _stream(y.device)))
+    return out
+
+
+def router_logits(x: torch.Tensor, w_router: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """logits [T, E] fp32 = x [T, H] (bf16) . w_router [E, H] (fp32)^T."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    xb = x.view(torch.int16) if x.dtype == torch.bfloat16 else x
+    if out is None:
+        out = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    _check("moe_router_logits", lib().moe_router_logits(
+        _dev(xb, torch.int16, "x"), T, H, _dev(w_router, torch.float32, "w_router"), E,
+        _dev(out, torch.float32, "logits"), _stream(x.device)))
     return out

@@ -128,4 +128,17 @@ moe_status moe_rms_rescale_bf16(const float* y, int32_t T, int32_t H, float eps,
   return from_hip(moe::launch_rms_rescale(y, T, H, eps, x_next, (hipStream_t)stream));
 }
 
+moe_status moe_router_logits(const uint16_t* x_bf16, int32_t T, int32_t H, const float* w_router, int32_t E,
+                             float* logits, moe_stream_t stream) {
+  if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || H < 32 || H > MOE_MAX_DIM || (H & 31) != 0)
+    return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!x_bf16 || !w_router || !logits)) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!aligned16(x_bf16) || !aligned16(w_router) || ((uintptr_t)logits & 3) != 0))
+    return MOE_ERR_INVALID_ARG;
+  if ((int64_t)T * E > INT32_MAX) return MOE_ERR_INVALID_ARG;
+  const moe_status d = check_device();
+  if (d != MOE_OK) return d;
+  return from_hip(moe::launch_router_logits(x_bf16, T, H, w_router, E, logits, (hipStream_t)stream));
+}
+
 }  // extern "C"

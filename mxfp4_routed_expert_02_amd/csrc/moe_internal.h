@@ -123,4 +123,7 @@ hipError_t launch_combine(const float* y_rows, const float* w, const int32_t* ro
 
 hipError_t launch_rms_rescale(const float* y, int T, int H, float eps, uint16_t* x_next, hipStream_t s);
 
+hipError_t launch_router_logits(const uint16_t* x, int T, int H, const float* wr, int E, float* logits,
+                                hipStream_t s);
+
 }  // namespace moe

@@ -111,6 +111,18 @@ def test_combine_and_rescale_reject_bad_arguments(L):
     assert L.moe_rms_rescale_bf16(FAKE + 4, 1, 64, 1e-6, FAKE, None) == INVALID  # y not 16-byte aligned
 
 
+def test_router_logits_validation(L):
+    assert L.moe_router_logits(FAKE, 1, 7168, FAKE, 896, FAKE, None) == HIPERR  # valid args, no GPU here
+    assert L.moe_router_logits(FAKE, -1, 7168, FAKE, 896, FAKE, None) == INVALID
+    assert L.moe_router_logits(FAKE, 1, 7100, FAKE, 896, FAKE, None) == INVALID  # H not a multiple of 32
+    assert L.moe_router_logits(FAKE, 1, 7168, FAKE, 0, FAKE, None) == INVALID
+    assert L.moe_router_logits(FAKE, 1, 7168, FAKE, 5000, FAKE, None) == INVALID
+    assert L.moe_router_logits(None, 1, 7168, FAKE, 896, FAKE, None) == INVALID
+    assert L.moe_router_logits(FAKE + 8, 1, 7168, FAKE, 896, FAKE, None) == INVALID  # x not 16-byte aligned
+    assert L.moe_router_logits(FAKE, 1, 7168, FAKE + 4, 896, FAKE, None) == INVALID  # w not 16-byte aligned
+    assert L.moe_router_logits(None, 0, 7168, None, 896, None, None) == HIPERR  # empty batch: nothing to check
+
+
 def test_valid_call_without_gpu_reports_hip_error(L):
     import torch
 
