@@ -27,18 +27,21 @@
 // Tiles: 256 weight rows x 128 tokens per block of 4 waves, one block per
 // CU (32 tokens per wave, 8 row blocks of 32 each, accumulators in AGPRs).
 // For gate/up the 256 rows are gate rows i0..i0+127 followed by the same up
-// rows, so SiLU(g)*u is formed in registers.  The A tile of each 256-value K
-// stage is staged in LDS (double-buffered, rows padded against bank
-// conflicts) and shared by the 4 waves; each wave streams its own B into
-// registers one stage ahead.  256 rows per tile halve the B bytes per MFMA
-// against 128, which keeps the vector-memory path under the MFMA time.
+// rows, so SiLU(g)*u is formed in registers.  Every operand of a 128-value
+// K stage (weight codes and scales, activation terms and scales) travels
+// from global memory into an LDS ring slot by LDS DMA loads, with no trip
+// through registers; the ring keeps up to five stages in flight per CU, so
+// tiles with few tokens stream their weights at memory speed and full
+// tiles keep the MFMA pipe fed.  The waits on those loads are explicit
+// counts of each wave's own loads, which complete in issue order.
 // A tile's 128 token slots form 4 groups of 32; a tile whose expert rows
 // fill only 1 or 2 groups runs with the 4 waves splitting the row blocks
-// instead (2 or 4 blocks each, gate blocks kept with their up blocks), so
-// MFMA work follows the routed rows rather than the padded tile.  The plan
-// orders (expert, token tile) pairs heaviest first and deals them to the 8
-// XCDs in turn; each XCD runs its pairs' weight tiles consecutively, so
-// tiles sharing a token tile share that XCD's L2.
+// instead (2 or 4 blocks each, gate blocks kept with their up blocks) and a
+// deeper ring of smaller slots, so MFMA work follows the routed rows rather
+// than the padded tile.  The plan orders (expert, token tile) pairs
+// heaviest first and deals them to the 8 XCDs in turn; each XCD runs its
+// pairs' weight tiles consecutively, so tiles sharing a token tile share
+// that XCD's L2.
 #include <climits>
 #include <type_traits>
 
@@ -49,8 +52,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTileRows = 256;    // weight rows per block
 constexpr int kTileTok = 128;     // tokens per block
-constexpr int kStageK = 256;      // K values per LDS stage
-constexpr int kStageBytes = 128;  // FP4 bytes per row per stage
+constexpr int kStageK = 128;      // K values per LDS stage
 
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef float v16f_t __attribute__((ext_vector_type(16)));
@@ -93,12 +95,15 @@ __device__ __forceinline__ int e4m3_block_exp(float amax) {
 }
 
 // Quantizes rows of a [rows][K] matrix (bf16 bits or fp32) into two E4M3
-// terms: q[row][2][K] bytes (quarters of each 64 values in the order
-// 0,2,1,3), s[row][2][K/256][2][4] scale bytes where the scale of 32-block
-// j = 8*stage + 2*step + half sits at [stage][half][step].
+// terms, stored stage-major so that one 128-value K stage of every row is
+// one contiguous block (whatever rows a GEMM tile gathers, its loads of a
+// stage stay within a few pages):
+//   q[K/128][rows][2][128]  bytes (quarters of each 64 values in the order
+//                           0,2,1,3)
+//   s[K/128][rows][2][4]    E8M0 scale bytes of the stage's four 32-blocks
 // One thread per (row, 32-block).
 template <bool BF16_IN>
-__device__ __forceinline__ void quantize_block(const void* src, int row, int blk, int K, uint8_t* __restrict__ q,
+__device__ __forceinline__ void quantize_block(const void* src, int row, int rows, int blk, int K, uint8_t* __restrict__ q,
                                                uint8_t* __restrict__ s) {
   float v[32];
   if (BF16_IN) {
@@ -124,7 +129,6 @@ __device__ __forceinline__ void quantize_block(const void* src, int row, int blk
       v[4 * i + 3] = w.w;
     }
   }
-  const int sidx = (blk >> 3) * 8 + (blk & 1) * 4 + ((blk >> 1) & 3);
 #pragma unroll
   for (int term = 0; term < 2; ++term) {
     float amax = 0.0f;
@@ -144,16 +148,17 @@ __device__ __forceinline__ void quantize_block(const void* src, int row, int blk
       v[i] -= qv * scl;  // residual for the next term (exact)
     }
     // quarters 0,1,2,3 of each 64 values are stored in the order 0,2,1,3
-    uint8_t* g64 = q + ((int64_t)row * 2 + term) * K + 64 * (blk >> 1);
+    const int64_t st = blk >> 2;
+    uint8_t* g64 = q + (st * rows + row) * 256 + term * 128 + 64 * ((blk >> 1) & 1);
     *(uint4*)(g64 + 16 * (blk & 1)) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
     *(uint4*)(g64 + 32 + 16 * (blk & 1)) = make_uint4(packed[4], packed[5], packed[6], packed[7]);
-    s[((int64_t)row * 2 + term) * (K / 32) + sidx] = (uint8_t)(e + 127);
+    s[(st * rows + row) * 8 + term * 4 + (blk & 3)] = (uint8_t)(e + 127);
   }
 }
 
 // x [T][H] bf16 -> two E4M3 terms; block 0 also writes the tile plan: one
 // (slot, token tile) pair per token tile of every active expert with more
-// than kRegRows rows, in active-list order, and the pair count in plan[0].
+// than kRegRows rows, and the pair count in plan[0].
 __global__ __launch_bounds__(kThreads) void mfma_prep_kernel(const uint16_t* __restrict__ x, int T, int H,
                                                             const int32_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ active,
@@ -241,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void mfma_prep_kernel(const uint16_t* __r
   const int nblk = H >> 5;
   const int64_t i = (int64_t)(blockIdx.x - 1) * kThreads + threadIdx.x;
   if (i >= (int64_t)T * nblk) return;
-  quantize_block<true>(x, (int)(i / nblk), (int)(i % nblk), H, xq, xs);
+  quantize_block<true>(x, (int)(i / nblk), T, (int)(i % nblk), H, xq, xs);
 }
 
 // h [R][I] fp32 -> two E4M3 terms, for every row
@@ -250,49 +255,107 @@ __global__ __launch_bounds__(kThreads) void quantize_h_kernel(const float* __res
   const int nblk = I >> 5;
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (i >= (int64_t)R * nblk) return;
-  quantize_block<false>(h, (int)(i / nblk), (int)(i % nblk), I, hq, hs);
+  quantize_block<false>(h, (int)(i / nblk), R, (int)(i % nblk), I, hq, hs);
 }
 
 // ------------------------------------------------------------------ GEMM --
 
-// 8 scale bytes of a row (natural order j = 2*step + half) -> [half][step]
-__device__ __forceinline__ uint2 scales_by_half(uint2 v) {
-  // bytes b0..b7 -> (b0, b2, b4, b6), (b1, b3, b5, b7)
-  const uint32_t lo = __builtin_amdgcn_perm(v.y, v.x, 0x06040200u);
-  const uint32_t hi = __builtin_amdgcn_perm(v.y, v.x, 0x07050301u);
-  return make_uint2(lo, hi);
+// LDS ring.  A slot holds one 128-value K stage of every operand of the tile,
+// written straight from global memory by LDS DMA loads (a wave's load puts
+// lane l's 16 or 4 bytes at the slot offset + size * l):
+//   A   [256 rows][64 B]    weight codes; 16-byte piece p of row r at
+//                           r*64 + 16*(p ^ ((r >> 2) & 3))
+//   AS  [256 rows][4 B]     the rows' four scale bytes of the stage, as stored
+//   B   [2][32*TG][128 B]   activation terms; piece p of (term u, token t) at
+//                           (u*32*TG + t)*128 + 16*(p ^ ((t >> 1) & 7))
+//   BS  [2][32*TG][4 B]     their four scale bytes of the stage
+// The XOR swizzles give the 16 lanes that read one K offset of 16
+// consecutive rows or tokens 16 distinct 16-byte bank groups.  A tile with
+// TG token groups of 32 has slots of 25.3, 33.5 or 50 KB and a ring of 6, 4
+// or 3 of them, so 5, 3 or 2 stages (126, 100, 100 KB) are in flight per CU
+// while one is read.
+constexpr int kLdsBytes = 160 * 1024;
+
+template <int TG>
+struct Ring {
+  static constexpr int kTok = 32 * TG;
+  static constexpr int kA = kTileRows * 64;
+  static constexpr int kAS = kTileRows * 4;
+  static constexpr int kB = 2 * kTok * 128;
+  static constexpr int kBS = 2 * kTok * 4;
+  static constexpr int kStage = kA + kAS + kB + kBS;
+  static constexpr int kSlots = kLdsBytes / kStage;
+  static constexpr int kOps = 4 + 1 + 2 * TG + 1;  // DMA loads per wave per stage
+  static_assert(kStage % 16 == 0, "16-byte aligned slots");
+};
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+constexpr int kRingBytes = cmax(cmax(Ring<1>::kSlots * Ring<1>::kStage, Ring<2>::kSlots * Ring<2>::kStage),
+                                Ring<4>::kSlots * Ring<4>::kStage);
+
+// LDS DMA loads of 16 and 4 bytes per lane to the wave-uniform LDS address
+// `lds` (lane l at lds + size*l).  Issued from asm, so the compiler neither
+// counts them nor waits for them: the ring's waits below are explicit.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
 }
 
-// One 64-deep K step of a 32x32 block: FP4 weights (format 4) times the
-// two E4M3 activation terms (format 0); OPSEL picks byte OPSEL of each
-// packed scale word (the step's block scale).
-template <int OPSEL>
-__device__ __forceinline__ v16f_t mfma_step(const v8i_t& A, const v8i_t& B0, const v8i_t& B1, v16f_t acc,
-                                            uint32_t sa, uint32_t sb0, uint32_t sb1) {
-  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B0, acc, 4, 0, OPSEL, sa, OPSEL, sb0);
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B1, acc, 4, 0, OPSEL, sa, OPSEL, sb1);
+// s_waitcnt vmcnt(N) (N clamped to the counter's 63) with the other counters free
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  constexpr int M = N > 63 ? 63 : N;
+  __builtin_amdgcn_s_waitcnt((M & 15) | ((M >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Wait until at most n stages of this wave's DMA loads (OPS each) are
+// outstanding.  Vector-memory loads complete in issue order, so this waits
+// for every stage issued before the n most recent ones.
+template <int OPS>
+__device__ __forceinline__ void wait_stages(int n) {
+  switch (n) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<OPS>(); break;
+    case 2: wait_vm<2 * OPS>(); break;
+    case 3: wait_vm<3 * OPS>(); break;
+    case 4: wait_vm<4 * OPS>(); break;
+    default: wait_vm<5 * OPS>(); break;
+  }
+}
+
+__device__ __forceinline__ v8i_t pack_b(const uint4& lo, const uint4& hi) {
+  v8i_t v;
+  v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+  v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+  return v;
+}
+
+// f(integral_constant<int, I>) for I = B .. E-1, in order
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>());
+    static_for<B + 1, E>(f);
+  }
 }
 
 template <bool GATEUP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void mfma_ffn_kernel(
     moe_mxfp4_weights w, int k, const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_rows,
     const int32_t* __restrict__ active, const int32_t* __restrict__ plan,
-    const uint8_t* __restrict__ bq,  // B terms [rows][2][K]
-    const uint8_t* __restrict__ bs,  // B scales [rows][2][K/32]
-    float* __restrict__ out, int m_tiles) {
-  // A stage: kTileRows rows of 128 bytes, rows padded to 144 bytes so that
-  // 16 consecutive rows read at the same column fall in distinct LDS banks
-  constexpr int kRowPitch = kStageBytes + 16;
-  constexpr int kRB = kTileRows / 32;  // 32-row blocks per wave
-  static_assert(kTileRows == kThreads, "one scale row per thread");
-  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][kTileRows * kRowPitch];
-  __shared__ __attribute__((aligned(16))) uint32_t s_sc[2][kTileRows * 2];  // [row][half] words by step
+    const uint8_t* __restrict__ bq,  // B terms [K/128][brows][2][128]
+    const uint8_t* __restrict__ bs,  // B scales [K/128][brows][2][4]
+    int brows, float* __restrict__ out, int m_tiles) {
+  __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kRingBytes];
+  constexpr int kRB = kTileRows / 32;  // 32-row blocks of the tile
 
   const int H = w.hidden, I = w.inter;
-  const int K = GATEUP ? H : I;               // reduction length
-  const int out_cols = GATEUP ? I : H;        // columns of the output rows
-  const uint32_t qrow = (uint32_t)K >> 1;     // FP4 bytes per weight row
-  const int nsb = K >> 5;                     // scale bytes per weight row
+  const int K = GATEUP ? H : I;         // reduction length
+  const int out_cols = GATEUP ? I : H;  // columns of the output rows
+  const int64_t qrow = K >> 1;          // FP4 bytes per weight row
+  const int nsb = K >> 5;               // scale bytes per weight row
+  const int nst = K / kStageK;
 
   // tile: XCD x = blockIdx % 8 runs pairs g = x, x + 8, ... of the plan
   // (heaviest first), each as m_tiles consecutive weight tiles
@@ -305,99 +368,117 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int p0 = offsets[e], cnt = offsets[e + 1] - p0;
   const int tok0 = ntile * kTileTok;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, half = lane >> 5;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)s_ring;
   const int64_t eo = (int64_t)e * w.expert_stride;
   // tile rows: gate/up = gate rows row0 .. row0+127 then the same up rows;
   // down = rows row0 .. row0+255
   const int row0 = GATEUP ? mt * (kTileRows / 2) : mt * kTileRows;
 
-  // A staging: thread t copies the 16-byte pieces (row (t/8) + 32 i, piece
-  // t%8), i = 0..7, and the 8 scale bytes of row t.  The pieces travel
-  // through named registers (no array, so they stay in VGPRs).
-  const int64_t rstride = (int64_t)32 * qrow;  // 32 rows
-  const uint8_t* a_lo;                         // pieces 0..3
-  const uint8_t* a_hi;                         // pieces 4..7
-  const uint8_t* s_row;
-  if (GATEUP) {
-    a_lo = w.gate_q + eo + (int64_t)(row0 + (tid >> 3)) * qrow + 16 * (tid & 7);
-    a_hi = w.up_q + eo + (int64_t)(row0 + (tid >> 3)) * qrow + 16 * (tid & 7);
-    s_row = tid < kTileRows / 2 ? w.gate_s + eo + (int64_t)(row0 + tid) * nsb
-                                : w.up_s + eo + (int64_t)(row0 + tid - kTileRows / 2) * nsb;
-  } else {
-    a_lo = w.down_q + eo + (int64_t)(row0 + (tid >> 3)) * qrow + 16 * (tid & 7);
-    a_hi = a_lo + 4 * rstride;
-    s_row = w.down_s + eo + (int64_t)(row0 + tid) * nsb;
-  }
-  uint4 aq0, aq1, aq2, aq3, aq4, aq5, aq6, aq7;
-  uint2 as2;
-#define MFMA_LOAD_A(ST)                                                  \
-  do {                                                                   \
-    const int so_ = (ST) * kStageBytes;                                  \
-    aq0 = *(const uint4*)(a_lo + so_);                                   \
-    aq1 = *(const uint4*)(a_lo + rstride + so_);                         \
-    aq2 = *(const uint4*)(a_lo + 2 * rstride + so_);                     \
-    aq3 = *(const uint4*)(a_lo + 3 * rstride + so_);                     \
-    aq4 = *(const uint4*)(a_hi + so_);                                   \
-    aq5 = *(const uint4*)(a_hi + rstride + so_);                         \
-    aq6 = *(const uint4*)(a_hi + 2 * rstride + so_);                     \
-    aq7 = *(const uint4*)(a_hi + 3 * rstride + so_);                     \
-    as2 = *(const uint2*)(s_row + (ST) * 8);                             \
-  } while (0)
-#define MFMA_STORE_A(BUF)                                                          \
-  do {                                                                             \
-    uint8_t* d_ = &s_a[BUF][(tid >> 3) * kRowPitch + 16 * (tid & 7)];              \
-    *(uint4*)(d_) = aq0;                                                           \
-    *(uint4*)(d_ + 32 * kRowPitch) = aq1;                                          \
-    *(uint4*)(d_ + 64 * kRowPitch) = aq2;                                          \
-    *(uint4*)(d_ + 96 * kRowPitch) = aq3;                                          \
-    *(uint4*)(d_ + 128 * kRowPitch) = aq4;                                         \
-    *(uint4*)(d_ + 160 * kRowPitch) = aq5;                                         \
-    *(uint4*)(d_ + 192 * kRowPitch) = aq6;                                         \
-    *(uint4*)(d_ + 224 * kRowPitch) = aq7;                                         \
-    *(uint2*)(&s_sc[BUF][2 * tid]) = scales_by_half(as2);                          \
-  } while (0)
+  auto a_row = [&](int r) -> const uint8_t* {  // codes of tile row r
+    if (GATEUP)
+      return r < kTileRows / 2 ? w.gate_q + eo + (int64_t)(row0 + r) * qrow
+                               : w.up_q + eo + (int64_t)(row0 + r - kTileRows / 2) * qrow;
+    return w.down_q + eo + (int64_t)(row0 + r) * qrow;
+  };
+  auto a_srow = [&](int r) -> const uint8_t* {  // scales of tile row r
+    if (GATEUP)
+      return r < kTileRows / 2 ? w.gate_s + eo + (int64_t)(row0 + r) * nsb
+                               : w.up_s + eo + (int64_t)(row0 + r - kTileRows / 2) * nsb;
+    return w.down_s + eo + (int64_t)(row0 + r) * nsb;
+  };
+  // B row of tile token t; tokens past the expert's count re-read its last row
+  auto b_row = [&](int t) -> int64_t {
+    const int tok = tok0 + t;
+    const int p = p0 + (tok < cnt ? tok : cnt - 1);
+    return GATEUP ? (int64_t)(sorted_rows[p] / k) : (int64_t)p;
+  };
 
   // Token groups of 32 that hold routed rows: 1, 2 or 4 (3 runs as 4).
-  // With tg groups, wave w takes token group w % tg and 2*tg of the 8 row
+  // With TG groups, wave w takes token group w % TG and 2*TG of the 8 row
   // blocks: gate/up keeps each gate block with its up block (b and b+4).
   const int rows_in_tile = min(cnt - tok0, kTileTok);
   const int tg = rows_in_tile <= 32 ? 1 : rows_in_tile <= 64 ? 2 : 4;
 
-  auto body = [&](auto rbw_c) {
-    constexpr int RBW = decltype(rbw_c)::value;  // row blocks of this wave
-    constexpr int TG = RBW / 2;                  // token groups of the tile
-    // row block of slot j is rb_base + rel(j); rel(j) is a compile-time
-    // offset so LDS addresses fold to immediates (rb_base = 0 with 8 blocks)
+  auto body = [&](auto tg_c) {
+    constexpr int TG = decltype(tg_c)::value;
+    using G = Ring<TG>;
+    constexpr int R = G::kSlots;
+    constexpr int RBW = 2 * TG;  // row blocks of this wave
+    const int tgi = wave % TG;
     const int rb_base = RBW == kRB ? 0 : (wave / TG) * (RBW / 2);
     auto rel = [](int j) { return j < RBW / 2 ? j : kRB / 2 + (j - RBW / 2); };
     auto rb_of = [&](int j) { return rb_base + rel(j); };
 
-    // this lane's B row (token); rows past the expert's count re-read its last row
-    const int n = lane & 31, half = lane >> 5;
-    const int tok = tok0 + (wave % TG) * 32 + n;
-    const bool tok_ok = tok < cnt;
-    const int p = p0 + (tok_ok ? tok : cnt - 1);
-    const int64_t brow = GATEUP ? (int64_t)(sorted_rows[p] / k) : (int64_t)p;
-    const uint8_t* b0 = bq + (brow * 2 + 0) * K + 32 * half;
-    const uint8_t* b1 = bq + (brow * 2 + 1) * K + 32 * half;
-    const uint32_t* bs0 = (const uint32_t*)(bs + (brow * 2 + 0) * nsb) + half;
-    const uint32_t* bs1 = (const uint32_t*)(bs + (brow * 2 + 1) * nsb) + half;
-
-    // B of one stage in two register sets used in turn: [step][piece]
-    // (pieces 0,1 = term 1, pieces 2,3 = term 2) and the two scale words
-    uint4 bp[16], bq2[16];
-    uint32_t sp0, sp1, sq0, sq1;
-    auto load_b = [&](int st, uint4 (&bb)[16], uint32_t& s0, uint32_t& s1) {
+    // DMA sources of this lane (stage 0).  A: load i of wave w fills 1 KB
+    // chunk c = 4i + w, rows 16c + lane/4, slot lane%4 of the row taking
+    // piece (lane%4) ^ ((lane >> 4) & 3).  AS: rows 64w + lane.  B: load j
+    // fills chunk c = w + 4j: term c / (4TG), tokens 8 (c % 4TG) + lane/8,
+    // slot lane%8 taking piece (lane%8) ^ ((token >> 1) & 7).  BS: entry
+    // 64 (w % TG) + lane = term * 32TG + token (waves past TG repeat it).
+    const int apiece = (lane & 3) ^ ((lane >> 4) & 3);
+    const uint8_t* asrc[4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int koff = st * kStageK + 64 * s;
-        bb[4 * s + 0] = *(const uint4*)(b0 + koff);
-        bb[4 * s + 1] = *(const uint4*)(b0 + koff + 16);
-        bb[4 * s + 2] = *(const uint4*)(b1 + koff);
-        bb[4 * s + 3] = *(const uint4*)(b1 + koff + 16);
-      }
-      s0 = bs0[2 * st];
-      s1 = bs1[2 * st];
+    for (int i = 0; i < 4; ++i) asrc[i] = a_row(16 * (4 * i + wave) + (lane >> 2)) + 16 * apiece;
+    const uint8_t* assrc = a_srow(64 * wave + lane);
+    const uint8_t* bsrc[2 * TG];
+#pragma unroll
+    for (int j = 0; j < 2 * TG; ++j) {
+      const int c = wave + 4 * j, u = c / (4 * TG);
+      const int t = 8 * (c % (4 * TG)) + (lane >> 3);
+      bsrc[j] = bq + (b_row(t) * 2 + u) * 128 + 16 * ((lane & 7) ^ ((t >> 1) & 7));
+    }
+    const int be = 64 * tgi + lane;
+    const uint8_t* bssrc = bs + (b_row(be % G::kTok) * 2 + be / G::kTok) * 4;
+    const int64_t bq_stage = (int64_t)brows * 256, bs_stage = (int64_t)brows * 8;
+
+    // load o (0 .. kOps-1) of this wave's share of stage st into slot sl
+    auto issue_op = [&](int st, int sl, auto o_c) {
+      constexpr int o = decltype(o_c)::value;
+      const uint32_t sb = lds0 + (uint32_t)(sl * G::kStage);
+      if constexpr (o < 4) lds_dma16(asrc[o] + st * 64, sb + (4 * o + wave) * 1024);
+      else if constexpr (o == 4) lds_dma4(assrc + st * 4, sb + G::kA + wave * 256);
+      else if constexpr (o < 5 + 2 * TG)
+        lds_dma16(bsrc[o - 5] + st * bq_stage, sb + G::kA + G::kAS + (wave + 4 * (o - 5)) * 1024);
+      else lds_dma4(bssrc + st * bs_stage, sb + G::kA + G::kAS + G::kB + tgi * 256);
+    };
+    auto issue = [&](int st, int sl) { static_for<0, G::kOps>([&](auto o) { issue_op(st, sl, o); }); };
+
+    // fragment offsets of this lane within a slot: A row 32 rb + n, piece
+    // 2 s + half; B token 32 tgi + n, pieces 4 s + 2 half + i (i = 0, 1)
+    const int tt = 32 * tgi + n;
+    const uint32_t a_off[2] = {(uint32_t)((32 * rb_base + n) * 64 + 16 * ((0 + half) ^ ((n >> 2) & 3))),
+                               (uint32_t)((32 * rb_base + n) * 64 + 16 * ((2 + half) ^ ((n >> 2) & 3)))};
+    const uint32_t as_off = (uint32_t)(G::kA + (32 * rb_base + n) * 4);
+    uint32_t b_off[2][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        b_off[s][i] = (uint32_t)(G::kA + G::kAS + tt * 128 + 16 * ((4 * s + 2 * half + i) ^ ((n >> 1) & 7)));
+    const uint32_t bs_off = (uint32_t)(G::kA + G::kAS + G::kB + tt * 4);
+
+    auto read_a = [&](int sl, int s, uint4 (&a)[RBW]) {
+      const uint8_t* base = s_ring + sl * G::kStage + a_off[s];
+#pragma unroll
+      for (int j = 0; j < RBW; ++j) a[j] = *(const uint4*)(base + 32 * rel(j) * 64);
+    };
+    auto read_b = [&](int sl, int s, uint4 (&b)[2][2]) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) b[u][i] = *(const uint4*)(s_ring + sl * G::kStage + b_off[s][i] + u * G::kTok * 128);
+    };
+    // the stage's scale words, shifted so that step s's byte is byte 2s
+    auto read_sc = [&](int sl, uint32_t (&sa)[RBW], uint32_t (&sb)[2]) {
+#pragma unroll
+      for (int j = 0; j < RBW; ++j)
+        sa[j] = *(const uint32_t*)(s_ring + sl * G::kStage + as_off + 32 * rel(j) * 4) >> (8 * half);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        sb[u] = *(const uint32_t*)(s_ring + sl * G::kStage + bs_off + u * G::kTok * 4) >> (8 * half);
     };
 
     v16f_t acc[RBW];
@@ -406,100 +487,133 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[j][i] = 0.0f;
 
-    // the MFMAs of one stage: 4 steps x RBW row blocks x 2 terms.  Each A
-    // fragment (16 bytes per lane from LDS) feeds two MFMAs (128 cycles),
-    // less than the LDS latency under load, so the reads run kAhead
-    // fragments ahead of their use in a rotating set of registers.
-    constexpr int kAhead = 3;
-    constexpr int kFrags = 4 * RBW;  // (step, row block), step-major
-    auto compute = [&](int buf, const uint4 (&bb)[16], uint32_t s0, uint32_t s1) {
-      const uint8_t* a_base = &s_a[buf][(32 * rb_base + n) * kRowPitch + 16 * half];
-      const uint32_t* sc_base = &s_sc[buf][2 * (32 * rb_base + n) + half];
-      uint32_t sa[RBW];
+    // One 64-deep step: FP4 weights (format 4) times the two E4M3 terms
+    // (format 0), byte 2s of the scale words.
+    auto mma = [&](auto s_c, const uint4 (&a)[RBW], const uint4 (&b)[2][2], const uint32_t (&sa)[RBW],
+                   const uint32_t (&sb)[2]) {
+      constexpr int OP = 2 * decltype(s_c)::value;
+      const v8i_t B0 = pack_b(b[0][0], b[0][1]), B1 = pack_b(b[1][0], b[1][1]);
 #pragma unroll
-      for (int j = 0; j < RBW; ++j) sa[j] = sc_base[64 * rel(j)];
-      // fragment f = (s, j): row 32 rb_of(j) + n, 16-byte piece 2 s + half
-      // (block 2s+half of the stage row)
-      auto frag = [&](int f) {
-        return *(const uint4*)(a_base + (32 * rel(f % RBW)) * kRowPitch + 32 * (f / RBW));
-      };
-      uint4 fr[kAhead + 1];
-#pragma unroll
-      for (int f = 0; f < kAhead; ++f) fr[f] = frag(f);
-#pragma unroll
-      for (int f = 0; f < kFrags; ++f) {
-        if (f + kAhead < kFrags) fr[(f + kAhead) % (kAhead + 1)] = frag(f + kAhead);
-        const int s = f / RBW, j = f % RBW;
-        v8i_t B0, B1;
-        B0[0] = bb[4 * s].x; B0[1] = bb[4 * s].y; B0[2] = bb[4 * s].z; B0[3] = bb[4 * s].w;
-        B0[4] = bb[4 * s + 1].x; B0[5] = bb[4 * s + 1].y; B0[6] = bb[4 * s + 1].z; B0[7] = bb[4 * s + 1].w;
-        B1[0] = bb[4 * s + 2].x; B1[1] = bb[4 * s + 2].y; B1[2] = bb[4 * s + 2].z; B1[3] = bb[4 * s + 2].w;
-        B1[4] = bb[4 * s + 3].x; B1[5] = bb[4 * s + 3].y; B1[6] = bb[4 * s + 3].z; B1[7] = bb[4 * s + 3].w;
-        const uint4 wa = fr[f % (kAhead + 1)];
+      for (int j = 0; j < RBW; ++j) {
         v8i_t A;
-        A[0] = wa.x; A[1] = wa.y; A[2] = wa.z; A[3] = wa.w;
+        A[0] = a[j].x; A[1] = a[j].y; A[2] = a[j].z; A[3] = a[j].w;
         A[4] = 0; A[5] = 0; A[6] = 0; A[7] = 0;
-        if (s == 0) acc[j] = mfma_step<0>(A, B0, B1, acc[j], sa[j], s0, s1);
-        else if (s == 1) acc[j] = mfma_step<1>(A, B0, B1, acc[j], sa[j], s0, s1);
-        else if (s == 2) acc[j] = mfma_step<2>(A, B0, B1, acc[j], sa[j], s0, s1);
-        else acc[j] = mfma_step<3>(A, B0, B1, acc[j], sa[j], s0, s1);
+        acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B0, acc[j], 4, 0, OP, sa[j], OP, sb[0]);
+        acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B1, acc[j], 4, 0, OP, sa[j], OP, sb[1]);
       }
     };
 
-    // Issue order of one stage (masks: 0x100 LDS read, 0x008 MFMA, 0x020
-    // global read, 0x200 LDS write): the scale reads and the first kAhead
-    // fragments, then two MFMAs, one fragment read and the next share of
-    // the next stage's global loads at a time, and the A stores last.
-    // Spreading the 27 global loads over the MFMAs keeps the wave from
-    // stalling on the address path with its MFMAs queued behind them.
-    constexpr int kLoads = 9 + 18;  // A pieces + scales, B pieces + scale words
-    constexpr int kSlots = kFrags - kAhead;
-    constexpr int kPer = (kLoads + kSlots - 1) / kSlots;
-    auto stage_schedule = [&]() {
-      __builtin_amdgcn_sched_group_barrier(0x100, (RBW + 1) / 2 + kAhead, 0);
+    // Pipeline over stages st (slot st % R).  The ring is filled R stages
+    // ahead.  Within stage st: read its step-1 fragments, run step 0, wait
+    // for this wave's loads of stage st+1 and meet the other waves (after
+    // which stage st+1 is in LDS and nobody reads slot st % R any more),
+    // refill that slot with stage st+R, read stage st+1's step-0 fragments
+    // and scales, run step 1.  The steady-state loop (a stage R ahead left
+    // to load) is one basic block, so the step-0 MFMAs stay ahead of the
+    // wait and keep the pipe busy through it; the last R stages drain.
 #pragma unroll
-      for (int f = 0; f < kSlots; ++f) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        if (f * kPer < kLoads) __builtin_amdgcn_sched_group_barrier(0x020, kPer, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * kAhead, 0);
-      __builtin_amdgcn_sched_group_barrier(0x200, 9, 0);
-    };
-
-    // Pipeline: while the MFMAs of stage st run on LDS buffer st&1 and B
-    // register set st&1, the A pieces of stage st+1 (registers, stored to
-    // the other buffer after the MFMAs) and its B (the other register set)
-    // are in flight.  Both halves of a loop iteration are single basic
-    // blocks whose prefetches are used unconditionally (the odd half of the
-    // last pair re-loads the last stage), so the stage schedule applies to
-    // each.
-    const int nst = K / kStageK;
-    load_b(0, bp, sp0, sp1);
-    MFMA_LOAD_A(0);
-    MFMA_STORE_A(0);
+    for (int j = 0; j < R; ++j)
+      if (j < nst) issue(j, j);
+    wait_stages<G::kOps>(min(R - 1, nst - 1));
     __syncthreads();
-    int st = 0;
-    for (; st + 1 < nst; st += 2) {
-      // even stage: LDS buffer 0, register set bp; stage st+1 -> buffer 1 / bq2
-      MFMA_LOAD_A(st + 1);
-      load_b(st + 1, bq2, sq0, sq1);
-      compute(0, bp, sp0, sp1);
-      MFMA_STORE_A(1);
-      stage_schedule();
+    uint4 a0[RBW], b0[2][2];
+    uint32_t sa[RBW], sb[2];
+    read_sc(0, sa, sb);
+    read_a(0, 0, a0);
+    read_b(0, 0, b0);
+    int st = 0, sl = 0;
+    // one MFMA pair (both terms) of row block j at step s
+    auto mma_j = [&](auto s_c, auto j_c, const uint4& a, const v8i_t& B0, const v8i_t& B1, uint32_t sa_j,
+                     const uint32_t (&sbw)[2]) {
+      constexpr int OP = 2 * decltype(s_c)::value;
+      constexpr int j = decltype(j_c)::value;
+      v8i_t A;
+      A[0] = a.x; A[1] = a.y; A[2] = a.z; A[3] = a.w;
+      A[4] = 0; A[5] = 0; A[6] = 0; A[7] = 0;
+      acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B0, acc[j], 4, 0, OP, sa_j, OP, sbw[0]);
+      acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B1, acc[j], 4, 0, OP, sa_j, OP, sbw[1]);
+    };
+    // Steady stage (a stage R ahead left to load).  Issue order, fixed by
+    // scheduling fences between row-block groups: step 0's MFMA pairs each
+    // followed by a share of the step-1 fragment reads; the wait and the
+    // barrier; step 1's MFMA pairs each followed by a share of the refill
+    // loads and of the next stage's step-0 and scale reads.  Vector-memory
+    // issues spread over the MFMAs this way never back up the address path
+    // far enough to hold up the next MFMA.
+    auto steady_stage = [&]() {
+      constexpr int kReads1 = RBW + 4;        // step-1 fragments: RBW of A, 4 of B
+      constexpr int kReadsN = RBW + 4 + RBW + 2;  // next stage: A, B fragments and scale words
+      uint4 a1[RBW], b1[2][2];
+      const v8i_t B0 = pack_b(b0[0][0], b0[0][1]), B1 = pack_b(b0[1][0], b0[1][1]);
+      const uint8_t* a1_base = s_ring + sl * G::kStage + a_off[1];
+      static_for<0, RBW>([&](auto j_c) {
+        constexpr int j = decltype(j_c)::value;
+        mma_j(std::integral_constant<int, 0>(), j_c, a0[j], B0, B1, sa[j], sb);
+        static_for<j * kReads1 / RBW, (j + 1) * kReads1 / RBW>([&](auto r_c) {
+          constexpr int r = decltype(r_c)::value;
+          if constexpr (r < RBW) a1[r] = *(const uint4*)(a1_base + 32 * rel(r) * 64);
+          else b1[(r - RBW) / 2][(r - RBW) % 2] =
+                   *(const uint4*)(s_ring + sl * G::kStage + b_off[1][(r - RBW) % 2] + ((r - RBW) / 2) * G::kTok * 128);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      uint32_t sa1[RBW], sb1[2];
+#pragma unroll
+      for (int j = 0; j < RBW; ++j) sa1[j] = sa[j];
+      sb1[0] = sb[0];
+      sb1[1] = sb[1];
+      const int nsl = sl + 1 == R ? 0 : sl + 1;
+      wait_vm<(R - 2) * G::kOps>();
       __syncthreads();
-      // odd stage: LDS buffer 1, register set bq2; stage st+2 -> buffer 0 / bp
-      const int nx = min(st + 2, nst - 1);
-      MFMA_LOAD_A(nx);
-      load_b(nx, bp, sp0, sp1);
-      compute(1, bq2, sq0, sq1);
-      MFMA_STORE_A(0);
-      stage_schedule();
-      __syncthreads();
-    }
-    if (st < nst) compute(0, bp, sp0, sp1);  // odd stage count: the last stage
+      const v8i_t C0 = pack_b(b1[0][0], b1[0][1]), C1 = pack_b(b1[1][0], b1[1][1]);
+      const uint8_t* an_base = s_ring + nsl * G::kStage + a_off[0];
+      const uint8_t* sn_base = s_ring + nsl * G::kStage;
+      static_for<0, RBW>([&](auto j_c) {
+        constexpr int j = decltype(j_c)::value;
+        mma_j(std::integral_constant<int, 1>(), j_c, a1[j], C0, C1, sa1[j], sb1);
+        static_for<j * G::kOps / RBW, (j + 1) * G::kOps / RBW>([&](auto o_c) { issue_op(st + R, sl, o_c); });
+        static_for<j * kReadsN / RBW, (j + 1) * kReadsN / RBW>([&](auto r_c) {
+          constexpr int r = decltype(r_c)::value;
+          if constexpr (r < RBW) a0[r] = *(const uint4*)(an_base + 32 * rel(r) * 64);
+          else if constexpr (r < RBW + 4)
+            b0[(r - RBW) / 2][(r - RBW) % 2] =
+                *(const uint4*)(sn_base + b_off[0][(r - RBW) % 2] + ((r - RBW) / 2) * G::kTok * 128);
+          else if constexpr (r < 2 * RBW + 4)
+            sa[r - RBW - 4] = *(const uint32_t*)(sn_base + as_off + 32 * rel(r - RBW - 4) * 4) >> (8 * half);
+          else
+            sb[r - 2 * RBW - 4] = *(const uint32_t*)(sn_base + bs_off + (r - 2 * RBW - 4) * G::kTok * 4) >> (8 * half);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      sl = nsl;
+    };
+    // Draining stage: nothing left to load.
+    auto drain_stage = [&]() {
+      uint4 a1[RBW], b1[2][2];
+      read_a(sl, 1, a1);
+      read_b(sl, 1, b1);
+      mma(std::integral_constant<int, 0>(), a0, b0, sa, sb);
+      uint32_t sa1[RBW], sb1[2];
+#pragma unroll
+      for (int j = 0; j < RBW; ++j) sa1[j] = sa[j];
+      sb1[0] = sb[0];
+      sb1[1] = sb[1];
+      const int nsl = sl + 1 == R ? 0 : sl + 1;
+      if (st + 1 < nst) {
+        wait_stages<G::kOps>(nst - 2 - st);
+        __syncthreads();
+        read_sc(nsl, sa, sb);
+        read_a(nsl, 0, a0);
+        read_b(nsl, 0, b0);
+      }
+      mma(std::integral_constant<int, 1>(), a1, b1, sa1, sb1);
+      sl = nsl;
+    };
+    for (; st + R < nst; ++st) steady_stage();
+    for (; st < nst; ++st) drain_stage();
 
-    if (!tok_ok) return;
+    const int tok = tok0 + tgi * 32 + n;
+    if (tok >= cnt) return;
     float* orow = out + (int64_t)(p0 + tok) * out_cols;
     if (GATEUP) {
       // j < RBW/2: gate block rb_of(j); j + RBW/2: the matching up block
@@ -527,11 +641,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       }
     }
   };
-  if (tg == 1) body(std::integral_constant<int, 2>());
-  else if (tg == 2) body(std::integral_constant<int, 4>());
-  else body(std::integral_constant<int, 8>());
-#undef MFMA_LOAD_A
-#undef MFMA_STORE_A
+  if (tg == 1) body(std::integral_constant<int, 1>());
+  else if (tg == 2) body(std::integral_constant<int, 2>());
+  else body(std::integral_constant<int, 4>());
 }
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
@@ -540,10 +652,10 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 namespace moe {
 
-// K of both products in whole stages, whole row tiles (gate/up: I/128 tiles
-// of 128 gate + 128 up rows; down: H/256 tiles)
+// Whole row tiles (gate/up: I/128 tiles of 128 gate + 128 up rows; down:
+// H/256 tiles); K of both products is then a whole number of stages
 bool mfma_shape_ok(int H, int I) {
-  return H % kStageK == 0 && I % kStageK == 0 && I % (kTileRows / 2) == 0 && H % kTileRows == 0;
+  return H % kTileRows == 0 && I % (kTileRows / 2) == 0;
 }
 
 // Workspace of the MFMA path after the h buffer: x terms, x scales, h terms,
@@ -583,7 +695,7 @@ hipError_t launch_mfma_gateup(const uint16_t* x, int T, int k, const moe_mxfp4_w
   const int m_tiles = I / (kTileRows / 2);
   const unsigned grid = (unsigned)(8 * ((mfma_max_pairs(T, k, w.num_experts) + 7) / 8) * m_tiles);
   hipLaunchKernelGGL((mfma_ffn_kernel<true>), dim3(grid), dim3(kThreads), 0, s, w, k, offsets, sorted_rows, active,
-                     plan, xq, xs, h, m_tiles);
+                     plan, xq, xs, T, h, m_tiles);
   return hipGetLastError();
 }
 
@@ -606,7 +718,7 @@ hipError_t launch_mfma_down(int T, int k, const moe_mxfp4_weights& w, const int3
   const int m_tiles = H / kTileRows;
   const unsigned grid = (unsigned)(8 * ((mfma_max_pairs(T, k, w.num_experts) + 7) / 8) * m_tiles);
   hipLaunchKernelGGL((mfma_ffn_kernel<false>), dim3(grid), dim3(kThreads), 0, s, w, k, offsets, sorted_rows, active,
-                     plan, hq, hs, y_rows, m_tiles);
+                     plan, hq, hs, (int)R, y_rows, m_tiles);
   return hipGetLastError();
 }
 
