@@ -76,7 +76,8 @@ typedef enum {
  * array; expert e's array starts expert_stride bytes after expert e-1's.
  * The struct itself is host memory read during the call; the arrays are
  * device memory.  gate_q/up_q/down_q and expert_stride must be multiples of
- * 16 bytes; hidden and inter multiples of 32. */
+ * 16 bytes, gate_s/up_s/down_s multiples of 4; hidden and inter multiples
+ * of 32. */
 typedef struct {
   const uint8_t* gate_q; /* [E][I][H/2] */
   const uint8_t* gate_s; /* [E][I][H/32] */

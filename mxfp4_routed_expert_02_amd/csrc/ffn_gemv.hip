@@ -279,11 +279,12 @@ __device__ __forceinline__ uint32_t load1(__amdgpu_buffer_rsrc_t r, uint32_t off
 // items, so the work spreads over the experts that exist, not the upper
 // bound of them.
 
-// Slots of the experts with exactly one routed row (l1) and with 2 ..
-// kRegRows rows (l4), in slot order: l[0] = count, l[1..] = slots.  One block.
+// Slots of the experts with exactly one routed row (l1) and with 2 .. reg_max
+// rows (l4), in slot order: l[0] = count, l[1..] = slots.  One block.
 __global__ __launch_bounds__(kThreads) void small_lists_kernel(const int32_t* __restrict__ offsets,
                                                               const int32_t* __restrict__ active,
-                                                              int32_t* __restrict__ l1, int32_t* __restrict__ l4) {
+                                                              int32_t* __restrict__ l1, int32_t* __restrict__ l4,
+                                                              int reg_max) {
   __shared__ int s_part[2][kWaves];
   const int na = active[0];
   const int lane = threadIdx.x & (MOE_WAVE - 1), wave = threadIdx.x / MOE_WAVE;
@@ -295,7 +296,7 @@ __global__ __launch_bounds__(kThreads) void small_lists_kernel(const int32_t* __
       const int e = active[1 + a];
       const int cnt = offsets[e + 1] - offsets[e];
       f1 = cnt == 1;
-      f4 = cnt >= 2 && cnt <= kRegRows;
+      f4 = cnt >= 2 && cnt <= reg_max;
     }
     int v1 = f1, v4 = f4;
 #pragma unroll
@@ -711,7 +712,7 @@ hipError_t launch_expert_ffn(const uint16_t* x, int T, int k, const moe_mxfp4_we
   const int R = T * k, E = w.num_experts, H = w.hidden, I = w.inter;
   const int max_active = R < E ? R : E;
   float* hbuf = (float*)ws;
-  // Register GEMVs: experts with one row (MT = 1) and with 2..kRegRows rows
+  // Register GEMVs: experts with one row (MT = 1) and with 2..reg_max rows
   // (MT = kRegRows, same per-row arithmetic); a single token sends every
   // expert through MT = 1 (its row loop covers an id repeated in the token).
   // Experts with more rows take the grouped GEMM (MFMA) when the shape
@@ -719,6 +720,8 @@ hipError_t launch_expert_ffn(const uint16_t* x, int T, int k, const moe_mxfp4_we
   // (more than 8 blocks per lane) run on the LDS GEMV throughout.
   const GemvShape sg = gemv_shape(H >> 5, true), sd = gemv_shape(I >> 5, false);
   const bool reg_g = sg.ok, reg_d = sd.ok;
+  const bool use_mfma = T > 1 && reg_g && reg_d && mfma_shape_ok(H, I);
+  const int reg_max = use_mfma ? reg_rows_max(T) : kRegRows;
 
   hipError_t err = hipSuccess;
   const GemvArgs ga{x, k, &w, offsets, sorted_rows, active, hbuf, y_rows, s};
@@ -730,7 +733,7 @@ hipError_t launch_expert_ffn(const uint16_t* x, int T, int k, const moe_mxfp4_we
     l4 = l1 + 1 + max_active;
     off += lists_bytes(T, k, E);
     if (reg_g || reg_d) {
-      hipLaunchKernelGGL(small_lists_kernel, dim3(1), dim3(kThreads), 0, s, offsets, active, l1, l4);
+      hipLaunchKernelGGL(small_lists_kernel, dim3(1), dim3(kThreads), 0, s, offsets, active, l1, l4, reg_max);
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
   }
@@ -749,11 +752,10 @@ hipError_t launch_expert_ffn(const uint16_t* x, int T, int k, const moe_mxfp4_we
       const GemvGrid gg = multi_grid(iters);
       gateup_reg<1>(ga, sg, gg, multi(n1_max, gg), l1, 1, 1);
       if ((err = hipGetLastError()) != hipSuccess) return err;
-      gateup_reg<kRegRows>(ga, sg, gg, multi(n4_max, gg), l4, 2, kRegRows);
+      if (reg_max > 1) gateup_reg<kRegRows>(ga, sg, gg, multi(n4_max, gg), l4, 2, kRegRows);
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  const bool use_mfma = T > 1 && reg_g && reg_d && mfma_shape_ok(H, I);
   uint8_t* mfma_ws = (uint8_t*)ws + off;
   if (use_mfma) {
     if ((err = launch_mfma_gateup(x, T, k, w, offsets, sorted_rows, active, hbuf, mfma_ws, s)) != hipSuccess)
@@ -784,7 +786,7 @@ hipError_t launch_expert_ffn(const uint16_t* x, int T, int k, const moe_mxfp4_we
       const GemvGrid gd = multi_grid(iters);
       down_reg<1>(ga, sd, gd, multi(n1_max, gd), l1, 1, 1);
       if ((err = hipGetLastError()) != hipSuccess) return err;
-      down_reg<kRegRows>(ga, sd, gd, multi(n4_max, gd), l4, 2, kRegRows);
+      if (reg_max > 1) down_reg<kRegRows>(ga, sd, gd, multi(n4_max, gd), l4, 2, kRegRows);
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }

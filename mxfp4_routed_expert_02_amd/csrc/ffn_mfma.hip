@@ -1,6 +1,6 @@
 // ffn_mfma.hip - expert-major grouped GEMM of the expert FFN on the CDNA4
 // scaled MFMA (v_mfma_scale_f32_32x32x64_f8f6f4), for experts whose routed
-// rows make the product a dense contraction (more than kRegRows rows).
+// rows make the product a dense contraction (more than reg_rows_max(T) rows).
 //
 // A operand = the expert's MXFP4 weights exactly as stored (E2M1 codes with
 // their own E8M0 scale per 32 values); B operand = the activations split in
@@ -158,15 +158,15 @@ __device__ __forceinline__ void quantize_block(const void* src, int row, int row
 
 // x [T][H] bf16 -> two E4M3 terms; block 0 also writes the tile plan: one
 // (slot, token tile) pair per token tile of every active expert with more
-// than kRegRows rows, and the pair count in plan[0].
+// than reg_max rows, and the pair count in plan[0].
 __global__ __launch_bounds__(kThreads) void mfma_prep_kernel(const uint16_t* __restrict__ x, int T, int H,
                                                             const int32_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ active,
                                                             uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
-                                                            int32_t* __restrict__ plan) {
+                                                            int32_t* __restrict__ plan, int reg_max) {
   if (blockIdx.x == 0) {
     // Tile plan: the (slot, token tile) pairs of experts with more than
-    // kRegRows rows, heaviest first: tiles with 4 token groups (65..128
+    // reg_max rows, heaviest first: tiles with 4 token groups (65..128
     // rows), then 2 (33..64), then 1 (5..32).  The GEMM deals pair g to XCD
     // g % 8, so every XCD gets a near-equal share of each class and starts
     // with its heaviest tiles.  Within a class pairs keep slot order, so
@@ -180,7 +180,7 @@ __global__ __launch_bounds__(kThreads) void mfma_prep_kernel(const uint16_t* __r
       if (a >= na) return;
       const int e = active[1 + a];
       const int cnt = offsets[e + 1] - offsets[e];
-      if (cnt <= kRegRows) return;
+      if (cnt <= reg_max) return;
       const int nt = (cnt + kTileTok - 1) / kTileTok;
       const int last = cnt - (nt - 1) * kTileTok;
       c[0] = nt - 1 + (last > 64);
@@ -260,37 +260,44 @@ __global__ __launch_bounds__(kThreads) void quantize_h_kernel(const float* __res
 
 // ------------------------------------------------------------------ GEMM --
 
-// LDS ring.  A slot holds one 128-value K stage of every operand of the tile,
-// written straight from global memory by LDS DMA loads (a wave's load puts
-// lane l's 16 or 4 bytes at the slot offset + size * l):
+// LDS ring.  A slot holds one 128-value K stage of the tile's weight codes
+// and activations, written straight from global memory by LDS DMA loads (a
+// wave's load puts lane l's 16 or 4 bytes at the slot offset + size * l):
 //   A   [256 rows][64 B]    weight codes; 16-byte piece p of row r at
 //                           r*64 + 16*(p ^ ((r >> 2) & 3))
-//   AS  [256 rows][4 B]     the rows' four scale bytes of the stage, as stored
 //   B   [2][32*TG][128 B]   activation terms; piece p of (term u, token t) at
 //                           (u*32*TG + t)*128 + 16*(p ^ ((t >> 1) & 7))
 //   BS  [2][32*TG][4 B]     their four scale bytes of the stage
 // The XOR swizzles give the 16 lanes that read one K offset of 16
 // consecutive rows or tokens 16 distinct 16-byte bank groups.  A tile with
-// TG token groups of 32 has slots of 25.3, 33.5 or 50 KB and a ring of 6, 4
-// or 3 of them, so 5, 3 or 2 stages (126, 100, 100 KB) are in flight per CU
-// while one is read.
+// TG token groups of 32 has slots of 24.3, 32.5 or 49 KB and a ring of 5, 4
+// or 3 of them, so 4, 3 or 2 stages are in flight per CU while one is read.
+// The weight scales travel in blocks of four stages (16 bytes per row, one
+// memory request per row instead of four) through kScaleBufs buffers of
+// [256 rows][16 B] after the ring; each stage's loads carry a quarter of
+// the next block.
 constexpr int kLdsBytes = 160 * 1024;
+constexpr int kScaleBuf = kTileRows * 16;
 
 template <int TG>
 struct Ring {
   static constexpr int kTok = 32 * TG;
   static constexpr int kA = kTileRows * 64;
-  static constexpr int kAS = kTileRows * 4;
   static constexpr int kB = 2 * kTok * 128;
   static constexpr int kBS = 2 * kTok * 4;
-  static constexpr int kStage = kA + kAS + kB + kBS;
-  static constexpr int kSlots = kLdsBytes / kStage;
+  static constexpr int kStage = kA + kB + kBS;
+  static constexpr int kSlots = TG == 1 ? 5 : TG == 2 ? 4 : 3;
+  // a scale block is refilled only after the barrier that follows its last
+  // reader: 4 * kScaleBufs >= kSlots + 7
+  static constexpr int kScaleBufs = (kSlots + 7 + 3) / 4;
+  static constexpr int kScaleBase = kSlots * kStage;
+  static constexpr int kBytes = kScaleBase + kScaleBufs * kScaleBuf;
   static constexpr int kOps = 4 + 1 + 2 * TG + 1;  // DMA loads per wave per stage
   static_assert(kStage % 16 == 0, "16-byte aligned slots");
+  static_assert(kBytes <= kLdsBytes, "ring fits in LDS");
 };
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
-constexpr int kRingBytes = cmax(cmax(Ring<1>::kSlots * Ring<1>::kStage, Ring<2>::kSlots * Ring<2>::kStage),
-                                Ring<4>::kSlots * Ring<4>::kStage);
+constexpr int kRingBytes = cmax(cmax(Ring<1>::kBytes, Ring<2>::kBytes), Ring<4>::kBytes);
 
 // LDS DMA loads of 16 and 4 bytes per lane to the wave-uniform LDS address
 // `lds` (lane l at lds + size*l).  Issued from asm, so the compiler neither
@@ -422,7 +429,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const uint8_t* asrc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) asrc[i] = a_row(16 * (4 * i + wave) + (lane >> 2)) + 16 * apiece;
-    const uint8_t* assrc = a_srow(64 * wave + lane);
+    // AS: quarter q of a scale block = rows 64q + 16w + lane/4, word lane%4
+    const uint8_t* assrc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) assrc[q] = a_srow(64 * q + 16 * wave + (lane >> 2)) + 4 * (lane & 3);
+    const int nblk = nst >> 2;  // scale blocks per row
     const uint8_t* bsrc[2 * TG];
 #pragma unroll
     for (int j = 0; j < 2 * TG; ++j) {
@@ -434,15 +445,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const uint8_t* bssrc = bs + (b_row(be % G::kTok) * 2 + be / G::kTok) * 4;
     const int64_t bq_stage = (int64_t)brows * 256, bs_stage = (int64_t)brows * 8;
 
-    // load o (0 .. kOps-1) of this wave's share of stage st into slot sl
+    // quarter q of weight-scale block b (clamped to the last block) into its buffer
+    auto issue_scales = [&](int b, int q) {
+      const uint8_t* src = q == 0 ? assrc[0] : q == 1 ? assrc[1] : q == 2 ? assrc[2] : assrc[3];
+      const uint32_t dst = lds0 + (uint32_t)(G::kScaleBase + (b % G::kScaleBufs) * kScaleBuf + (64 * q + 16 * wave) * 16);
+      lds_dma4(src + 16 * min(b, nblk - 1), dst);
+    };
+    // load o (0 .. kOps-1) of this wave's share of stage st into slot sl;
+    // load 4 is quarter st % 4 of the scale block after st's
     auto issue_op = [&](int st, int sl, auto o_c) {
       constexpr int o = decltype(o_c)::value;
       const uint32_t sb = lds0 + (uint32_t)(sl * G::kStage);
       if constexpr (o < 4) lds_dma16(asrc[o] + st * 64, sb + (4 * o + wave) * 1024);
-      else if constexpr (o == 4) lds_dma4(assrc + st * 4, sb + G::kA + wave * 256);
+      else if constexpr (o == 4) issue_scales((st >> 2) + 1, st & 3);
       else if constexpr (o < 5 + 2 * TG)
-        lds_dma16(bsrc[o - 5] + st * bq_stage, sb + G::kA + G::kAS + (wave + 4 * (o - 5)) * 1024);
-      else lds_dma4(bssrc + st * bs_stage, sb + G::kA + G::kAS + G::kB + tgi * 256);
+        lds_dma16(bsrc[o - 5] + st * bq_stage, sb + G::kA + (wave + 4 * (o - 5)) * 1024);
+      else lds_dma4(bssrc + st * bs_stage, sb + G::kA + G::kB + tgi * 256);
     };
     auto issue = [&](int st, int sl) { static_for<0, G::kOps>([&](auto o) { issue_op(st, sl, o); }); };
 
@@ -451,14 +469,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int tt = 32 * tgi + n;
     const uint32_t a_off[2] = {(uint32_t)((32 * rb_base + n) * 64 + 16 * ((0 + half) ^ ((n >> 2) & 3))),
                                (uint32_t)((32 * rb_base + n) * 64 + 16 * ((2 + half) ^ ((n >> 2) & 3)))};
-    const uint32_t as_off = (uint32_t)(G::kA + (32 * rb_base + n) * 4);
+    const uint32_t as_off = (uint32_t)((32 * rb_base + n) * 16);  // within a scale buffer
     uint32_t b_off[2][2];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        b_off[s][i] = (uint32_t)(G::kA + G::kAS + tt * 128 + 16 * ((4 * s + 2 * half + i) ^ ((n >> 1) & 7)));
-    const uint32_t bs_off = (uint32_t)(G::kA + G::kAS + G::kB + tt * 4);
+        b_off[s][i] = (uint32_t)(G::kA + tt * 128 + 16 * ((4 * s + 2 * half + i) ^ ((n >> 1) & 7)));
+    const uint32_t bs_off = (uint32_t)(G::kA + G::kB + tt * 4);
 
     auto read_a = [&](int sl, int s, uint4 (&a)[RBW]) {
       const uint8_t* base = s_ring + sl * G::kStage + a_off[s];
@@ -471,11 +489,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
         for (int i = 0; i < 2; ++i) b[u][i] = *(const uint4*)(s_ring + sl * G::kStage + b_off[s][i] + u * G::kTok * 128);
     };
-    // the stage's scale words, shifted so that step s's byte is byte 2s
-    auto read_sc = [&](int sl, uint32_t (&sa)[RBW], uint32_t (&sb)[2]) {
+    // weight-scale words of stage st in LDS
+    auto sa_base = [&](int st) -> const uint8_t* {
+      return s_ring + G::kScaleBase + ((st >> 2) % G::kScaleBufs) * kScaleBuf + as_off + 4 * (st & 3);
+    };
+    // stage st's scale words (in slot sl), shifted so that step s's byte is byte 2s
+    auto read_sc = [&](int st, int sl, uint32_t (&sa)[RBW], uint32_t (&sb)[2]) {
+      const uint8_t* ab = sa_base(st);
 #pragma unroll
-      for (int j = 0; j < RBW; ++j)
-        sa[j] = *(const uint32_t*)(s_ring + sl * G::kStage + as_off + 32 * rel(j) * 4) >> (8 * half);
+      for (int j = 0; j < RBW; ++j) sa[j] = *(const uint32_t*)(ab + 32 * rel(j) * 16) >> (8 * half);
 #pragma unroll
       for (int u = 0; u < 2; ++u)
         sb[u] = *(const uint32_t*)(s_ring + sl * G::kStage + bs_off + u * G::kTok * 4) >> (8 * half);
@@ -511,6 +533,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // and scales, run step 1.  The steady-state loop (a stage R ahead left
     // to load) is one basic block, so the step-0 MFMAs stay ahead of the
     // wait and keep the pipe busy through it; the last R stages drain.
+    // scale block 0, then stages 0 .. R-1 (each with a quarter of block 1, 2, ...)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) issue_scales(0, q);
 #pragma unroll
     for (int j = 0; j < R; ++j)
       if (j < nst) issue(j, j);
@@ -518,7 +543,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     __syncthreads();
     uint4 a0[RBW], b0[2][2];
     uint32_t sa[RBW], sb[2];
-    read_sc(0, sa, sb);
+    read_sc(0, 0, sa, sb);
     read_a(0, 0, a0);
     read_b(0, 0, b0);
     int st = 0, sl = 0;
@@ -568,6 +593,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       const v8i_t C0 = pack_b(b1[0][0], b1[0][1]), C1 = pack_b(b1[1][0], b1[1][1]);
       const uint8_t* an_base = s_ring + nsl * G::kStage + a_off[0];
       const uint8_t* sn_base = s_ring + nsl * G::kStage;
+      const uint8_t* san_base = sa_base(st + 1);
       static_for<0, RBW>([&](auto j_c) {
         constexpr int j = decltype(j_c)::value;
         mma_j(std::integral_constant<int, 1>(), j_c, a1[j], C0, C1, sa1[j], sb1);
@@ -579,7 +605,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             b0[(r - RBW) / 2][(r - RBW) % 2] =
                 *(const uint4*)(sn_base + b_off[0][(r - RBW) % 2] + ((r - RBW) / 2) * G::kTok * 128);
           else if constexpr (r < 2 * RBW + 4)
-            sa[r - RBW - 4] = *(const uint32_t*)(sn_base + as_off + 32 * rel(r - RBW - 4) * 4) >> (8 * half);
+            sa[r - RBW - 4] = *(const uint32_t*)(san_base + 32 * rel(r - RBW - 4) * 16) >> (8 * half);
           else
             sb[r - 2 * RBW - 4] = *(const uint32_t*)(sn_base + bs_off + (r - 2 * RBW - 4) * G::kTok * 4) >> (8 * half);
         });
@@ -602,7 +628,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       if (st + 1 < nst) {
         wait_stages<G::kOps>(nst - 2 - st);
         __syncthreads();
-        read_sc(nsl, sa, sb);
+        read_sc(st + 1, nsl, sa, sb);
         read_a(nsl, 0, a0);
         read_b(nsl, 0, b0);
       }
@@ -653,9 +679,10 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 namespace moe {
 
 // Whole row tiles (gate/up: I/128 tiles of 128 gate + 128 up rows; down:
-// H/256 tiles); K of both products is then a whole number of stages
+// H/256 tiles) and K of both products a whole number of weight-scale blocks
+// (four 128-value stages)
 bool mfma_shape_ok(int H, int I) {
-  return H % kTileRows == 0 && I % (kTileRows / 2) == 0;
+  return H % kTileRows == 0 && I % (kTileRows / 2) == 0 && H % 512 == 0 && I % 512 == 0;
 }
 
 // Workspace of the MFMA path after the h buffer: x terms, x scales, h terms,
@@ -663,7 +690,8 @@ bool mfma_shape_ok(int H, int I) {
 size_t mfma_workspace(int T, int k, int E, int H, int I) {
   const size_t R = (size_t)T * k;
   const size_t mx = (size_t)(R < (size_t)E ? R : E);
-  const size_t pairs = R / kTileTok + (mx < R / (kRegRows + 1) ? mx : R / (kRegRows + 1)) + 1;
+  const size_t per = (size_t)reg_rows_max(T) + 1;  // fewest rows of a GEMM expert
+  const size_t pairs = R / kTileTok + (mx < R / per ? mx : R / per) + 1;
   return align256((size_t)T * 2 * H) + align256((size_t)T * 2 * (H / 32)) + align256(R * 2 * I) +
          align256(R * 2 * (I / 32)) + align256((1 + 2 * pairs) * sizeof(int32_t));
 }
@@ -671,10 +699,11 @@ size_t mfma_workspace(int T, int k, int E, int H, int I) {
 size_t mfma_max_pairs(int T, int k, int E) {
   const size_t R = (size_t)T * k;
   const size_t mx = (size_t)(R < (size_t)E ? R : E);
-  return R / kTileTok + (mx < R / (kRegRows + 1) ? mx : R / (kRegRows + 1)) + 1;
+  const size_t per = (size_t)reg_rows_max(T) + 1;
+  return R / kTileTok + (mx < R / per ? mx : R / per) + 1;
 }
 
-// Launches prep, gate/up GEMM (h for experts with more than kRegRows rows).
+// Launches prep, gate/up GEMM (h for experts with more than reg_rows_max(T) rows).
 hipError_t launch_mfma_gateup(const uint16_t* x, int T, int k, const moe_mxfp4_weights& w, const int32_t* offsets,
                               const int32_t* sorted_rows, const int32_t* active, float* h, uint8_t* ws,
                               hipStream_t s) {
@@ -689,7 +718,7 @@ hipError_t launch_mfma_gateup(const uint16_t* x, int T, int k, const moe_mxfp4_w
   (void)hs;
   const int64_t nq = (int64_t)T * (H / 32);
   hipLaunchKernelGGL(mfma_prep_kernel, dim3(1 + (unsigned)((nq + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
-                     x, T, H, offsets, active, xq, xs, plan);
+                     x, T, H, offsets, active, xq, xs, plan, reg_rows_max(T));
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int m_tiles = I / (kTileRows / 2);

@@ -37,6 +37,7 @@ bool weights_ok(const moe_mxfp4_weights* w) {
   if (!w) return false;
   if (!w->gate_q || !w->gate_s || !w->up_q || !w->up_s || !w->down_q || !w->down_s) return false;
   if (!aligned16(w->gate_q) || !aligned16(w->up_q) || !aligned16(w->down_q)) return false;
+  if (((uintptr_t)w->gate_s & 3) || ((uintptr_t)w->up_s & 3) || ((uintptr_t)w->down_s & 3)) return false;
   if (w->expert_stride <= 0 || (w->expert_stride & 15) != 0) return false;
   if (w->num_experts < 1 || w->num_experts > MOE_MAX_EXPERTS) return false;
   if (w->hidden < 32 || w->hidden > MOE_MAX_DIM || (w->hidden & 31) != 0) return false;
