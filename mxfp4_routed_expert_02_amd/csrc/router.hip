@@ -7,10 +7,8 @@
 //
 // Few tokens (decode, T <= 4): the projection streams Wr once (25.7 MB at
 // 896 x 7168), so it is a GEMV, one block per expert row.
-// More tokens: a tiled fp32 GEMM, 32 tokens x 64 experts per block of 256
-// threads, K tiles of 32 in LDS (x converted to fp32 as it is staged), each
-// thread 2 tokens x 4 experts; every output is one thread's sum over K in
-// ascending order.
+// More tokens: a GEMM on the bf16 MFMA with the weights split exactly in
+// three bf16 terms (below).
 #include "moe_internal.h"
 
 namespace {
@@ -78,68 +76,163 @@ __global__ __launch_bounds__(kThreads) void router_gemv_kernel(const uint16_t* _
   }
 }
 
-constexpr int kTileT = 32, kTileE = 64, kTileK = 32;
+// More tokens: a GEMM on the bf16 MFMA (v_mfma_f32_32x32x16_bf16).  x is
+// bf16 already; each fp32 weight w splits exactly into three bf16 terms
+// (w1 = w with its low 16 bits cleared, w2 the same of w - w1, w3 = the
+// remainder, at most 8 significant bits), so every product x * w_i is exact
+// in fp32 and the MFMA accumulates sum_c x[c] * (w1 + w2 + w3)[c] in fp32,
+// three bf16 MFMAs per 16-deep step (a third of the bf16 rate, five times
+// the fp32 MFMA's).  Tile: 64 experts x 64 tokens per block of 4 waves,
+// each wave one 32 x 32 output block (the weights are split once per token
+// tile, so wider token tiles split less); K stages of 64 values in LDS as
+// three weight planes and one x plane of [64][64] bf16, double-buffered,
+// the 16-byte piece p of row r at
+// r*128 + 16*(p ^ ((r >> 1) & 7)) so that the fragment reads of 16
+// consecutive rows hit distinct bank groups.  Global loads run two stages
+// ahead through two register sets.  Blocks of one expert tile run on one
+// XCD, which then reads that tile of Wr once.
+constexpr int kRe = 64, kRtok = 64;  // experts and tokens per block
+constexpr int kRk = 64;              // K values per stage
+constexpr int kRthreads = 256;
+constexpr int kWPlane = kRe * kRk * 2, kXPlane = kRtok * kRk * 2;  // bytes
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float v16f_t __attribute__((ext_vector_type(16)));
 
-__global__ __launch_bounds__(kThreads) void router_gemm_kernel(const uint16_t* __restrict__ x, int H,
-                                                               const float* __restrict__ wr, int E,
-                                                               float* __restrict__ logits, int T) {
-  __shared__ float s_x[kTileK][kTileT];  // k-major
-  __shared__ float s_w[kTileK][kTileE];
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  const int t0 = blockIdx.y * kTileT, e0 = blockIdx.x * kTileE;
-  float acc[2][4] = {};
-  // staging: the x tile (32 tokens x 32 k) as one uint2 of 4 bf16 per thread
-  // (token tid/8, k 4*(tid%8)); the w tile (64 experts x 32 k) as two float4
-  // per thread; both stored k-major
-  for (int k0 = 0; k0 < H; k0 += kTileK) {
-    {
-      const int t = tid >> 3, kk = 4 * (tid & 7);
-      float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      if (t0 + t < T) {
-        const uint2 b = *(const uint2*)(x + (int64_t)(t0 + t) * H + k0 + kk);
-        v = make_float4(bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y));
-      }
-      s_x[kk + 0][t] = v.x;
-      s_x[kk + 1][t] = v.y;
-      s_x[kk + 2][t] = v.z;
-      s_x[kk + 3][t] = v.w;
+__device__ __forceinline__ int swz(int r, int p) { return r * 128 + 16 * (p ^ ((r >> 1) & 7)); }
+
+struct RouterStage {
+  float4 w[4];  // 16 weights of one expert row
+  uint4 x[2];   // 16 bf16 of one token row
+};
+
+// high halves of two fp32 bit patterns packed as two bf16 (a low, b high)
+__device__ __forceinline__ uint32_t hi_pair(float a, float b) {
+  return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
+__device__ __forceinline__ float lo_rest(float v) {  // v minus v with its low 16 bits cleared (exact)
+  return v - __uint_as_float(__float_as_uint(v) & 0xFFFF0000u);
+}
+
+__global__ __launch_bounds__(kRthreads) void router_mfma_kernel(const uint16_t* __restrict__ x, int H,
+                                                                const float* __restrict__ wr, int E,
+                                                                float* __restrict__ logits, int T, int n_t) {
+  // [buffer]: w1, w2, w3 planes then the x plane
+  __shared__ __attribute__((aligned(16))) uint8_t s_buf[2][3 * kWPlane + kXPlane];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // XCD x = blockIdx % 8 takes expert tiles x, x + 8, ...; within one, all token tiles
+  const int bx = blockIdx.x, slot = bx >> 3;
+  const int et = (bx & 7) + 8 * (slot / n_t), ttile = slot - (slot / n_t) * n_t;
+  const int e0 = et * kRe, t0 = ttile * kRtok;
+  if (e0 >= E) return;
+
+  // staging: thread t takes expert row t/4 and token row t/4, K values
+  // 16 (t%4) .. +15 of the stage
+  const int wrow = tid >> 2, wk = 16 * (tid & 3), xrow = tid >> 2, xk = 16 * (tid & 3);
+  // rows past E or T read row 0 (their outputs are never stored); K past H
+  // reads in range and is zeroed, so every load is unconditional
+  const float* wsrc = wr + (int64_t)(e0 + wrow < E ? e0 + wrow : 0) * H;
+  const uint16_t* xsrc = x + (int64_t)(t0 + xrow < T ? t0 + xrow : 0) * H;
+  auto load = [&](int k0, RouterStage& r) {
+    // H % 32 == 0: a 16-value segment is all in or all out
+    const bool win = k0 + wk < H, xin = k0 + xk < H;
+    const int kw = win ? k0 + wk : 0, kx = xin ? k0 + xk : 0;
+    const uint32_t mw = win ? ~0u : 0u, mx = xin ? ~0u : 0u;  // bit masks, not branches
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = *(const uint4*)(wsrc + kw + 4 * i);
+      r.w[i] = make_float4(__uint_as_float(v.x & mw), __uint_as_float(v.y & mw), __uint_as_float(v.z & mw),
+                           __uint_as_float(v.w & mw));
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int i = tid + kThreads * h;  // 512 float4 = 64 experts x 8 float4
-      const int ee = i >> 3, kk = 4 * (i & 7);
-      float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      if (e0 + ee < E) v = *(const float4*)(wr + (int64_t)(e0 + ee) * H + k0 + kk);
-      s_w[kk + 0][ee] = v.x;
-      s_w[kk + 1][ee] = v.y;
-      s_w[kk + 2][ee] = v.z;
-      s_w[kk + 3][ee] = v.w;
+    for (int i = 0; i < 2; ++i) {
+      const uint4 v = *(const uint4*)(xsrc + kx + 8 * i);
+      r.x[i] = make_uint4(v.x & mx, v.y & mx, v.z & mx, v.w & mx);
     }
+  };
+  auto store = [&](int b, const RouterStage& r) {
+#pragma unroll
+    for (int pc = 0; pc < 2; ++pc) {  // 8 weights per 16-byte piece
+      const float f[8] = {r.w[2 * pc].x, r.w[2 * pc].y, r.w[2 * pc].z, r.w[2 * pc].w,
+                          r.w[2 * pc + 1].x, r.w[2 * pc + 1].y, r.w[2 * pc + 1].z, r.w[2 * pc + 1].w};
+      uint32_t t1[4], t2[4], t3[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = f[2 * i], c = f[2 * i + 1];
+        const float ra = lo_rest(a), rc = lo_rest(c);      // w - w1
+        const float qa = lo_rest(ra), qc = lo_rest(rc);    // w - w1 - w2 = w3
+        t1[i] = hi_pair(a, c);
+        t2[i] = hi_pair(ra, rc);
+        t3[i] = hi_pair(qa, qc);
+      }
+      const int o = swz(wrow, (wk >> 3) + pc);
+      *(uint4*)&s_buf[b][o] = make_uint4(t1[0], t1[1], t1[2], t1[3]);
+      *(uint4*)&s_buf[b][kWPlane + o] = make_uint4(t2[0], t2[1], t2[2], t2[3]);
+      *(uint4*)&s_buf[b][2 * kWPlane + o] = make_uint4(t3[0], t3[1], t3[2], t3[3]);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) *(uint4*)&s_buf[b][3 * kWPlane + swz(xrow, (xk >> 3) + h)] = r.x[h];
+  };
+
+  // wave's output block: experts 32 (wave & 1) .., tokens 32 (wave >> 1) ..
+  const int n = lane & 31, kh = lane >> 5;
+  const int arow = 32 * (wave & 1) + n, brow = 32 * (wave >> 1) + n;
+  v16f_t acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  auto compute = [&](int b) {
+#pragma unroll
+    for (int s = 0; s < kRk / 16; ++s) {
+      const int p = 2 * s + kh;  // lane's 8 K values: 16 s + 8 kh
+      const bf16x8_t xb = *(const bf16x8_t*)&s_buf[b][3 * kWPlane + swz(brow, p)];
+#pragma unroll
+      for (int term = 0; term < 3; ++term) {
+        const bf16x8_t wa = *(const bf16x8_t*)&s_buf[b][term * kWPlane + swz(arow, p)];
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, xb, acc, 0, 0, 0);
+      }
+    }
+  };
+
+  // stage st in LDS buffer st % 2; its global loads were issued two stages
+  // earlier into register set st % 2.  The main loop (a stage three ahead
+  // still to load) has no conditions, so its body schedules as one block;
+  // the last (at most three) stages follow.
+  const int nst = (H + kRk - 1) / kRk;
+  RouterStage r0, r1;
+  load(0, r0);
+  if (nst > 1) load(kRk, r1);
+  store(0, r0);
+  __syncthreads();
+  int st = 0;
+  for (; st + 3 < nst; st += 2) {
+    load((st + 2) * kRk, r0);
+    compute(0);
+    store(1, r1);
     __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < kTileK; ++kk) {
-      const float2 xv = *(const float2*)&s_x[kk][2 * ty];
-      const float4 wv = *(const float4*)&s_w[kk][4 * tx];
-      acc[0][0] += xv.x * wv.x;
-      acc[0][1] += xv.x * wv.y;
-      acc[0][2] += xv.x * wv.z;
-      acc[0][3] += xv.x * wv.w;
-      acc[1][0] += xv.y * wv.x;
-      acc[1][1] += xv.y * wv.y;
-      acc[1][2] += xv.y * wv.z;
-      acc[1][3] += xv.y * wv.w;
-    }
+    load((st + 3) * kRk, r1);
+    compute(1);
+    store(0, r0);
     __syncthreads();
   }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int t = t0 + 2 * ty + i;
-    if (t >= T) continue;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + 4 * tx + j;
-      if (e < E) logits[(int64_t)t * E + e] = acc[i][j];
+  // buffer 0 holds stage st, r1 stage st + 1 (if they exist)
+  if (st + 2 < nst) load((st + 2) * kRk, r0);
+  compute(0);
+  if (st + 1 < nst) {
+    store(1, r1);
+    __syncthreads();
+    compute(1);
+    if (st + 2 < nst) {
+      store(0, r0);
+      __syncthreads();
+      compute(0);
     }
+  }
+  // D lane l, register r: token l % 32 of the wave's block, expert 8 (r/4) + 4 (l/32) + r%4
+  const int t = t0 + 32 * (wave >> 1) + n;
+  if (t >= T) return;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int e = e0 + 32 * (wave & 1) + 8 * (r >> 2) + 4 * kh + (r & 3);
+    if (e < E) logits[(int64_t)t * E + e] = acc[r];
   }
 }
 
@@ -157,8 +250,9 @@ hipError_t launch_router_logits(const uint16_t* x, int T, int H, const float* wr
     else
       hipLaunchKernelGGL(router_gemv_kernel<kGemvTokens>, g, b, 0, s, x, H, wr, E, logits, T);
   } else {
-    const dim3 g((E + kTileE - 1) / kTileE, (T + kTileT - 1) / kTileT), b(kThreads);
-    hipLaunchKernelGGL(router_gemm_kernel, g, b, 0, s, x, H, wr, E, logits, T);
+    const int n_e = (E + kRe - 1) / kRe, n_t = (T + kRtok - 1) / kRtok;
+    const dim3 g((unsigned)(8 * ((n_e + 7) / 8) * n_t)), b(kRthreads);
+    hipLaunchKernelGGL(router_mfma_kernel, g, b, 0, s, x, H, wr, E, logits, T, n_t);
   }
   return hipGetLastError();
 }

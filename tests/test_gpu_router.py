@@ -19,6 +19,7 @@ pytestmark = pytest.mark.gpu
 CASES = [  # E, H, T: GEMV (T <= 4) and tiled paths, ragged tiles, the ranges' ends
     (8, 256, 4), (896, 7168, 1), (896, 7168, 3), (896, 7168, 8), (896, 7168, 512), (100, 96, 37),
     (4096, 32, 5), (64, 16384, 2), (64, 16384, 5), (1, 32, 1), (896, 7168, 0), (896, 7168, 4), (33, 224, 2),
+    (130, 128, 65),
 ]
 
 
