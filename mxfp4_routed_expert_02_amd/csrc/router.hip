@@ -82,9 +82,11 @@ __global__ __launch_bounds__(kThreads) void router_gemv_kernel(const uint16_t* _
 // remainder, at most 8 significant bits), so every product x * w_i is exact
 // in fp32 and the MFMA accumulates sum_c x[c] * (w1 + w2 + w3)[c] in fp32,
 // three bf16 MFMAs per 16-deep step (a third of the bf16 rate, five times
-// the fp32 MFMA's).  Tile: 64 experts x 64 tokens per block of 4 waves,
-// each wave one 32 x 32 output block (the weights are split once per token
-// tile, so wider token tiles split less); K stages of 64 values in LDS as
+// the fp32 MFMA's).  Tile: 64 experts x 64 tokens per block of 8 waves:
+// waves 0-3 take the first half of K and waves 4-7 the second, each wave
+// one 32 x 32 output block of its half, and the halves' sums meet in LDS
+// at the end, first half plus second half (the weights are split once per
+// token tile, so wider token tiles split less); K stages of 64 values in LDS as
 // three weight planes and one x plane of [64][64] bf16, double-buffered,
 // the 16-byte piece p of row r at
 // r*128 + 16*(p ^ ((r >> 1) & 7)) so that the fragment reads of 16
@@ -93,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void router_gemv_kernel(const uint16_t* _
 // XCD, which then reads that tile of Wr once.
 constexpr int kRe = 64, kRtok = 64;  // experts and tokens per block
 constexpr int kRk = 64;              // K values per stage
-constexpr int kRthreads = 256;
+constexpr int kRthreads = 512;  // two halves of 4 waves
 constexpr int kWPlane = kRe * kRk * 2, kXPlane = kRtok * kRk * 2;  // bytes
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float v16f_t __attribute__((ext_vector_type(16)));
@@ -116,9 +118,11 @@ __device__ __forceinline__ float lo_rest(float v) {  // v minus v with its low 1
 __global__ __launch_bounds__(kRthreads) void router_mfma_kernel(const uint16_t* __restrict__ x, int H,
                                                                 const float* __restrict__ wr, int E,
                                                                 float* __restrict__ logits, int T, int n_t) {
-  // [buffer]: w1, w2, w3 planes then the x plane
-  __shared__ __attribute__((aligned(16))) uint8_t s_buf[2][3 * kWPlane + kXPlane];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // [K half][buffer]: w1, w2, w3 planes then the x plane
+  __shared__ __attribute__((aligned(16))) uint8_t s_all[2][2][3 * kWPlane + kXPlane];
+  const int khalf = threadIdx.x >> 8;
+  uint8_t(&s_buf)[2][3 * kWPlane + kXPlane] = s_all[khalf];
+  const int tid = threadIdx.x & 255, lane = tid & 63, wave = tid >> 6;
   // XCD x = blockIdx % 8 takes expert tiles x, x + 8, ...; within one, all token tiles
   const int bx = blockIdx.x, slot = bx >> 3;
   const int et = (bx & 7) + 8 * (slot / n_t), ttile = slot - (slot / n_t) * n_t;
@@ -130,12 +134,17 @@ __global__ __launch_bounds__(kRthreads) void router_mfma_kernel(const uint16_t* 
   const int wrow = tid >> 2, wk = 16 * (tid & 3), xrow = tid >> 2, xk = 16 * (tid & 3);
   // rows past E or T read row 0 (their outputs are never stored); K past H
   // reads in range and is zeroed, so every load is unconditional
+  // this half's stages: nst of 64 K values from kbase (both halves run the
+  // same number, so their barriers pair up; the second half's last may lie
+  // past H and loads zeros)
+  const int nst = ((H + kRk - 1) / kRk + 1) / 2;
+  const int kbase = khalf * nst * kRk;
   const float* wsrc = wr + (int64_t)(e0 + wrow < E ? e0 + wrow : 0) * H;
   const uint16_t* xsrc = x + (int64_t)(t0 + xrow < T ? t0 + xrow : 0) * H;
   auto load = [&](int k0, RouterStage& r) {
     // H % 32 == 0: a 16-value segment is all in or all out
-    const bool win = k0 + wk < H, xin = k0 + xk < H;
-    const int kw = win ? k0 + wk : 0, kx = xin ? k0 + xk : 0;
+    const bool win = kbase + k0 + wk < H, xin = kbase + k0 + xk < H;
+    const int kw = win ? kbase + k0 + wk : 0, kx = xin ? kbase + k0 + xk : 0;
     const uint32_t mw = win ? ~0u : 0u, mx = xin ? ~0u : 0u;  // bit masks, not branches
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -192,11 +201,10 @@ __global__ __launch_bounds__(kRthreads) void router_mfma_kernel(const uint16_t* 
     }
   };
 
-  // stage st in LDS buffer st % 2; its global loads were issued two stages
-  // earlier into register set st % 2.  The main loop (a stage three ahead
-  // still to load) has no conditions, so its body schedules as one block;
-  // the last (at most three) stages follow.
-  const int nst = (H + kRk - 1) / kRk;
+  // stage st of the half in LDS buffer st % 2; its global loads were issued
+  // two stages earlier into register set st % 2.  The main loop (a stage
+  // three ahead still to load) has no conditions, so its body schedules as
+  // one block; the last (at most three) stages follow.
   RouterStage r0, r1;
   load(0, r0);
   if (nst > 1) load(kRk, r1);
@@ -226,13 +234,23 @@ __global__ __launch_bounds__(kRthreads) void router_mfma_kernel(const uint16_t* 
       compute(0);
     }
   }
-  // D lane l, register r: token l % 32 of the wave's block, expert 8 (r/4) + 4 (l/32) + r%4
+  // the second half's sums to LDS (over its buffers, now free), then the
+  // first half adds them in and stores.  D lane l, register r: token l % 32
+  // of the wave's block, expert 8 (r/4) + 4 (l/32) + r%4
+  float* s_red = (float*)&s_all[1][0][0];
+  __syncthreads();  // every wave is done reading its stages
+  if (khalf == 1) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s_red[(wave * 16 + r) * 64 + lane] = acc[r];
+  }
+  __syncthreads();
+  if (khalf == 1) return;
   const int t = t0 + 32 * (wave >> 1) + n;
   if (t >= T) return;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int e = e0 + 32 * (wave & 1) + 8 * (r >> 2) + 4 * kh + (r & 3);
-    if (e < E) logits[(int64_t)t * E + e] = acc[r];
+    if (e < E) logits[(int64_t)t * E + e] = acc[r] + s_red[(wave * 16 + r) * 64 + lane];
   }
 }
 
