@@ -322,12 +322,13 @@ def prefill_side(dev, pool, seed, reps, name):
 
 def stack_side(dev, seed, reps):
     """Batch-1 decode through the 92-layer stack (96 experts per layer, 155 GB
-    resident), RMS rescale between layers; the token step (92 x 5 calls) is
+    resident), RMS rescale between layers; the token step (92 x 3 launches:
+    fused route+group, expert FFN, fused combine+rescale) is
     captured once in a HIP graph and replayed."""
     import numpy as np
     import torch
 
-    from mxfp4_routed_expert_02_amd import ExpertPool, rms_rescale_bf16, synth
+    from mxfp4_routed_expert_02_amd import ExpertPool, synth
     from mxfp4_routed_expert_02_amd.layer import RoutedExpertLayer
 
     wl = synth.WORKLOADS["stack92"]
@@ -344,9 +345,8 @@ def stack_side(dev, seed, reps):
 
     def token():
         x = x0
-        for l in range(wl.layers):
-            layer(x, logits[l], pools[l], out)
-            x = rms_rescale_bf16(out, 1e-6, out=xbuf[l & 1])
+        for l in range(wl.layers):  # route+group, FFN, combine+rescale: 3 launches a layer
+            x = layer.step(x, logits[l], pools[l], out, xbuf[l & 1], 1e-6)
 
     token()
     torch.cuda.synchronize()

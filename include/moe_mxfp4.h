@@ -201,6 +201,36 @@ MOE_API moe_status moe_router_logits(const uint16_t* x_bf16, int32_t T, int32_t 
 MOE_API moe_status moe_rms_rescale_bf16(const float* y, int32_t T, int32_t H, float eps, uint16_t* x_next,
                                 moe_stream_t stream);
 
+/*
+ * Fused calls for callers that step one token, or one layer of a stack, at
+ * a time (batch-1 decode through the layer stack: page
+ * "hn.213312.xyz/article/49090233", technical highlights, double-buffered
+ * layer loading; each of the calls below replaces two launches).  Their
+ * outputs equal those of the calls they replace bit for bit.
+ *
+ * moe_route_group_one - moe_route_topk followed by moe_group_rows for a
+ * single token (T = 1): logits [E] fp32 in; topk_ids [k], topk_weights [k],
+ * expert_offsets [E+1], sorted_rows [k], row_pos [k], active [E+1] out, as
+ * those two calls define them.  E in 1..MOE_MAX_EXPERTS, 1 <= k <=
+ * min(E, MOE_MAX_TOPK); all pointers non-null (MOE_ERR_INVALID_ARG
+ * otherwise).  Needs no workspace.
+ */
+MOE_API moe_status moe_route_group_one(const float* logits, int32_t E, int32_t k, int32_t* topk_ids,
+                                       float* topk_weights, int32_t* expert_offsets, int32_t* sorted_rows,
+                                       int32_t* row_pos, int32_t* active, moe_stream_t stream);
+
+/*
+ * moe_combine_rms_bf16 - moe_combine followed by moe_rms_rescale_bf16 of its
+ * output: out [T][H] fp32 as moe_combine writes it and x_next [T][H] bf16 as
+ * moe_rms_rescale_bf16(out) writes it, in one launch (one block per token).
+ * Arguments as those two calls take them: H a multiple of 32 in
+ * 32..MOE_MAX_DIM, eps >= 0, y_rows and out 16-byte and x_next 8-byte
+ * aligned (MOE_ERR_INVALID_ARG otherwise).
+ */
+MOE_API moe_status moe_combine_rms_bf16(const float* y_rows, const float* topk_weights, const int32_t* row_pos,
+                                        int32_t T, int32_t k, int32_t H, float eps, float* out, uint16_t* x_next,
+                                        moe_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,6 +14,10 @@ token, MXFP4 weights, SwiGLU FFN, weighted combine):
     grp = group_rows(ids, E, workspace)
     y_rows = expert_ffn_mxfp4(x, k, pool, grp, workspace)
     out = combine(y_rows, w, grp.row_pos)
+
+One token at a time (decode, the layer stack), route_group_one replaces the
+first two calls and combine_rms_bf16 fuses the combine with the RMS rescale
+that feeds the next layer.
 """
 from ._binding import (  # noqa: F401
     LIB_PATH,
@@ -22,10 +26,12 @@ from ._binding import (  # noqa: F401
     Grouping,
     MoeWeights,
     combine,
+    combine_rms_bf16,
     expert_ffn_mxfp4,
     group_rows,
     lib,
     rms_rescale_bf16,
+    route_group_one,
     route_topk,
     router_logits,
     status_string,

@@ -52,6 +52,8 @@ def lib():
         L.moe_combine.argtypes = [_P, _P, _P, _I32, _I32, _I32, _P, _P]
         L.moe_rms_rescale_bf16.argtypes = [_P, _I32, _I32, ctypes.c_float, _P, _P]
         L.moe_router_logits.argtypes = [_P, _I32, _I32, _P, _I32, _P, _P]
+        L.moe_route_group_one.argtypes = [_P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P]
+        L.moe_combine_rms_bf16.argtypes = [_P, _P, _P, _I32, _I32, _I32, ctypes.c_float, _P, _P, _P]
         L.moe_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32, _I32]
         L.moe_workspace_bytes.restype = ctypes.c_size_t
         L.moe_status_string.argtypes = [ctypes.c_int]
@@ -188,6 +190,32 @@ def rms_rescale_bf16(y: torch.Tensor, eps: float = 1e-6, out: Optional[torch.Ten
         _dev(y, torch.float32, "y"), T, H, eps, _dev(out.view(torch.int16), torch.int16, "x_next"),
         _stream(y.device)))
     return out
+
+
+def route_group_one(logits: torch.Tensor, k: int, ids: torch.Tensor, weights: torch.Tensor,
+                    out: Grouping) -> Grouping:
+    """route_topk then group_rows for one token, in one launch; logits [1, E]."""
+    T, E = logits.shape
+    if T != 1:
+        raise ValueError("route_group_one takes one token")
+    _check("moe_route_group_one", lib().moe_route_group_one(
+        _dev(logits, torch.float32, "logits"), E, k, _dev(ids, torch.int32, "ids"),
+        _dev(weights, torch.float32, "weights"), _dev(out.expert_offsets, torch.int32, "expert_offsets"),
+        _dev(out.sorted_rows, torch.int32, "sorted_rows"), _dev(out.row_pos, torch.int32, "row_pos"),
+        _dev(out.active, torch.int32, "active"), _stream(logits.device)))
+    return out
+
+
+def combine_rms_bf16(y_rows: torch.Tensor, weights: torch.Tensor, row_pos: torch.Tensor, out: torch.Tensor,
+                     x_next: torch.Tensor, eps: float = 1e-6) -> torch.Tensor:
+    """combine into out [T, H] fp32, then x_next [T, H] bf16 = its RMS rescale, in one launch."""
+    T, k = weights.shape
+    H = y_rows.shape[1]
+    _check("moe_combine_rms_bf16", lib().moe_combine_rms_bf16(
+        _dev(y_rows, torch.float32, "y_rows"), _dev(weights, torch.float32, "weights"),
+        _dev(row_pos, torch.int32, "row_pos"), T, k, H, eps, _dev(out, torch.float32, "out"),
+        _dev(x_next.view(torch.int16), torch.int16, "x_next"), _stream(y_rows.device)))
+    return x_next
 
 
 def router_logits(x: torch.Tensor, w_router: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -95,9 +95,85 @@ __global__ __launch_bounds__(kRmsThreads) void rms_rescale_kernel(const float* _
   }
 }
 
+// combine then RMS rescale, one block of 1024 threads per token: thread c
+// of the rescale's layout forms its float4 of out with the combine's
+// arithmetic (j ascending), stores it, and goes on as rms_rescale_kernel
+// with those values in registers, so out and x_next equal the two separate
+// launches' bit for bit.
+__global__ __launch_bounds__(kRmsThreads) void combine_rms_kernel(const float* __restrict__ y_rows,
+                                                                  const float* __restrict__ w,
+                                                                  const int32_t* __restrict__ row_pos, int k, int H,
+                                                                  float eps, float* __restrict__ out,
+                                                                  uint16_t* __restrict__ x_next) {
+  __shared__ float s_part[kRmsThreads / MOE_WAVE];
+  const int t = blockIdx.x;
+  const int n4 = H >> 2;
+  const float* wt = w + (int64_t)t * k;
+  const int32_t* rp = row_pos + (int64_t)t * k;
+  float4 v[kRmsVec];
+#pragma unroll
+  for (int i = 0; i < kRmsVec; ++i) v[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int j0 = 0; j0 < k; j0 += 8) {
+#pragma unroll
+    for (int i = 0; i < kRmsVec; ++i) {
+      const int c = threadIdx.x + kRmsThreads * i;
+      if (c >= n4) continue;
+      float4 y[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (j0 + u < k) y[u] = ((const float4*)(y_rows + (int64_t)rp[j0 + u] * H))[c];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (j0 + u < k) {
+          const float cw = wt[j0 + u];
+          v[i].x += cw * y[u].x;
+          v[i].y += cw * y[u].y;
+          v[i].z += cw * y[u].z;
+          v[i].w += cw * y[u].w;
+        }
+      }
+    }
+  }
+  float4* orow = (float4*)(out + (int64_t)t * H);
+  float ss = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kRmsVec; ++i) {
+    const int c = threadIdx.x + kRmsThreads * i;
+    if (c < n4) orow[c] = v[i];
+  }
+#pragma unroll
+  for (int i = 0; i < kRmsVec; ++i) ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+  ss = wave_sum(ss);
+  if ((threadIdx.x & (MOE_WAVE - 1)) == 0) s_part[threadIdx.x / MOE_WAVE] = ss;
+  __syncthreads();
+  float tot = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kRmsThreads / MOE_WAVE; ++i) tot += s_part[i];
+  const float r = 1.0f / sqrtf(tot / (float)H + eps);
+  uint2* xo = (uint2*)(x_next + (int64_t)t * H);
+#pragma unroll
+  for (int i = 0; i < kRmsVec; ++i) {
+    const int c = threadIdx.x + kRmsThreads * i;
+    if (c < n4) {
+      const uint32_t lo = f32_to_bf16_rne_dev(v[i].x * r) | ((uint32_t)f32_to_bf16_rne_dev(v[i].y * r) << 16);
+      const uint32_t hi = f32_to_bf16_rne_dev(v[i].z * r) | ((uint32_t)f32_to_bf16_rne_dev(v[i].w * r) << 16);
+      xo[c] = make_uint2(lo, hi);
+    }
+  }
+}
+
 }  // namespace
 
 namespace moe {
+
+hipError_t launch_combine_rms(const float* y_rows, const float* w, const int32_t* row_pos, int T, int k, int H,
+                              float eps, float* out, uint16_t* x_next, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  static_assert(MOE_MAX_DIM <= 4 * kRmsVec * kRmsThreads, "one register tile per token");
+  hipLaunchKernelGGL(combine_rms_kernel, dim3(T), dim3(kRmsThreads), 0, s, y_rows, w, row_pos, k, H, eps, out,
+                     x_next);
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(const float* y_rows, const float* w, const int32_t* row_pos, int T, int k, int H,
                           float* out, hipStream_t s) {

@@ -129,6 +129,36 @@ moe_status moe_rms_rescale_bf16(const float* y, int32_t T, int32_t H, float eps,
   return from_hip(moe::launch_rms_rescale(y, T, H, eps, x_next, (hipStream_t)stream));
 }
 
+moe_status moe_route_group_one(const float* logits, int32_t E, int32_t k, int32_t* topk_ids, float* topk_weights,
+                               int32_t* expert_offsets, int32_t* sorted_rows, int32_t* row_pos, int32_t* active,
+                               moe_stream_t stream) {
+  if (!logits || !topk_ids || !topk_weights || !expert_offsets || !sorted_rows || !row_pos || !active)
+    return MOE_ERR_INVALID_ARG;
+  if (E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > MOE_MAX_TOPK || k > E) return MOE_ERR_INVALID_ARG;
+  const moe_status d = check_device();
+  if (d != MOE_OK) return d;
+  const hipStream_t s = (hipStream_t)stream;
+  if (E <= 2048)
+    return from_hip(moe::launch_route_group_one(logits, E, k, topk_ids, topk_weights, expert_offsets, sorted_rows,
+                                                row_pos, active, s));
+  hipError_t err = moe::launch_route_topk(logits, 1, E, k, topk_ids, topk_weights, s);
+  if (err == hipSuccess)  // k rows: the grouping needs no workspace
+    err = moe::launch_group_rows(topk_ids, 1, k, E, expert_offsets, sorted_rows, row_pos, active, nullptr, s);
+  return from_hip(err);
+}
+
+moe_status moe_combine_rms_bf16(const float* y_rows, const float* topk_weights, const int32_t* row_pos, int32_t T,
+                                int32_t k, int32_t H, float eps, float* out, uint16_t* x_next, moe_stream_t stream) {
+  if (T > 0 && (!y_rows || !topk_weights || !row_pos || !out || !x_next)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(y_rows) || !aligned16(out) || ((uintptr_t)x_next & 7) != 0) return MOE_ERR_INVALID_ARG;
+  if (!rows_fit(T, k) || k > MOE_MAX_TOPK || H < 32 || H > MOE_MAX_DIM || (H & 31) != 0 || !(eps >= 0.0f))
+    return MOE_ERR_INVALID_ARG;
+  const moe_status d = check_device();
+  if (d != MOE_OK) return d;
+  return from_hip(moe::launch_combine_rms(y_rows, topk_weights, row_pos, T, k, H, eps, out, x_next,
+                                          (hipStream_t)stream));
+}
+
 moe_status moe_router_logits(const uint16_t* x_bf16, int32_t T, int32_t H, const float* w_router, int32_t E,
                              float* logits, moe_stream_t stream) {
   if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || H < 32 || H > MOE_MAX_DIM || (H & 31) != 0)

@@ -128,6 +128,10 @@ hipError_t launch_combine(const float* y_rows, const float* w, const int32_t* ro
                           float* out, hipStream_t s);
 
 hipError_t launch_rms_rescale(const float* y, int T, int H, float eps, uint16_t* x_next, hipStream_t s);
+hipError_t launch_route_group_one(const float* logits, int E, int k, int32_t* ids, float* w, int32_t* offsets,
+                                  int32_t* sorted_rows, int32_t* row_pos, int32_t* active, hipStream_t s);
+hipError_t launch_combine_rms(const float* y_rows, const float* w, const int32_t* row_pos, int T, int k, int H,
+                              float eps, float* out, uint16_t* x_next, hipStream_t s);
 
 hipError_t launch_router_logits(const uint16_t* x, int T, int H, const float* wr, int E, float* logits,
                                 hipStream_t s);

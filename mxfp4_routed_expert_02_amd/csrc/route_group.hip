@@ -116,16 +116,15 @@ __device__ __forceinline__ void wave_topk(uint32_t (&key)[C], int k, int lane, u
   }
 }
 
+// Top-k and softmax of one token's logits row by a block of 4 waves: each
+// wave picks the top-k of its quarter, wave 0 picks from the 4k candidates
+// in id order.  On return lanes j < k of wave 0 hold the j-th pick's id and
+// weight (the return value tells whether this thread holds a pick).
 template <int C>
-__global__ __launch_bounds__(kRoute4Threads) void route_topk_4w_kernel(const float* __restrict__ logits, int E,
-                                                                      int k, int32_t* __restrict__ ids,
-                                                                      float* __restrict__ weights) {
+__device__ __forceinline__ bool topk_block(const float* __restrict__ row, int E, int k, uint32_t* s_key,
+                                           int32_t* s_id, int& out_id, float& out_w) {
   constexpr int Q = MOE_WAVE * C;
-  __shared__ uint32_t s_key[4 * MOE_MAX_TOPK];
-  __shared__ int32_t s_id[4 * MOE_MAX_TOPK];
-  const int t = blockIdx.x;
   const int lane = threadIdx.x & (MOE_WAVE - 1), wave = threadIdx.x / MOE_WAVE;
-  const float* row = logits + (int64_t)t * E;
   uint32_t key[C];
 #pragma unroll
   for (int i = 0; i < C; ++i) {
@@ -140,7 +139,7 @@ __global__ __launch_bounds__(kRoute4Threads) void route_topk_4w_kernel(const flo
     s_id[wave * k + lane] = wave * Q + mp;
   }
   __syncthreads();
-  if (wave != 0) return;
+  if (wave != 0) return false;
   // candidate c = w*k + r in lane c/2, slot c%2
   uint32_t ck[2];
 #pragma unroll
@@ -160,10 +159,66 @@ __global__ __launch_bounds__(kRoute4Threads) void route_topk_4w_kernel(const flo
   const float ex = lane < k ? expf(my_val - mx) : 0.0f;
   float S = 0.0f;
   for (int j = 0; j < k; ++j) S += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
-  if (lane < k) {
-    ids[(int64_t)t * k + lane] = my_id;
-    weights[(int64_t)t * k + lane] = ex / S;
+  out_id = my_id;
+  out_w = ex / S;
+  return lane < k;
+}
+
+template <int C>
+__global__ __launch_bounds__(kRoute4Threads) void route_topk_4w_kernel(const float* __restrict__ logits, int E,
+                                                                      int k, int32_t* __restrict__ ids,
+                                                                      float* __restrict__ weights) {
+  __shared__ uint32_t s_key[4 * MOE_MAX_TOPK];
+  __shared__ int32_t s_id[4 * MOE_MAX_TOPK];
+  const int t = blockIdx.x;
+  int id;
+  float wv;
+  if (topk_block<C>(logits + (int64_t)t * E, E, k, s_key, s_id, id, wv)) {
+    const int lane = threadIdx.x & (MOE_WAVE - 1);
+    ids[(int64_t)t * k + lane] = id;
+    weights[(int64_t)t * k + lane] = wv;
   }
+}
+
+// One token: the top-k as above, then its grouping in the same block.  The
+// k picks are distinct experts, so every group holds one row: the offset of
+// expert e is the number of picks below e, and pick j's place in the
+// expert-major order is the number of picks below its id.  The outputs
+// equal group_rows_small_kernel's on the same ids.
+template <int C>
+__global__ __launch_bounds__(kRoute4Threads) void route_group_one_kernel(const float* __restrict__ logits, int E,
+                                                                        int k, int32_t* __restrict__ ids,
+                                                                        float* __restrict__ weights,
+                                                                        int32_t* __restrict__ offsets,
+                                                                        int32_t* __restrict__ sorted_rows,
+                                                                        int32_t* __restrict__ row_pos,
+                                                                        int32_t* __restrict__ active) {
+  __shared__ uint32_t s_key[4 * MOE_MAX_TOPK];
+  __shared__ int32_t s_id[4 * MOE_MAX_TOPK];
+  __shared__ int32_t s_pick[MOE_MAX_TOPK];
+  int id;
+  float wv;
+  const int lane = threadIdx.x & (MOE_WAVE - 1);
+  const bool mine = topk_block<C>(logits, E, k, s_key, s_id, id, wv);
+  if (mine) {
+    ids[lane] = id;
+    weights[lane] = wv;
+    s_pick[lane] = id;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e <= E; e += kRoute4Threads) {
+    int below = 0;
+    for (int j = 0; j < k; ++j) below += s_pick[j] < e;
+    offsets[e] = below;
+  }
+  if (mine) {
+    int r = 0;
+    for (int j = 0; j < k; ++j) r += s_pick[j] < id;
+    sorted_rows[r] = lane;
+    row_pos[lane] = r;
+    active[1 + r] = id;
+  }
+  if (threadIdx.x == 0) active[0] = k;
 }
 
 // ------------------------------------------------------------------ group --
@@ -397,6 +452,26 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
     const size_t lds = (size_t)E * sizeof(float) + (size_t)((E + 31) / 32) * sizeof(uint32_t);
     hipLaunchKernelGGL(route_topk_kernel, g, b, lds, s, logits, E, k, ids, w);
   }
+  return hipGetLastError();
+}
+
+// One token's top-k and grouping in one launch (E <= 2048; the caller falls
+// back to the two launches above that).
+hipError_t launch_route_group_one(const float* logits, int E, int k, int32_t* ids, float* w, int32_t* offsets,
+                                  int32_t* sorted_rows, int32_t* row_pos, int32_t* active, hipStream_t s) {
+  const dim3 g(1), b4(kRoute4Threads);
+  if (E <= 4 * 64 * 1)
+    hipLaunchKernelGGL(route_group_one_kernel<1>, g, b4, 0, s, logits, E, k, ids, w, offsets, sorted_rows, row_pos,
+                       active);
+  else if (E <= 4 * 64 * 2)
+    hipLaunchKernelGGL(route_group_one_kernel<2>, g, b4, 0, s, logits, E, k, ids, w, offsets, sorted_rows, row_pos,
+                       active);
+  else if (E <= 4 * 64 * 4)
+    hipLaunchKernelGGL(route_group_one_kernel<4>, g, b4, 0, s, logits, E, k, ids, w, offsets, sorted_rows, row_pos,
+                       active);
+  else
+    hipLaunchKernelGGL(route_group_one_kernel<8>, g, b4, 0, s, logits, E, k, ids, w, offsets, sorted_rows, row_pos,
+                       active);
   return hipGetLastError();
 }
 

@@ -1,5 +1,6 @@
 """A routed-expert layer object: owns the workspace and output buffers for a
-maximum token count and issues the four C-ABI calls on the current stream.
+maximum token count and issues the four C-ABI calls on the current stream
+(for one token, the fused route + group call in place of the first two).
 Reusing one object across stacked layers reuses its buffers (the buffers of
 one layer template serve every layer)."""
 from __future__ import annotations
@@ -49,7 +50,26 @@ class RoutedExpertLayer:
         if T > self.max_tokens:
             raise ValueError("more tokens than the layer was sized for")
         ids, w, grp, y_rows, o = self._views(T)
-        B.route_topk(logits, self.k, ids, w)
-        B.group_rows(ids, self.E, self.workspace, grp)
+        self._route_group(logits, ids, w, grp)
         B.expert_ffn_mxfp4(x, self.k, pool, grp, self.workspace, y_rows)
         return B.combine(y_rows, w, grp.row_pos, o if out is None else out)
+
+    def _route_group(self, logits, ids, w, grp):
+        if logits.shape[0] == 1:  # one token: top-k and grouping in one launch
+            B.route_group_one(logits, self.k, ids, w, grp)
+        else:
+            B.route_topk(logits, self.k, ids, w)
+            B.group_rows(ids, self.E, self.workspace, grp)
+
+    def step(self, x: torch.Tensor, logits: torch.Tensor, pool: B.ExpertPool, out: torch.Tensor,
+             x_next: torch.Tensor, eps: float = 1e-6) -> torch.Tensor:
+        """One layer of a stack: out [T, H] fp32 as __call__ gives it, and
+        x_next [T, H] bf16 = its RMS rescale, the next layer's input (the
+        combine and the rescale in one launch)."""
+        T = x.shape[0]
+        if T > self.max_tokens:
+            raise ValueError("more tokens than the layer was sized for")
+        ids, w, grp, y_rows, _ = self._views(T)
+        self._route_group(logits, ids, w, grp)
+        B.expert_ffn_mxfp4(x, self.k, pool, grp, self.workspace, y_rows)
+        return B.combine_rms_bf16(y_rows, w, grp.row_pos, out, x_next, eps)

@@ -132,3 +132,19 @@ def test_valid_call_without_gpu_reports_hip_error(L):
     if torch.cuda.is_available():
         pytest.skip("a GPU is present; this checks the no-device path only")
     assert L.moe_route_topk(FAKE, 1, 8, 2, FAKE, FAKE, None) == HIPERR
+
+
+def test_fused_calls_validation(L):
+    # moe_route_group_one: nulls, k out of range
+    assert L.moe_route_group_one(None, 896, 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == INVALID
+    assert L.moe_route_group_one(FAKE, 896, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == INVALID
+    assert L.moe_route_group_one(FAKE, 8, 9, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == INVALID
+    assert L.moe_route_group_one(FAKE, 896, 33, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == INVALID
+    assert L.moe_route_group_one(FAKE, 896, 16, FAKE, FAKE, FAKE, None, FAKE, FAKE, None) == INVALID
+    # moe_combine_rms_bf16: H not a multiple of 32, misaligned x_next, negative eps, nulls
+    assert L.moe_combine_rms_bf16(FAKE, FAKE, FAKE, 1, 16, 100, 1e-6, FAKE, FAKE, None) == INVALID
+    assert L.moe_combine_rms_bf16(FAKE, FAKE, FAKE, 1, 16, 7168, 1e-6, FAKE, FAKE + 2, None) == INVALID
+    assert L.moe_combine_rms_bf16(FAKE, FAKE, FAKE, 1, 16, 7168, -1.0, FAKE, FAKE, None) == INVALID
+    assert L.moe_combine_rms_bf16(FAKE, None, FAKE, 1, 16, 7168, 1e-6, FAKE, FAKE, None) == INVALID
+    assert L.moe_combine_rms_bf16(FAKE + 4, FAKE, FAKE, 1, 16, 7168, 1e-6, FAKE, FAKE, None) == INVALID
+

@@ -1,0 +1,101 @@
+"""The fused one-token calls on the GPU: moe_route_group_one against the
+separate moe_route_topk + moe_group_rows and against the oracle's top-k and
+grouping; moe_combine_rms_bf16 against the separate moe_combine +
+moe_rms_rescale_bf16 and against the oracle's combine and rescale.
+
+Against the separate GPU calls the fused outputs must be bit for bit the
+same.  Against the oracle: ids and grouping bit for bit, routing weights
+within 1e-6; the combine within the layer's tolerance (the GPU sums with
+fused multiply-adds, the oracle without), the rescale within one bf16 ulp of
+the oracle's rescale of the GPU's own combine.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mxfp4_routed_expert_02_amd import (Grouping, combine, combine_rms_bf16, group_rows, rms_rescale_bf16,
+                                        route_group_one, route_topk, synth)
+from tests.gpu_common import say
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda", 0)
+
+ROUTE_CASES = [  # E, k, logits kind: every register-top-k width, the fallback above 2048, ties
+    (896, 16, "normal"), (96, 16, "normal"), (8, 2, "normal"), (2048, 32, "normal"), (4096, 16, "normal"),
+    (896, 16, "ties"), (96, 1, "normal"), (300, 32, "ties"), (1, 1, "normal"),
+]
+
+
+def _logits(E, kind, seed):
+    wl = synth.Workload("fused", E=E, H=32, I=32, k=1, T=1, sub=seed)
+    lg = synth.router_logits(0, wl)
+    if kind == "ties":
+        lg = np.floor(np.abs(lg) * 2.0).astype(np.float32) % 4  # values in {0, 1, 2, 3}
+    return np.ascontiguousarray(lg, dtype=np.float32)
+
+
+def _grouping(E, R):
+    z = lambda n: torch.empty(n, dtype=torch.int32, device=DEV)  # noqa: E731
+    return Grouping(z(E + 1), z(R), z(R), z(E + 1))
+
+
+@pytest.mark.parametrize("E,k,kind", ROUTE_CASES, ids=[f"E{e}_k{k}_{c}" for e, k, c in ROUTE_CASES])
+def test_route_group_one(E, k, kind):
+    say(f"route_group_one E={E} k={k} {kind}")
+    lg = _logits(E, kind, 50 + E % 7)
+    lgd = torch.from_numpy(lg).to(DEV)
+    ids = torch.empty((1, k), dtype=torch.int32, device=DEV)
+    w = torch.empty((1, k), dtype=torch.float32, device=DEV)
+    fused = route_group_one(lgd, k, ids, w, _grouping(E, k))
+    ids2, w2 = route_topk(lgd, k)
+    ws = torch.empty(256, dtype=torch.uint8, device=DEV)
+    sep = group_rows(ids2, E, ws)
+    torch.cuda.synchronize()
+    n = int(sep.active[0].item())
+    assert n == k
+    assert torch.equal(ids, ids2) and torch.equal(w.view(torch.int32), w2.view(torch.int32))
+    for name in ("expert_offsets", "sorted_rows", "row_pos"):
+        assert torch.equal(getattr(fused, name), getattr(sep, name)), name
+    assert torch.equal(fused.active[:1 + n], sep.active[:1 + n])
+    # against the oracle
+    rid, rw = oracle.route_topk(lg, k)
+    rg = oracle.group_rows(rid, E)
+    np.testing.assert_array_equal(ids.cpu().numpy(), rid)
+    assert np.abs(w.cpu().numpy() - rw).max() <= 1e-6
+    np.testing.assert_array_equal(fused.expert_offsets.cpu().numpy(), rg["expert_offsets"])
+    np.testing.assert_array_equal(fused.sorted_rows.cpu().numpy(), rg["sorted_rows"])
+    np.testing.assert_array_equal(fused.row_pos.cpu().numpy(), rg["row_pos"])
+    np.testing.assert_array_equal(fused.active.cpu().numpy()[:1 + n], rg["active"][:1 + n])
+
+
+COMBINE_CASES = [(1, 16, 7168), (3, 16, 7168), (1, 1, 32), (2, 32, 16384), (5, 4, 96), (0, 16, 7168)]
+
+
+@pytest.mark.parametrize("T,k,H", COMBINE_CASES, ids=[f"T{t}_k{k}_H{h}" for t, k, h in COMBINE_CASES])
+def test_combine_rms_bf16(T, k, H):
+    say(f"combine_rms T={T} k={k} H={H}")
+    rng = np.random.default_rng(1000 + 7 * T + k + H)
+    R = T * k
+    y = (rng.standard_normal((R, H)) * 300.0).astype(np.float32)
+    w = rng.random((T, k)).astype(np.float32)
+    row_pos = rng.permutation(R).astype(np.int32)
+    yd, wd, rpd = (torch.from_numpy(a).to(DEV) for a in (y, w, row_pos))
+    out = torch.empty((T, H), dtype=torch.float32, device=DEV)
+    xn = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    combine_rms_bf16(yd, wd, rpd, out, xn, 1e-6)
+    out2 = combine(yd, wd, rpd)
+    xn2 = rms_rescale_bf16(out2, 1e-6)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int32), out2.view(torch.int32))
+    assert torch.equal(xn.view(torch.int16), xn2.view(torch.int16))
+    if T == 0:
+        return
+    ref = oracle.combine(y, w, row_pos, T, k, H)
+    got = out.cpu().numpy()
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    rms = np.sqrt(np.mean(ref.astype(np.float64) ** 2))
+    assert rel <= 2e-3 and np.abs(got - ref).max() <= 1e-2 * rms
+    ref_x = oracle.rms_rescale_bf16(got, 1e-6).astype(np.int32)
+    got_x = xn.view(torch.int16).cpu().numpy().astype(np.uint16).astype(np.int32)
+    assert np.abs(got_x - ref_x).max() <= 1, "rescale more than one bf16 ulp off"
