@@ -53,11 +53,16 @@ SMALL = [
     synth.Workload("many_rows_chunks", E=24, H=64, I=32, k=6, T=400, pool=26, sub=26),
     synth.Workload("wide_rows", E=4, H=4096, I=64, k=2, T=6, pool=27, sub=27),
     synth.Workload("long_rows_down", E=4, H=64, I=4096, k=2, T=6, pool=28, sub=28),
-    # grouped-GEMM (MFMA) path: experts with more than 4 rows, several K stages,
-    # weight tiles and ragged token tiles
-    synth.Workload("mfma_mid", E=8, H=512, I=256, k=2, T=300, pool=30, sub=30),
-    synth.Workload("mfma_ragged", E=12, H=768, I=512, k=3, T=97, logits="zipf", pool=31, sub=31),
-    synth.Workload("mfma_one_hot_expert", E=6, H=256, I=256, k=1, T=260, logits="dense16", pool=32, sub=32),
+    # grouped-GEMM (MFMA) path (H and I multiples of 512): several K stages,
+    # weight tiles and ragged token tiles; a long K that runs the steady-state
+    # ring loops; batches on both sides of the 16-token GEMV threshold (up to
+    # 16 tokens experts of 2..4 rows stay on the GEMV, above it they move)
+    synth.Workload("mfma_mid", E=8, H=512, I=512, k=2, T=300, pool=30, sub=30),
+    synth.Workload("mfma_ragged", E=12, H=1024, I=512, k=3, T=97, logits="zipf", pool=31, sub=31),
+    synth.Workload("mfma_one_hot_expert", E=6, H=512, I=512, k=1, T=260, logits="dense16", pool=32, sub=32),
+    synth.Workload("mfma_long_k", E=6, H=4096, I=2048, k=2, T=90, pool=34, sub=34),
+    synth.Workload("threshold_T16", E=16, H=512, I=512, k=4, T=16, pool=35, sub=35),
+    synth.Workload("threshold_T17", E=16, H=512, I=512, k=4, T=17, pool=36, sub=36),
 ]
 
 
@@ -67,13 +72,14 @@ def test_small_shapes(wl):
 
 
 def test_mfma_row_count_edges():
-    """Per-expert row counts at the edges of the GEMV/MFMA split (4, 5 rows) and
-    of the MFMA tile's 32-token groups and 128-token tiles: with k = 1, a +40
-    boost on one logit per token routes it, so every count is exact."""
-    counts = [1, 4, 5, 31, 32, 33, 64, 65, 97, 128, 129, 200]
+    """Per-expert row counts at the edges of the GEMV/MFMA split (1, 2 rows
+    above 16 tokens; 4, 5 below) and of the MFMA tile's 32-token groups and
+    128-token tiles: with k = 1, a +40 boost on one logit per token routes it,
+    so every count is exact."""
+    counts = [1, 2, 4, 5, 31, 32, 33, 64, 65, 97, 128, 129, 200]
     E = len(counts)
     T = sum(counts)
-    wl = synth.Workload("row_count_edges", E=E, H=512, I=256, k=1, T=T, pool=33, sub=33)
+    wl = synth.Workload("row_count_edges", E=E, H=512, I=512, k=1, T=T, pool=33, sub=33)
     say(f"case {wl.name}: counts {counts}")
     first = np.random.default_rng(1).permutation(np.repeat(np.arange(E), counts))
     logits = synth.router_logits(0, wl)
