@@ -94,6 +94,34 @@ def copy_probe(mib):
     log(f"copy probe: 5 copies of {mib} MiB ({n * 4} bytes read and written each)")
 
 
+def stream_read_gbs(dev, gib=4, reps=5):
+    """The box's achievable read bandwidth: a plain streaming-read kernel over
+    a `gib` GiB buffer (synth library), median of `reps` event-timed runs."""
+    import numpy as np
+    import torch
+
+    from mxfp4_routed_expert_02_amd import synth
+
+    L = synth.gpu_lib()
+    nbytes = gib << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    blocks = 1024
+    out = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def run(i):
+        rc = L.synth_stream_read(buf.data_ptr(), nbytes, out.data_ptr(), blocks, stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"synth_stream_read failed ({rc})")
+
+    run(0)
+    each = per_call_us(run, reps, stream)
+    del buf
+    gbs = nbytes / (float(np.median(each)) * 1e-6) / 1e9
+    log(f"streaming-read probe: {gbs:.0f} GB/s over {gib} GiB")
+    return gbs
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -175,6 +203,7 @@ def main():
     ffn_each = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
     ffn_us = float(np.mean(ffn_each))
     achieved = ffn_bytes / (ffn_us * 1e-6) / 1e9
+    stream_gbs = stream_read_gbs(dev)  # outside the timed regions
     log(f"expert FFN call: {ffn_us:.1f} us, {achieved:.0f} GB/s of {ffn_bytes} algorithmic bytes")
     layer_each = per_call_us(lambda i: step(i), K, stream)
 
@@ -187,7 +216,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "moe_expert_ffn_mxfp4 call", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": profiled_traffic(), "launch_us": round(ffn_us, 2),
-                     "algorithmic_bytes": ffn_bytes},
+                     "algorithmic_bytes": ffn_bytes, "achievable_read_gbs": round(stream_gbs, 1),
+                     "frac_achievable": round(achieved / stream_gbs, 4)},
         "decode896_us": {"ffn_call": pct(ffn_each), "layer": pct(layer_each),
                          "ffn_call_gbs_at_median": round(ffn_bytes / (np.median(ffn_each) * 1e-6) / 1e9, 1)},
     }

@@ -68,6 +68,9 @@ def gpu_lib():
         L.synth_expert_slabs_gpu.argtypes = [ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                              ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                              ctypes.c_uint64, ctypes.c_void_p]
+        L.synth_stream_read.restype = ctypes.c_int
+        L.synth_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int,
+                                        ctypes.c_void_p]
         _gpu_lib = L
     return _gpu_lib
 

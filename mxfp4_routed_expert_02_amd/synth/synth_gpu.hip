@@ -5,7 +5,9 @@
 //
 // Like moe_synth.c it draws inputs only and holds none of the layer's
 // arithmetic.  Byte for byte it must equal synth_expert_slabs() of
-// moe_synth.c; a GPU test compares the two.
+// moe_synth.c; a GPU test compares the two.  It also holds a plain
+// streaming-read probe that the benchmark times as the box's achievable
+// read bandwidth.
 //
 //   key(seed, tag) = mix(mix(seed + GAMMA) ^ tag)
 //   tag(array, sub, layer, expert) = array<<56 | sub<<40 | layer<<24 | expert
@@ -48,9 +50,39 @@ __global__ void slab_kernel(uint64_t seed, int pool, int layer, int e0, uint64_t
   dst[(uint64_t)blockIdx.y * stride_words + w] = z;
 }
 
+// Streaming-read probe, measurement context for the bandwidth-bound kernels:
+// every 16-byte word of the buffer is read once by grid-stride loads (four
+// per thread in flight), each thread writing the XOR of what it read so
+// the loads are live.  It draws and computes nothing of the layer.
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ src, uint64_t n16,
+                                                          uint32_t* __restrict__ out) {
+  const uint64_t step = (uint64_t)gridDim.x * 256 * 4;
+  uint32_t acc = 0u;
+  for (uint64_t i = (uint64_t)blockIdx.x * 256 * 4 + threadIdx.x; i < n16; i += step) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = i + 256u * u < n16 ? src[i + 256u * u] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  out[(uint64_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
 }  // namespace
 
 extern "C" {
+
+// Reads `bytes` (a multiple of 16) from 16-byte aligned device memory `src`
+// with `blocks` blocks of 256 threads; `out` holds blocks * 256 words.
+// Returns 0, -1 for arguments it cannot take, or the HIP error code.
+__attribute__((visibility("default"))) int synth_stream_read(const void* src, uint64_t bytes, void* out, int blocks,
+                                                             void* stream) {
+  if (!src || !out || blocks < 1 || (bytes & 15) || ((uintptr_t)src & 15)) return -1;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const uint4*)src,
+                     bytes / 16, (uint32_t*)out);
+  const hipError_t err = hipGetLastError();
+  return err == hipSuccess ? 0 : (int)err;
+}
 
 // Fills experts e0 .. e0+n-1 of (pool, layer) into device memory, slab i at
 // dst + i*stride bytes (stride and dst 8-byte aligned), on `stream`.
