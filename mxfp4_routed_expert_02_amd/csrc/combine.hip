@@ -11,7 +11,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kCombineThreads = 64;
 
-// all k loads of a thread are issued before the sums (k <= 32, 8 at a time)
+// a thread's loads are issued before its sums, 16 rows at a time (k <= 32),
+// so the usual k = 16 takes one round trip
 __global__ __launch_bounds__(kCombineThreads) void combine_vec4_kernel(const float* __restrict__ y_rows,
                                                                        const float* __restrict__ w,
                                                                        const int32_t* __restrict__ row_pos, int k,
@@ -22,13 +23,13 @@ __global__ __launch_bounds__(kCombineThreads) void combine_vec4_kernel(const flo
   const float* wt = w + (int64_t)t * k;
   const int32_t* rp = row_pos + (int64_t)t * k;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j0 = 0; j0 < k; j0 += 8) {
-    float4 y[8];
+  for (int j0 = 0; j0 < k; j0 += 16) {
+    float4 y[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < 16; ++u)
       if (j0 + u < k) y[u] = ((const float4*)(y_rows + (int64_t)rp[j0 + u] * H))[i];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < 16; ++u) {
       if (j0 + u < k) {
         const float c = wt[j0 + u];
         acc.x += c * y[u].x;

@@ -566,6 +566,189 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
 }
 
+// One token, rows of a compile-time NB blocks (the decode shape): the lane
+// layout and arithmetic of the MT = 1 kernels above, one work item per
+// block, with two changes to keep HBM busy:
+//  * every routed row belongs to token 0, so nothing the first weight loads
+//    need waits on the routing beyond the expert id (gate/up issues its
+//    activation loads before any routing read); the offsets are read while
+//    the first loads are in flight;
+//  * rolling prefetch: as soon as chunk j of an iteration has been used, the
+//    same registers are refilled with chunk j of the wave's next iteration,
+//    so a wave's loads stay in flight through its math instead of stopping
+//    at every iteration boundary, at no extra register cost;
+//  * the waves of an expert take its row-iterations round robin (wave i of
+//    the expert takes i, i + istep, ...), so at any moment they read one
+//    contiguous front of each matrix rather than one stretch per wave.
+// An expert the token picked more than once gets the same h (and y) in each
+// of its rows.
+// Added to a buffer offset, puts it past every matrix these kernels address
+// (all are far below 2 GiB), so the load returns 0 without a memory access.
+constexpr uint32_t kPastEnd = 0x80000000u;
+
+template <int J, int U, int NB>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void gateup_gemv_one_kernel(
+    const uint16_t* __restrict__ x, moe_mxfp4_weights w, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ active, float* __restrict__ h, int blocks_per_expert) {
+  extern __shared__ uint4 s_x4[];  // [4][NB]
+  // x's 4*NB uint4 in four named registers per thread (an array here went to scratch)
+  static_assert(4 * NB > 3 * kThreads && 4 * NB <= 4 * kThreads, "x staging assumes 3..4 uint4 per thread");
+  const uint4* x4 = (const uint4*)x;
+  const int tx = threadIdx.x;
+  const uint4 xs0 = x4[tx], xs1 = x4[tx + kThreads], xs2 = x4[tx + 2 * kThreads];
+  uint4 xs3 = make_uint4(0u, 0u, 0u, 0u);
+  if (tx + 3 * kThreads < 4 * NB) xs3 = x4[tx + 3 * kThreads];
+  const int slot = blockIdx.x / blocks_per_expert;
+  if (slot >= active[0]) return;
+  const int e = active[1 + slot];
+  constexpr int nb = NB, H = 32 * NB, lg = ctz_const(NB), G = 1 << lg, rpi = MOE_WAVE >> lg, rows_it = rpi * U;
+  const int I = w.inter;
+  const int lane = threadIdx.x & (MOE_WAVE - 1), wave = threadIdx.x / MOE_WAVE;
+  const int li = lane & (G - 1), gi = lane >> lg;
+  const int total_iters = (I + rows_it - 1) / rows_it;
+  const int it0 = (blockIdx.x % blocks_per_expert) * kWaves + wave;
+  const int istep = blocks_per_expert * kWaves;
+  const int it1 = total_iters;
+  constexpr uint32_t qrow = (uint32_t)H >> 1;
+  const int64_t eo = (int64_t)e * w.expert_stride;
+  const __amdgpu_buffer_rsrc_t rgq = make_rsrc(w.gate_q + eo, (uint32_t)I * qrow);
+  const __amdgpu_buffer_rsrc_t ruq = make_rsrc(w.up_q + eo, (uint32_t)I * qrow);
+  const __amdgpu_buffer_rsrc_t rgs = make_rsrc(w.gate_s + eo, (uint32_t)(I * nb));
+  const __amdgpu_buffer_rsrc_t rus = make_rsrc(w.up_s + eo, (uint32_t)(I * nb));
+  const uint32_t vq0 = (uint32_t)gi * qrow + 16u * li, vs0 = (uint32_t)(gi * nb + li);
+  uint4 qg[U][J], qu[U][J];
+  uint32_t sg[U][J], su[U][J];
+  // chunk j of row group u of iteration it
+  // chunk j of row group u of iteration it; `off` = kPastEnd turns the loads
+  // into out-of-range buffer reads, which return 0 and touch no memory
+  auto load_chunk = [&](int it, int u, int j, uint32_t off) {
+    const int n = it * rows_it + u * rpi;
+    const uint32_t bq = (uint32_t)n * qrow + off, bs = (uint32_t)(n * nb) + off;
+    qg[u][j] = load16(rgq, vq0 + bq + 16u * G * j);
+    qu[u][j] = load16(ruq, vq0 + bq + 16u * G * j);
+    sg[u][j] = load1(rgs, vs0 + bs + G * j);
+    su[u][j] = load1(rus, vs0 + bs + G * j);
+  };
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_chunk(it0, u, j, it0 < it1 ? 0u : kPastEnd);
+  const int p0 = offsets[e];
+  const int cnt = offsets[e + 1] - p0;
+  auto stage = [&](int c, const uint4& v) { s_x4[(c & 3) * nb + (c >> 2)] = v; };
+  stage(tx, xs0);
+  stage(tx + kThreads, xs1);
+  stage(tx + 2 * kThreads, xs2);
+  if (tx + 3 * kThreads < 4 * NB) stage(tx + 3 * kThreads, xs3);
+  __syncthreads();
+  for (int it = it0; it < it1; it += istep) {
+    const uint32_t next_off = it + istep < it1 ? 0u : kPastEnd;
+    const int n0 = it * rows_it;
+    float ag[U], au[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) ag[u] = au[u] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      uint4 xr[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xr[q] = s_x4[q * nb + li + G * j];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        bf16x2_t wv[16];
+        dequant_bf16(qg[u][j], wv);
+        ag[u] += chunk_dot_bf16_reg(wv, xr) * e8m0_to_f32(sg[u][j]);
+        dequant_bf16(qu[u][j], wv);
+        au[u] += chunk_dot_bf16_reg(wv, xr) * e8m0_to_f32(su[u][j]);
+        load_chunk(it + istep, u, j, next_off);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int n = n0 + u * rpi + gi;
+      const float g = group_sum_last(ag[u], G);
+      const float uu = group_sum_last(au[u], G);
+      if (li == G - 1 && n < I) {
+        const float v = silu_mul(g, uu);
+        for (int r = 0; r < cnt; ++r) h[(int64_t)(p0 + r) * I + n] = v;
+      }
+    }
+  }
+}
+
+template <int J, int U, int NB>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void down_gemv_one_kernel(
+    const float* __restrict__ h, moe_mxfp4_weights w, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ active, float* __restrict__ y_rows, int blocks_per_expert) {
+  extern __shared__ float4 s_h4[];  // [8][NB]
+  static_assert(8 * NB > kThreads && 8 * NB <= 2 * kThreads, "h staging assumes 1..2 float4 per thread");
+  const int slot = blockIdx.x / blocks_per_expert;
+  if (slot >= active[0]) return;
+  const int e = active[1 + slot];
+  constexpr int nb = NB, I = 32 * NB, lg = ctz_const(NB), G = 1 << lg, rpi = MOE_WAVE >> lg, rows_it = rpi * U;
+  const int H = w.hidden;
+  const int lane = threadIdx.x & (MOE_WAVE - 1), wave = threadIdx.x / MOE_WAVE;
+  const int li = lane & (G - 1), gi = lane >> lg;
+  const int total_iters = (H + rows_it - 1) / rows_it;
+  const int it0 = (blockIdx.x % blocks_per_expert) * kWaves + wave;
+  const int istep = blocks_per_expert * kWaves;
+  const int it1 = total_iters;
+  constexpr uint32_t qrow = (uint32_t)I >> 1;
+  const int64_t eo = (int64_t)e * w.expert_stride;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(w.down_q + eo, (uint32_t)H * qrow);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(w.down_s + eo, (uint32_t)(H * nb));
+  const uint32_t vq0 = (uint32_t)gi * qrow + 16u * li, vs0 = (uint32_t)(gi * nb + li);
+  uint4 q[U][J];
+  uint32_t sc[U][J];
+  auto load_chunk = [&](int it, int u, int j, uint32_t off) {
+    const int n = it * rows_it + u * rpi;
+    q[u][j] = load16(rq, vq0 + (uint32_t)n * qrow + off + 16u * G * j);
+    sc[u][j] = load1(rs, vs0 + (uint32_t)(n * nb) + off + G * j);
+  };
+  const int p0 = offsets[e];
+  const int cnt = offsets[e + 1] - p0;
+  const float4* h4 = (const float4*)(h + (int64_t)p0 * I);
+  const int tx = threadIdx.x;
+  const float4 hs0 = h4[tx];
+  float4 hs1 = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (tx + kThreads < 8 * NB) hs1 = h4[tx + kThreads];
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_chunk(it0, u, j, it0 < it1 ? 0u : kPastEnd);
+  s_h4[(tx & 7) * nb + (tx >> 3)] = hs0;
+  if (tx + kThreads < 8 * NB) s_h4[((tx + kThreads) & 7) * nb + ((tx + kThreads) >> 3)] = hs1;
+  __syncthreads();
+  for (int it = it0; it < it1; it += istep) {
+    const uint32_t next_off = it + istep < it1 ? 0u : kPastEnd;
+    const int n0 = it * rows_it;
+    float acc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc[u] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      float4 hr[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) hr[i] = s_h4[i * nb + li + G * j];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        f32x2_t wv[16];
+        dequant_f32(q[u][j], wv);
+        acc[u] += chunk_dot_f32_reg(wv, hr) * e8m0_to_f32(sc[u][j]);
+        load_chunk(it + istep, u, j, next_off);
+        __builtin_amdgcn_sched_barrier(0);  // one dequantized chunk live at a time
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int n = n0 + u * rpi + gi;
+      const float v = group_sum_last(acc[u], G);
+      if (li == G - 1 && n < H)
+        for (int r = 0; r < cnt; ++r) y_rows[(int64_t)(p0 + r) * H + n] = v;
+    }
+  }
+}
+
 constexpr size_t kMaxLds = 65536;
 
 int pick_mt(size_t bytes_per_row) {
@@ -747,7 +930,11 @@ hipError_t launch_expert_ffn(const uint16_t* x, int T, int k, const moe_mxfp4_we
     const int rows_it = (64 >> sg.lg) * sg.U, iters = (I + rows_it - 1) / rows_it;
     if (T == 1) {
       const GemvGrid gg = gemv_grid(iters, max_active, H == 7168 ? 4 : 2);
-      gateup_reg<1>(ga, sg, gg, dim3(max_active * gg.blocks_per_expert), nullptr, 1, INT32_MAX);
+      if (H == 7168)
+        hipLaunchKernelGGL((gateup_gemv_one_kernel<7, kGateU224, 224>), dim3(max_active * gg.blocks_per_expert),
+                           dim3(kThreads), (size_t)H * 2, s, x, w, offsets, active, hbuf, gg.blocks_per_expert);
+      else
+        gateup_reg<1>(ga, sg, gg, dim3(max_active * gg.blocks_per_expert), nullptr, 1, INT32_MAX);
     } else {
       const GemvGrid gg = multi_grid(iters);
       gateup_reg<1>(ga, sg, gg, multi(n1_max, gg), l1, 1, 1);
@@ -780,8 +967,14 @@ hipError_t launch_expert_ffn(const uint16_t* x, int T, int k, const moe_mxfp4_we
   if (reg_d) {
     const int rows_it = (64 >> sd.lg) * sd.U, iters = (H + rows_it - 1) / rows_it;
     if (T == 1) {
-      const GemvGrid gd = gemv_grid(iters, max_active, I == 1536 ? 3 : 2);
-      down_reg<1>(ga, sd, gd, dim3(max_active * gd.blocks_per_expert), nullptr, 1, INT32_MAX);
+      // the one-token down kernel holds 2 waves per SIMD (188 VGPRs)
+      const GemvGrid gd = gemv_grid(iters, max_active, 2);
+      if (I == 1536)
+        hipLaunchKernelGGL((down_gemv_one_kernel<3, kDownU48, 48>), dim3(max_active * gd.blocks_per_expert),
+                           dim3(kThreads), (size_t)I * 4, s, hbuf, w, offsets, active, y_rows,
+                           gd.blocks_per_expert);
+      else
+        down_reg<1>(ga, sd, gd, dim3(max_active * gd.blocks_per_expert), nullptr, 1, INT32_MAX);
     } else {
       const GemvGrid gd = multi_grid(iters);
       down_reg<1>(ga, sd, gd, multi(n1_max, gd), l1, 1, 1);

@@ -239,3 +239,34 @@ def test_prefill4096(pool896):
     ref = _ref_routing(wl, logits)
     toks = _sample_tokens(ref, wl.T, wl.k)
     _full_case(wl, pool896, tokens=toks)
+
+
+def test_decode896_repeated_ids(pool896):
+    """One token at the real decode shape whose id list repeats experts (the
+    grouping accepts that): every row of a repeated expert carries the same
+    y bits, and the combined output matches the oracle's token layer."""
+    from mxfp4_routed_expert_02_amd import Grouping, combine, expert_ffn_mxfp4, group_rows, workspace_bytes
+
+    wl = synth.WORKLOADS["decode896"]
+    say("case decode896_repeated_ids")
+    ids_np = np.array([[7, 300, 7, 895, 0, 300, 7, 41, 42, 43, 500, 501, 0, 650, 651, 7]], np.int32)
+    w_np = (np.arange(1, wl.k + 1, dtype=np.float32) / np.float32(wl.k * (wl.k + 1) / 2)).reshape(1, wl.k)
+    x_np = synth.activations_bf16(0, wl)
+    dev = torch.device("cuda", 0)
+    ws = torch.empty(workspace_bytes(1, wl.k, wl.E, wl.H, wl.I), dtype=torch.uint8, device=dev)
+    g = group_rows(torch.from_numpy(ids_np).to(dev), wl.E, ws)
+    x = torch.from_numpy(x_np.view(np.int16)).to(dev).view(torch.bfloat16)
+    y = torch.empty((wl.k, wl.H), dtype=torch.float32, device=dev)
+    expert_ffn_mxfp4(x, wl.k, pool896, g, ws, y)
+    out = combine(y, torch.from_numpy(w_np).to(dev), g.row_pos)
+    torch.cuda.synchronize()
+    ref_grp = oracle.group_rows(ids_np, wl.E)
+    assert np.array_equal(g.expert_offsets.cpu().numpy(), ref_grp["expert_offsets"])
+    y_np = y.cpu().numpy()
+    offs = ref_grp["expert_offsets"]
+    for e in (7, 300, 0):
+        rows = y_np[offs[e]:offs[e + 1]]
+        assert rows.shape[0] > 1 and all(np.array_equal(rows[0], r) for r in rows[1:]), f"expert {e}"
+    hpool = host_pool_subset(wl, ids_np.reshape(-1))
+    ref = oracle.token_layers_parallel(x_np, ids_np, w_np, hpool, [0], nthreads=NTH)
+    assert_close(out.cpu().numpy(), ref, "out")
