@@ -194,6 +194,15 @@ def main():
     for i in range(args.warmup):
         expert_ffn_mxfp4(xs[i % V], wl.k, pool, gobjs[i % V], layer.workspace, y_rows)
     torch.cuda.synchronize()
+    # average launch duration: K back-to-back calls between one event pair
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record(stream)
+    for i in range(K):
+        expert_ffn_mxfp4(xs[i % V], wl.k, pool, gobjs[i % V], layer.workspace, y_rows)
+    f1.record(stream)
+    torch.cuda.synchronize()
+    ffn_us = f0.elapsed_time(f1) * 1e3 / K
+    # spread of single calls (each bracketed by its own events, whose records add some time)
     for i in range(K):
         a, b = evs[i]
         a.record(stream)
@@ -201,7 +210,6 @@ def main():
         b.record(stream)
     torch.cuda.synchronize()
     ffn_each = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
-    ffn_us = float(np.mean(ffn_each))
     achieved = ffn_bytes / (ffn_us * 1e-6) / 1e9
     stream_gbs = stream_read_gbs(dev)  # outside the timed regions
     log(f"expert FFN call: {ffn_us:.1f} us, {achieved:.0f} GB/s of {ffn_bytes} algorithmic bytes")

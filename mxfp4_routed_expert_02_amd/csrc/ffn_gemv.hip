@@ -279,6 +279,10 @@ __device__ __forceinline__ uint32_t load1(__amdgpu_buffer_rsrc_t r, uint32_t off
 // items, so the work spreads over the experts that exist, not the upper
 // bound of them.
 
+// Added to a buffer offset, puts it past every matrix these kernels address
+// (all are far below 2 GiB), so the load returns 0 without a memory access.
+constexpr uint32_t kPastEnd = 0x80000000u;
+
 // Slots of the experts with exactly one routed row (l1) and with 2 .. reg_max
 // rows (l4), in slot order: l[0] = count, l[1..] = slots.  One block.
 __global__ __launch_bounds__(kThreads) void small_lists_kernel(const int32_t* __restrict__ offsets,
@@ -338,11 +342,16 @@ __global__ __launch_bounds__(kThreads) void small_lists_kernel(const int32_t* __
 // time: a weight chunk is loaded and dequantized once and applied to each of
 // the MT rows with exactly the arithmetic a single row gets, so a token's
 // result does not depend on how many other tokens share its experts.
+// The waves of an expert take its row-iterations round robin.  With a
+// compile-time row shape (NB > 0) each chunk's registers are refilled with
+// the wave's next iteration as soon as the chunk has been used (rolling
+// prefetch, as in the one-token kernels); run-time shapes load a whole
+// iteration at its start, which keeps their wider variants out of spills.
 template <int J, int U, int MT, int NB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void gateup_gemv_reg_kernel(
     const uint16_t* __restrict__ x, int k, moe_mxfp4_weights w, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_rows, const int32_t* __restrict__ active, const int32_t* __restrict__ list,
-    float* __restrict__ h, int lg_rt, int ipw, int blocks_per_expert, int cnt_lo, int cnt_hi) {
+    float* __restrict__ h, int lg_rt, int blocks_per_expert, int cnt_lo, int cnt_hi) {
   extern __shared__ uint4 s_x4[];  // [MT][4][nb]
   const int n_items = list ? list[0] * blocks_per_expert : (int)gridDim.x;
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
@@ -360,8 +369,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int G = 1 << lg, rpi = MOE_WAVE >> lg, rows_it = rpi * U;
   const int li = lane & (G - 1), gi = lane >> lg;
   const int total_iters = (I + rows_it - 1) / rows_it;
-  const int it0 = ((item % blocks_per_expert) * kWaves + wave) * ipw;
-  const int it1 = min(total_iters, it0 + ipw);
+  const int it0 = (item % blocks_per_expert) * kWaves + wave;
+  const int istep = blocks_per_expert * kWaves;
+  const int it1 = total_iters;
   const uint32_t qrow = (uint32_t)H >> 1;
   const int64_t eo = (int64_t)e * w.expert_stride;
   const __amdgpu_buffer_rsrc_t rgq = make_rsrc(w.gate_q + eo, (uint32_t)I * qrow);
@@ -372,22 +382,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int plane = 4 * nb;  // uint4 per staged row
   uint4 qg[U][J], qu[U][J];
   uint32_t sg[U][J], su[U][J];
-  auto load_iter = [&](int it) {
-    const int n0 = it * rows_it;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t bq = (uint32_t)(n0 + u * rpi) * qrow, bs = (uint32_t)((n0 + u * rpi) * nb);
-#pragma unroll
-      for (int j = 0; j < J; ++j) {
-        qg[u][j] = load16(rgq, vq0 + bq + 16u * G * j);
-        qu[u][j] = load16(ruq, vq0 + bq + 16u * G * j);
-        sg[u][j] = load1(rgs, vs0 + bs + G * j);
-        su[u][j] = load1(rus, vs0 + bs + G * j);
-      }
-    }
+  // chunk j of row group u of iteration it (off = kPastEnd: no memory access)
+  auto load_chunk = [&](int it, int u, int j, uint32_t off) {
+    const int n = it * rows_it + u * rpi;
+    const uint32_t bq = (uint32_t)n * qrow + off, bs = (uint32_t)(n * nb) + off;
+    qg[u][j] = load16(rgq, vq0 + bq + 16u * G * j);
+    qu[u][j] = load16(ruq, vq0 + bq + 16u * G * j);
+    sg[u][j] = load1(rgs, vs0 + bs + G * j);
+    su[u][j] = load1(rus, vs0 + bs + G * j);
   };
   for (int m0 = 0; m0 < cnt; m0 += MT) {
     const int mt = min(MT, cnt - m0);
+    if constexpr (NB > 0) {
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+#pragma unroll
+        for (int u = 0; u < U; ++u) load_chunk(it0, u, j, it0 < it1 ? 0u : kPastEnd);
+    }
     __syncthreads();
     for (int i = threadIdx.x; i < mt * plane; i += kThreads) {
       const int m = i / plane, c = i - m * plane;
@@ -395,9 +406,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       s_x4[m * plane + (c & 3) * nb + (c >> 2)] = ((const uint4*)(x + t * H))[c];
     }
     __syncthreads();
-    for (int it = it0; it < it1; ++it) {
+    for (int it = it0; it < it1; it += istep) {
+      const uint32_t next_off = it + istep < it1 ? 0u : kPastEnd;
       const int n0 = it * rows_it;
-      load_iter(it);
+      if constexpr (NB == 0) {
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+#pragma unroll
+          for (int u = 0; u < U; ++u) load_chunk(it, u, j, 0u);
+      }
       float ag[U][MT], au[U][MT];
 #pragma unroll
       for (int u = 0; u < U; ++u)
@@ -417,6 +434,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             ag[u][0] += chunk_dot_bf16_reg(wv, xr) * e8m0_to_f32(sg[u][j]);
             dequant_bf16(qu[u][j], wv);
             au[u][0] += chunk_dot_bf16_reg(wv, xr) * e8m0_to_f32(su[u][j]);
+            if constexpr (NB > 0) load_chunk(it + istep, u, j, next_off);
           }
         } else {
           // several rows: each chunk is dequantized once and serves every row
@@ -426,6 +444,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             dequant_bf16(qg[u][j], wg);
             dequant_bf16(qu[u][j], wu);
             const float fg = e8m0_to_f32(sg[u][j]), fu = e8m0_to_f32(su[u][j]);
+            if constexpr (NB > 0) load_chunk(it + istep, u, j, next_off);
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
               if (m < mt) {
@@ -462,7 +481,7 @@ template <int J, int U, int MT, int NB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void down_gemv_reg_kernel(
     const float* __restrict__ h, moe_mxfp4_weights w, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ active, const int32_t* __restrict__ list, float* __restrict__ y_rows, int lg_rt,
-    int ipw, int blocks_per_expert, int cnt_lo, int cnt_hi) {
+    int blocks_per_expert, int cnt_lo, int cnt_hi) {
   extern __shared__ float4 s_h4[];  // [MT][8][nb]
   const int n_items = list ? list[0] * blocks_per_expert : (int)gridDim.x;
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
@@ -478,8 +497,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int G = 1 << lg, rpi = MOE_WAVE >> lg, rows_it = rpi * U;
   const int li = lane & (G - 1), gi = lane >> lg;
   const int total_iters = (H + rows_it - 1) / rows_it;
-  const int it0 = ((item % blocks_per_expert) * kWaves + wave) * ipw;
-  const int it1 = min(total_iters, it0 + ipw);
+  const int it0 = (item % blocks_per_expert) * kWaves + wave;
+  const int istep = blocks_per_expert * kWaves;
+  const int it1 = total_iters;
   const uint32_t qrow = (uint32_t)I >> 1;
   const int64_t eo = (int64_t)e * w.expert_stride;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(w.down_q + eo, (uint32_t)H * qrow);
@@ -488,29 +508,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int plane = 8 * nb;  // float4 per staged row
   uint4 q[U][J];
   uint32_t sc[U][J];
-  auto load_iter = [&](int it) {
-    const int n0 = it * rows_it;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t bq = (uint32_t)(n0 + u * rpi) * qrow, bs = (uint32_t)((n0 + u * rpi) * nb);
-#pragma unroll
-      for (int j = 0; j < J; ++j) {
-        q[u][j] = load16(rq, vq0 + bq + 16u * G * j);
-        sc[u][j] = load1(rs, vs0 + bs + G * j);
-      }
-    }
+  auto load_chunk = [&](int it, int u, int j, uint32_t off) {
+    const int n = it * rows_it + u * rpi;
+    q[u][j] = load16(rq, vq0 + (uint32_t)n * qrow + off + 16u * G * j);
+    sc[u][j] = load1(rs, vs0 + (uint32_t)(n * nb) + off + G * j);
   };
   for (int m0 = 0; m0 < cnt; m0 += MT) {
     const int mt = min(MT, cnt - m0);
+    if constexpr (NB > 0) {
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+#pragma unroll
+        for (int u = 0; u < U; ++u) load_chunk(it0, u, j, it0 < it1 ? 0u : kPastEnd);
+    }
     __syncthreads();
     for (int i = threadIdx.x; i < mt * plane; i += kThreads) {
       const int m = i / plane, c = i - m * plane;
       s_h4[m * plane + (c & 7) * nb + (c >> 3)] = ((const float4*)(h + (int64_t)(p0 + m0 + m) * I))[c];
     }
     __syncthreads();
-    for (int it = it0; it < it1; ++it) {
+    for (int it = it0; it < it1; it += istep) {
+      const uint32_t next_off = it + istep < it1 ? 0u : kPastEnd;
       const int n0 = it * rows_it;
-      load_iter(it);
+      if constexpr (NB == 0) {
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+#pragma unroll
+          for (int u = 0; u < U; ++u) load_chunk(it, u, j, 0u);
+      }
       float acc[U][MT];
 #pragma unroll
       for (int u = 0; u < U; ++u)
@@ -528,6 +553,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             f32x2_t wv[16];
             dequant_f32(q[u][j], wv);
             acc[u][0] += chunk_dot_f32_reg(wv, hr) * e8m0_to_f32(sc[u][j]);
+            if constexpr (NB > 0) load_chunk(it + istep, u, j, next_off);
             __builtin_amdgcn_sched_barrier(0);  // one dequantized chunk live at a time
           }
         } else {
@@ -537,6 +563,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             f32x2_t wv[16];
             dequant_f32(q[u][j], wv);
             const float f = e8m0_to_f32(sc[u][j]);
+            if constexpr (NB > 0) load_chunk(it + istep, u, j, next_off);
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
               if (m < mt) {
@@ -582,10 +609,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 //    contiguous front of each matrix rather than one stretch per wave.
 // An expert the token picked more than once gets the same h (and y) in each
 // of its rows.
-// Added to a buffer offset, puts it past every matrix these kernels address
-// (all are far below 2 GiB), so the load returns 0 without a memory access.
-constexpr uint32_t kPastEnd = 0x80000000u;
-
 template <int J, int U, int NB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void gateup_gemv_one_kernel(
     const uint16_t* __restrict__ x, moe_mxfp4_weights w, const int32_t* __restrict__ offsets,
@@ -827,7 +850,7 @@ void gateup_reg(const GemvArgs& a, const GemvShape& sh, const GemvGrid& gg, dim3
   const size_t lds = (size_t)MT * H * 2;
 #define GU(JJ, UU, NB)                                                                                          \
   hipLaunchKernelGGL((gateup_gemv_reg_kernel<JJ, UU, MT, NB>), grid, dim3(kThreads), lds, a.s, a.x, a.k, *a.w, \
-                     a.offsets, a.sorted_rows, a.active, list, a.h, sh.lg, gg.ipw, gg.blocks_per_expert, lo, hi)
+                     a.offsets, a.sorted_rows, a.active, list, a.h, sh.lg, gg.blocks_per_expert, lo, hi)
   if (H == 7168) {
     GU(7, kGateU224, 224);
     return;
@@ -853,7 +876,7 @@ void down_reg(const GemvArgs& a, const GemvShape& sh, const GemvGrid& gg, dim3 g
   const size_t lds = (size_t)MT * I * 4;
 #define DN(JJ, UU, NB)                                                                                              \
   hipLaunchKernelGGL((down_gemv_reg_kernel<JJ, UU, MT, NB>), grid, dim3(kThreads), lds, a.s, a.h, *a.w, a.offsets, \
-                     a.active, list, a.y_rows, sh.lg, gg.ipw, gg.blocks_per_expert, lo, hi)
+                     a.active, list, a.y_rows, sh.lg, gg.blocks_per_expert, lo, hi)
   if (I == 1536) {
     DN(3, kDownU48, 48);
     return;
