@@ -210,7 +210,7 @@ MOE_API moe_status moe_rms_rescale_bf16(const float* y, int32_t T, int32_t H, fl
  * Fused calls for callers that step one token, or one layer of a stack, at
  * a time (batch-1 decode through the layer stack: page
  * "hn.213312.xyz/article/49090233", technical highlights, double-buffered
- * layer loading; each of the calls below replaces two launches).  Their
+ * layer loading; each of the calls below replaces two calls).  Their
  * outputs equal those of the calls they replace bit for bit.
  *
  * moe_route_group_one - moe_route_topk followed by moe_group_rows for a
@@ -235,6 +235,24 @@ MOE_API moe_status moe_route_group_one(const float* logits, int32_t E, int32_t k
 MOE_API moe_status moe_combine_rms_bf16(const float* y_rows, const float* topk_weights, const int32_t* row_pos,
                                         int32_t T, int32_t k, int32_t H, float eps, float* out, uint16_t* x_next,
                                         moe_stream_t stream);
+
+/*
+ * moe_expert_ffn_combine_mxfp4 - moe_expert_ffn_mxfp4 followed by
+ * moe_combine of its y_rows: y_rows [T*k][H] fp32 and out [T][H] fp32 as
+ * those two calls write them, bit for bit.  For a single token (T = 1) with
+ * I = 1536, k <= 16 and a hidden size the register gate/up takes, the down
+ * projection and the weighted combine run in one launch (block b owns
+ * output rows of every routed expert, so the combine needs no second pass
+ * over y_rows); other shapes run the two calls.  Arguments as
+ * moe_expert_ffn_mxfp4 and moe_combine take them (same workspace size;
+ * MOE_ERR_INVALID_ARG / MOE_ERR_WORKSPACE_TOO_SMALL as those calls).
+ */
+MOE_API moe_status moe_expert_ffn_combine_mxfp4(const uint16_t* x, int32_t T, int32_t k,
+                                                const moe_mxfp4_weights* w, const int32_t* expert_offsets,
+                                                const int32_t* sorted_rows, const int32_t* active,
+                                                const float* topk_weights, const int32_t* row_pos, float* y_rows,
+                                                float* out, void* workspace, size_t workspace_bytes,
+                                                moe_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -54,12 +54,15 @@ def lib():
         L.moe_router_logits.argtypes = [_P, _I32, _I32, _P, _I32, _P, _P]
         L.moe_route_group_one.argtypes = [_P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P]
         L.moe_combine_rms_bf16.argtypes = [_P, _P, _P, _I32, _I32, _I32, ctypes.c_float, _P, _P, _P]
+        L.moe_expert_ffn_combine_mxfp4.argtypes = [_P, _I32, _I32, W, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                   ctypes.c_size_t, _P]
         L.moe_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32, _I32]
         L.moe_workspace_bytes.restype = ctypes.c_size_t
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         for f in ("moe_route_topk", "moe_group_rows", "moe_expert_ffn_mxfp4", "moe_combine",
-                  "moe_rms_rescale_bf16", "moe_router_logits"):
+                  "moe_rms_rescale_bf16", "moe_router_logits", "moe_route_group_one", "moe_combine_rms_bf16",
+                  "moe_expert_ffn_combine_mxfp4"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -167,6 +170,21 @@ def expert_ffn_mxfp4(x: torch.Tensor, k: int, pool: ExpertPool, grp: Grouping, w
         _dev(grp.active, torch.int32, "active"), _dev(y_rows, torch.float32, "y_rows"),
         _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(x.device)))
     return y_rows
+
+
+def expert_ffn_combine_mxfp4(x: torch.Tensor, k: int, pool: ExpertPool, grp: Grouping, weights: torch.Tensor,
+                             workspace: torch.Tensor, y_rows: torch.Tensor, out: torch.Tensor) -> torch.Tensor:
+    """expert_ffn_mxfp4 then combine in one call: y_rows [T*k, H] and out [T, H] fp32 written; returns out."""
+    T, H = x.shape
+    xb = x.view(torch.int16) if x.dtype == torch.bfloat16 else x
+    _check("moe_expert_ffn_combine_mxfp4", lib().moe_expert_ffn_combine_mxfp4(
+        _dev(xb, torch.int16, "x"), T, k, ctypes.byref(pool.weights),
+        _dev(grp.expert_offsets, torch.int32, "expert_offsets"), _dev(grp.sorted_rows, torch.int32, "sorted_rows"),
+        _dev(grp.active, torch.int32, "active"), _dev(weights, torch.float32, "weights"),
+        _dev(grp.row_pos, torch.int32, "row_pos"), _dev(y_rows, torch.float32, "y_rows"),
+        _dev(out, torch.float32, "out"), _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+        _stream(x.device)))
+    return out
 
 
 def combine(y_rows: torch.Tensor, weights: torch.Tensor, row_pos: torch.Tensor,

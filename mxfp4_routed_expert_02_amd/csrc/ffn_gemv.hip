@@ -641,7 +641,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const uint32_t vq0 = (uint32_t)gi * qrow + 16u * li, vs0 = (uint32_t)(gi * nb + li);
   uint4 qg[U][J], qu[U][J];
   uint32_t sg[U][J], su[U][J];
-  // chunk j of row group u of iteration it
   // chunk j of row group u of iteration it; `off` = kPastEnd turns the loads
   // into out-of-range buffer reads, which return 0 and touch no memory
   auto load_chunk = [&](int it, int u, int j, uint32_t off) {
@@ -768,6 +767,123 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       const float v = group_sum_last(acc[u], G);
       if (li == G - 1 && n < H)
         for (int r = 0; r < cnt; ++r) y_rows[(int64_t)(p0 + r) * H + n] = v;
+    }
+  }
+}
+
+// One token, I = 32*NB, k <= kFMaxK: the down projection of every routed
+// expert and the weighted combine in one launch (the step after gate/up at
+// decode).  Block b owns output rows [kRows*b, kRows*b + kRows) of every
+// active expert.  The h rows of all active experts sit in LDS; each wave
+// takes (expert, 4-row iteration) items round robin with the rolling
+// prefetch of the kernels above, and every row's y (the arithmetic of the
+// down GEMVs: G lanes per row, per-block scaled partial sums, DPP
+// reduction) goes to y_rows and to an LDS tile indexed by sorted row.  After
+// one barrier, kRows threads form out[n] = sum_j w[j] * y[row_pos[j]][n]
+// with j ascending, the combine kernel's arithmetic, so both outputs equal
+// the separate down and combine launches bit for bit.
+constexpr int kFThreads = 1024;
+constexpr int kFWaves = kFThreads / MOE_WAVE;
+constexpr int kFIters = 7;  // 4-row iterations per block and expert
+constexpr int kFMaxK = 16;
+
+template <int NB>
+__global__ __launch_bounds__(kFThreads) void down_combine_one_kernel(
+    const float* __restrict__ h, moe_mxfp4_weights w, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ active, const float* __restrict__ topk_w, const int32_t* __restrict__ row_pos,
+    int k, float* __restrict__ y_rows, float* __restrict__ out) {
+  constexpr int nb = NB, I = 32 * NB, lg = ctz_const(NB), G = 1 << lg, J = NB / G, rpi = MOE_WAVE >> lg;
+  constexpr int kRows = kFIters * rpi;  // output rows per block
+  static_assert(J * G == NB && J <= 8, "register lane layout");
+  constexpr uint32_t qrow = (uint32_t)I >> 1;
+  __shared__ float4 s_h4[kFMaxK][8 * NB];  // h of each active expert, planes [8][NB]
+  __shared__ float s_y[kFMaxK][kRows];     // y of this block's rows, by sorted row
+  const int H = w.hidden;
+  const int na = active[0];
+  const int lane = threadIdx.x & (MOE_WAVE - 1), wave = threadIdx.x / MOE_WAVE;
+  const int li = lane & (G - 1), gi = lane >> lg;
+  const int n_base = blockIdx.x * kRows;
+  const int n_items = na * kFIters;
+  // lane s < na holds slot s's expert id, first sorted row and row count
+  int e_l = 0, p0_l = 0, cnt_l = 0;
+  if (lane < na) {
+    e_l = active[1 + lane];
+    p0_l = offsets[e_l];
+    cnt_l = offsets[e_l + 1] - p0_l;
+  }
+  uint4 q[J];
+  uint32_t sc[J];
+  __amdgpu_buffer_rsrc_t rq, rs;
+  uint32_t bq = 0, bs = 0;
+  // rsrc and row offsets of an item (wave-uniform); items past the last get
+  // the last slot's matrix and kPastEnd, so their loads touch no memory
+  auto set_item = [&](int item) {
+    const int slot = min(item / kFIters, na - 1), itr = item - (item / kFIters) * kFIters;
+    const int e = __builtin_amdgcn_readlane(e_l, slot);
+    const int64_t eo = (int64_t)e * w.expert_stride;
+    rq = make_rsrc(w.down_q + eo, (uint32_t)H * qrow);
+    rs = make_rsrc(w.down_s + eo, (uint32_t)(H * nb));
+    const int n = n_base + itr * rpi + gi;
+    const uint32_t off = item < n_items ? 0u : kPastEnd;
+    bq = (uint32_t)n * qrow + 16u * li + off;
+    bs = (uint32_t)(n * nb + li) + off;
+  };
+  auto load_chunk = [&](int j) {
+    q[j] = load16(rq, bq + 16u * G * j);
+    sc[j] = load1(rs, bs + G * j);
+  };
+  set_item(wave);
+#pragma unroll
+  for (int j = 0; j < J; ++j) load_chunk(j);
+  // all h loads of a thread in flight together (slots past na re-read the
+  // last slot's row and are not stored)
+  constexpr int kHPer = (kFMaxK * 8 * NB + kFThreads - 1) / kFThreads;
+  float4 hv[kHPer];
+#pragma unroll
+  for (int i = 0; i < kHPer; ++i) {
+    const int c = threadIdx.x + kFThreads * i;
+    const int s = min(c / (8 * NB), na - 1), cc = c % (8 * NB);
+    hv[i] = ((const float4*)(h + (int64_t)__shfl(p0_l, s, MOE_WAVE) * I))[cc];
+  }
+#pragma unroll
+  for (int i = 0; i < kHPer; ++i) {
+    const int c = threadIdx.x + kFThreads * i;
+    const int s = c / (8 * NB), cc = c % (8 * NB);
+    if (s < na) s_h4[s][(cc & 7) * nb + (cc >> 3)] = hv[i];
+  }
+  __syncthreads();
+  for (int item = wave; item < n_items; item += kFWaves) {
+    const int slot = item / kFIters, itr = item - slot * kFIters;
+    const int n = n_base + itr * rpi + gi;
+    set_item(item + kFWaves);
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      float4 hr[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) hr[i] = s_h4[slot][i * nb + li + G * j];
+      f32x2_t wv[16];
+      dequant_f32(q[j], wv);
+      acc += chunk_dot_f32_reg(wv, hr) * e8m0_to_f32(sc[j]);
+      load_chunk(j);  // chunk j of the wave's next item
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const float v = group_sum_last(acc, G);
+    const int p0 = __builtin_amdgcn_readlane(p0_l, slot), cnt = __builtin_amdgcn_readlane(cnt_l, slot);
+    if (li == G - 1 && n < H) {
+      for (int r = 0; r < cnt; ++r) {
+        y_rows[(int64_t)(p0 + r) * H + n] = v;
+        s_y[p0 + r][n - n_base] = v;
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < kRows) {
+    const int n = n_base + threadIdx.x;
+    if (n < H) {
+      float acc = 0.0f;
+      for (int j = 0; j < k; ++j) acc += topk_w[j] * s_y[row_pos[j]][threadIdx.x];
+      out[n] = acc;
     }
   }
 }
@@ -911,9 +1027,13 @@ size_t expert_ffn_workspace(int T, int k, int E, int H, int I) {
   return b;
 }
 
-hipError_t launch_expert_ffn(const uint16_t* x, int T, int k, const moe_mxfp4_weights& w, const int32_t* offsets,
-                             const int32_t* sorted_rows, const int32_t* active, float* y_rows, void* ws,
-                             hipStream_t s) {
+namespace {
+
+// The expert FFN; with gateup_only (one token, register gate/up shape) it
+// stops after h, for the fused down + combine launch.
+hipError_t expert_ffn_impl(const uint16_t* x, int T, int k, const moe_mxfp4_weights& w, const int32_t* offsets,
+                           const int32_t* sorted_rows, const int32_t* active, float* y_rows, void* ws,
+                           hipStream_t s, bool gateup_only) {
   if (T == 0) return hipSuccess;
   const int R = T * k, E = w.num_experts, H = w.hidden, I = w.inter;
   const int max_active = R < E ? R : E;
@@ -966,6 +1086,7 @@ hipError_t launch_expert_ffn(const uint16_t* x, int T, int k, const moe_mxfp4_we
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
+  if (gateup_only) return hipSuccess;
   uint8_t* mfma_ws = (uint8_t*)ws + off;
   if (use_mfma) {
     if ((err = launch_mfma_gateup(x, T, k, w, offsets, sorted_rows, active, hbuf, mfma_ws, s)) != hipSuccess)
@@ -1026,6 +1147,33 @@ hipError_t launch_expert_ffn(const uint16_t* x, int T, int k, const moe_mxfp4_we
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_expert_ffn(const uint16_t* x, int T, int k, const moe_mxfp4_weights& w, const int32_t* offsets,
+                             const int32_t* sorted_rows, const int32_t* active, float* y_rows, void* ws,
+                             hipStream_t s) {
+  return expert_ffn_impl(x, T, k, w, offsets, sorted_rows, active, y_rows, ws, s, false);
+}
+
+hipError_t launch_expert_ffn_combine(const uint16_t* x, int T, int k, const moe_mxfp4_weights& w,
+                                     const int32_t* offsets, const int32_t* sorted_rows, const int32_t* active,
+                                     const float* topk_w, const int32_t* row_pos, float* y_rows, float* out,
+                                     void* ws, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const bool fused = T == 1 && k <= kFMaxK && w.inter == 1536 && gemv_shape(w.hidden >> 5, true).ok;
+  if (!fused) {
+    hipError_t err = expert_ffn_impl(x, T, k, w, offsets, sorted_rows, active, y_rows, ws, s, false);
+    if (err != hipSuccess) return err;
+    return launch_combine(y_rows, topk_w, row_pos, T, k, w.hidden, out, s);
+  }
+  hipError_t err = expert_ffn_impl(x, T, k, w, offsets, sorted_rows, active, y_rows, ws, s, true);
+  if (err != hipSuccess) return err;
+  constexpr int kRows = kFIters * 4;  // NB = 48: 16 lanes per row, 4 rows per iteration
+  hipLaunchKernelGGL(down_combine_one_kernel<48>, dim3((w.hidden + kRows - 1) / kRows), dim3(kFThreads), 0, s,
+                     (const float*)ws, w, offsets, active, topk_w, row_pos, k, y_rows, out);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -159,6 +159,23 @@ moe_status moe_combine_rms_bf16(const float* y_rows, const float* topk_weights, 
                                           (hipStream_t)stream));
 }
 
+moe_status moe_expert_ffn_combine_mxfp4(const uint16_t* x, int32_t T, int32_t k, const moe_mxfp4_weights* w,
+                                        const int32_t* expert_offsets, const int32_t* sorted_rows,
+                                        const int32_t* active, const float* topk_weights, const int32_t* row_pos,
+                                        float* y_rows, float* out, void* workspace, size_t workspace_bytes,
+                                        moe_stream_t stream) {
+  if (!expert_offsets || !active || !workspace || !aligned16(workspace)) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!x || !sorted_rows || !y_rows || !topk_weights || !row_pos || !out)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(y_rows) || !aligned16(out)) return MOE_ERR_INVALID_ARG;
+  if (!rows_fit(T, k) || k > MOE_MAX_TOPK || !weights_ok(w)) return MOE_ERR_INVALID_ARG;
+  if (workspace_bytes < moe::expert_ffn_workspace(T, k, w->num_experts, w->hidden, w->inter))
+    return MOE_ERR_WORKSPACE_TOO_SMALL;
+  const moe_status d = check_device();
+  if (d != MOE_OK) return d;
+  return from_hip(moe::launch_expert_ffn_combine(x, T, k, *w, expert_offsets, sorted_rows, active, topk_weights,
+                                                 row_pos, y_rows, out, workspace, (hipStream_t)stream));
+}
+
 moe_status moe_router_logits(const uint16_t* x_bf16, int32_t T, int32_t H, const float* w_router, int32_t E,
                              float* logits, moe_stream_t stream) {
   if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || H < 32 || H > MOE_MAX_DIM || (H & 31) != 0)

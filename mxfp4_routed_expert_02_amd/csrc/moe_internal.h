@@ -113,6 +113,10 @@ hipError_t launch_expert_ffn(const uint16_t* x, int T, int k, const moe_mxfp4_we
                              const int32_t* sorted_rows, const int32_t* active, float* y_rows, void* ws,
                              hipStream_t s);
 size_t expert_ffn_workspace(int T, int k, int E, int H, int I);
+hipError_t launch_expert_ffn_combine(const uint16_t* x, int T, int k, const moe_mxfp4_weights& w,
+                                     const int32_t* offsets, const int32_t* sorted_rows, const int32_t* active,
+                                     const float* topk_w, const int32_t* row_pos, float* y_rows, float* out,
+                                     void* ws, hipStream_t s);
 
 // MFMA grouped-GEMM path (experts with more than 4 routed rows)
 bool mfma_shape_ok(int H, int I);

@@ -1,6 +1,8 @@
 """A routed-expert layer object: owns the workspace and output buffers for a
-maximum token count and issues the four C-ABI calls on the current stream
-(for one token, the fused route + group call in place of the first two).
+maximum token count and issues the C-ABI calls on the current stream: route
+and group (for one token the fused route + group call), then the expert FFN
+with the combine (moe_expert_ffn_combine_mxfp4, which for one token runs the
+down projection and the combine in one launch).
 Reusing one object across stacked layers reuses its buffers (the buffers of
 one layer template serve every layer)."""
 from __future__ import annotations
@@ -51,8 +53,10 @@ class RoutedExpertLayer:
             raise ValueError("more tokens than the layer was sized for")
         ids, w, grp, y_rows, o = self._views(T)
         self._route_group(logits, ids, w, grp)
-        B.expert_ffn_mxfp4(x, self.k, pool, grp, self.workspace, y_rows)
-        return B.combine(y_rows, w, grp.row_pos, o if out is None else out)
+        # expert FFN and combine (one token: the down projection and the
+        # combine share a launch)
+        return B.expert_ffn_combine_mxfp4(x, self.k, pool, grp, w, self.workspace, y_rows,
+                                          o if out is None else out)
 
     def _route_group(self, logits, ids, w, grp):
         if logits.shape[0] == 1:  # one token: top-k and grouping in one launch
@@ -71,5 +75,8 @@ class RoutedExpertLayer:
             raise ValueError("more tokens than the layer was sized for")
         ids, w, grp, y_rows, _ = self._views(T)
         self._route_group(logits, ids, w, grp)
+        if T == 1:  # down + combine in one launch, then the rescale
+            B.expert_ffn_combine_mxfp4(x, self.k, pool, grp, w, self.workspace, y_rows, out)
+            return B.rms_rescale_bf16(out, eps, x_next)
         B.expert_ffn_mxfp4(x, self.k, pool, grp, self.workspace, y_rows)
         return B.combine_rms_bf16(y_rows, w, grp.row_pos, out, x_next, eps)

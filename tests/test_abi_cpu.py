@@ -148,3 +148,27 @@ def test_fused_calls_validation(L):
     assert L.moe_combine_rms_bf16(FAKE, None, FAKE, 1, 16, 7168, 1e-6, FAKE, FAKE, None) == INVALID
     assert L.moe_combine_rms_bf16(FAKE + 4, FAKE, FAKE, 1, 16, 7168, 1e-6, FAKE, FAKE, None) == INVALID
 
+
+
+def test_ffn_combine_rejects_bad_arguments(L):
+    big = 1 << 30
+    w = _weights()
+    f = L.moe_expert_ffn_combine_mxfp4
+    ok = (FAKE, 1, 16, ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big, None)
+    for i in (0, 7, 8, 10, 11):  # x, topk_weights, row_pos, out, workspace null
+        args = list(ok)
+        args[i] = None
+        assert f(*args) == INVALID, i
+    args = list(ok)
+    args[10] = FAKE + 4  # out misaligned
+    assert f(*args) == INVALID
+    args = list(ok)
+    args[2] = 33  # k above the maximum
+    assert f(*args) == INVALID
+    bad = _weights(H=250)
+    args = list(ok)
+    args[3] = ctypes.byref(bad)
+    assert f(*args) == INVALID
+    args = list(ok)
+    args[12] = 16
+    assert f(*args) == WS_SMALL

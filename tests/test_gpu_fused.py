@@ -99,3 +99,45 @@ def test_combine_rms_bf16(T, k, H):
     ref_x = oracle.rms_rescale_bf16(got, 1e-6).astype(np.int32)
     got_x = xn.view(torch.int16).cpu().numpy().astype(np.uint16).astype(np.int32)
     assert np.abs(got_x - ref_x).max() <= 1, "rescale more than one bf16 ulp off"
+
+
+# moe_expert_ffn_combine_mxfp4 against moe_expert_ffn_mxfp4 + moe_combine:
+# the fused one-token down + combine launch (decode shape, k <= 16, with and
+# without repeated ids) and the shapes that fall back to the two calls
+FFN_COMBINE_CASES = [  # name, E, H, I, k, T, ids (None: routed from logits)
+    ("decode896", 896, 7168, 1536, 16, 1, None),
+    ("decode896_k8", 896, 7168, 1536, 8, 1, None),
+    ("decode896_k1", 896, 7168, 1536, 1, 1, None),
+    ("repeated_ids", 896, 7168, 1536, 16, 1, [7, 300, 7, 895, 0, 300, 7, 41, 42, 43, 500, 501, 0, 650, 651, 7]),
+    ("odd_hidden", 64, 4096, 1536, 16, 1, None),
+    ("k32_two_calls", 96, 7168, 1536, 32, 1, None),
+    ("tiny_two_calls", 8, 256, 128, 2, 4, None),
+    ("verify_two_calls", 64, 7168, 1536, 16, 3, None),
+]
+
+
+@pytest.mark.parametrize("case", FFN_COMBINE_CASES, ids=[c[0] for c in FFN_COMBINE_CASES])
+def test_ffn_combine_matches_two_calls(case):
+    from mxfp4_routed_expert_02_amd import expert_ffn_combine_mxfp4, expert_ffn_mxfp4, workspace_bytes
+    from tests.gpu_common import device_pool
+
+    name, E, H, I, k, T, ids_list = case
+    say(f"ffn_combine {name}: E={E} H={H} I={I} k={k} T={T}")
+    wl = synth.Workload(name, E=E, H=H, I=I, k=k, T=T, pool=40, sub=40)
+    pool = device_pool(wl)
+    x = torch.from_numpy(synth.activations_bf16(0, wl).view(np.int16)).to(DEV).view(torch.bfloat16)
+    if ids_list is None:
+        ids, w = route_topk(torch.from_numpy(synth.router_logits(0, wl)).to(DEV), k)
+    else:
+        ids = torch.tensor([ids_list], dtype=torch.int32, device=DEV)
+        w = torch.softmax(torch.arange(k, dtype=torch.float32, device=DEV), 0).view(1, k)
+    ws = torch.empty(workspace_bytes(T, k, E, H, I), dtype=torch.uint8, device=DEV)
+    g = group_rows(ids, E, ws)
+    y1 = expert_ffn_mxfp4(x, k, pool, g, ws)
+    out1 = combine(y1, w, g.row_pos)
+    y2 = torch.full_like(y1, float("nan"))
+    out2 = torch.full_like(out1, float("nan"))
+    expert_ffn_combine_mxfp4(x, k, pool, g, w, ws, y2, out2)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32)), "y_rows bits differ"
+    assert torch.equal(out1.view(torch.int32), out2.view(torch.int32)), "out bits differ"
