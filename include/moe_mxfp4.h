@@ -254,6 +254,30 @@ MOE_API moe_status moe_expert_ffn_combine_mxfp4(const uint16_t* x, int32_t T, in
                                                 float* out, void* workspace, size_t workspace_bytes,
                                                 moe_stream_t stream);
 
+/*
+ * moe_decode_layer_mxfp4 - one token through the whole layer: what
+ * moe_route_group_one followed by moe_expert_ffn_combine_mxfp4 (T = 1)
+ * write, bit for bit, for batch-1 decode (the pages' runtime steps one
+ * token through every layer: page "hn.213312.xyz/article/49090233", how it
+ * works).  At H = 7168, I = 1536, k <= 16 and E <= 2048 it takes two
+ * launches: the top-k runs inside every block of the gate/up launch (each
+ * block picks the expert of its slot itself, block 0 writes the routing and
+ * grouping outputs), then the down projection with the combine; other
+ * shapes run the two calls.
+ *   logits [E] fp32 (E = w->num_experts), x [H] bf16 bits (16-byte aligned)
+ *   topk_ids [k], topk_weights [k], expert_offsets [E+1], sorted_rows [k],
+ *   row_pos [k], active [E+1]: out, as moe_route_group_one writes them
+ *   y_rows [k][H] fp32 and out [H] fp32 (16-byte aligned): out
+ *   workspace: moe_workspace_bytes(1, k, E, H, I) bytes, 16-byte aligned
+ * 1 <= k <= min(E, MOE_MAX_TOPK); every pointer non-null
+ * (MOE_ERR_INVALID_ARG otherwise; MOE_ERR_WORKSPACE_TOO_SMALL).
+ */
+MOE_API moe_status moe_decode_layer_mxfp4(const float* logits, const uint16_t* x, int32_t k,
+                                          const moe_mxfp4_weights* w, int32_t* topk_ids, float* topk_weights,
+                                          int32_t* expert_offsets, int32_t* sorted_rows, int32_t* row_pos,
+                                          int32_t* active, float* y_rows, float* out, void* workspace,
+                                          size_t workspace_bytes, moe_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

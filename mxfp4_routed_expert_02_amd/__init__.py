@@ -27,6 +27,7 @@ from ._binding import (  # noqa: F401
     MoeWeights,
     combine,
     combine_rms_bf16,
+    decode_layer_mxfp4,
     expert_ffn_combine_mxfp4,
     expert_ffn_mxfp4,
     group_rows,

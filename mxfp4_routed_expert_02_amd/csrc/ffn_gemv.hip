@@ -16,6 +16,7 @@
 #include <climits>
 
 #include "moe_internal.h"
+#include "topk_device.h"
 
 namespace {
 
@@ -888,6 +889,124 @@ __global__ __launch_bounds__(kFThreads) void down_combine_one_kernel(
   }
 }
 
+// One token routed inside the gate/up launch: every block first runs the
+// token's four-wave top-k (the routing kernels' device code, so the picks are
+// theirs bit for bit) and takes the expert of its slot, the slot-th smallest
+// picked id (the active list the grouping writes; the picks are distinct, so
+// that expert's one row sits at sorted position `slot`).  Block 0 also
+// writes the routing weights and the grouping exactly as the fused
+// route + group kernel does.  The rest is gateup_gemv_one_kernel: the
+// activation loads go out before the top-k, the first weight loads as soon
+// as the expert is known.
+template <int J, int U, int NB, int C>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void route_gateup_one_kernel(
+    const float* __restrict__ logits, int E, int k, const uint16_t* __restrict__ x, moe_mxfp4_weights w,
+    float* __restrict__ h, int32_t* __restrict__ ids, float* __restrict__ topk_w, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_rows, int32_t* __restrict__ row_pos, int32_t* __restrict__ active,
+    int blocks_per_expert) {
+  static_assert(kThreads == kRoute4Threads, "the top-k runs on the whole block");
+  extern __shared__ uint4 s_x4[];  // [4][NB]
+  __shared__ TopkLds s;
+  static_assert(4 * NB > 3 * kThreads && 4 * NB <= 4 * kThreads, "x staging assumes 3..4 uint4 per thread");
+  const uint4* x4 = (const uint4*)x;
+  const int tx = threadIdx.x;
+  const uint4 xs0 = x4[tx], xs1 = x4[tx + kThreads], xs2 = x4[tx + 2 * kThreads];
+  uint4 xs3 = make_uint4(0u, 0u, 0u, 0u);
+  if (tx + 3 * kThreads < 4 * NB) xs3 = x4[tx + 3 * kThreads];
+  topk_block<C, true>(logits, E, k, s);
+  if (blockIdx.x == 0) {
+    if (tx < MOE_WAVE) {
+      int id;
+      float wv;
+      if (topk_softmax(s, k, tx, id, wv)) {
+        ids[tx] = id;
+        topk_w[tx] = wv;
+      }
+    } else if (k <= 16) {
+      group_one<4>(s, E, k, offsets, sorted_rows, row_pos, active);
+    } else {
+      group_one<8>(s, E, k, offsets, sorted_rows, row_pos, active);
+    }
+  }
+  const int slot = blockIdx.x / blocks_per_expert;
+  if (slot >= k) return;
+  const int lane = tx & (MOE_WAVE - 1), wave = tx / MOE_WAVE;
+  // lane j < k: pick j's id and its rank among the picks by id
+  int pid = INT_MAX, prank = -1;
+  if (lane < k) {
+    pid = s.pick_id[lane];
+    prank = 0;
+    for (int i = 0; i < k; ++i) prank += s.pick_id[i] < pid;
+  }
+  const int src = __ffsll((unsigned long long)__ballot(prank == slot)) - 1;
+  const int e = __builtin_amdgcn_readlane(pid, src);
+  const int p0 = slot;  // offsets[e]: the picks below e
+  constexpr int nb = NB, H = 32 * NB, lg = ctz_const(NB), G = 1 << lg, rpi = MOE_WAVE >> lg, rows_it = rpi * U;
+  const int I = w.inter;
+  const int li = lane & (G - 1), gi = lane >> lg;
+  const int total_iters = (I + rows_it - 1) / rows_it;
+  const int it0 = (blockIdx.x % blocks_per_expert) * kWaves + wave;
+  const int istep = blocks_per_expert * kWaves;
+  const int it1 = total_iters;
+  constexpr uint32_t qrow = (uint32_t)H >> 1;
+  const int64_t eo = (int64_t)e * w.expert_stride;
+  const __amdgpu_buffer_rsrc_t rgq = make_rsrc(w.gate_q + eo, (uint32_t)I * qrow);
+  const __amdgpu_buffer_rsrc_t ruq = make_rsrc(w.up_q + eo, (uint32_t)I * qrow);
+  const __amdgpu_buffer_rsrc_t rgs = make_rsrc(w.gate_s + eo, (uint32_t)(I * nb));
+  const __amdgpu_buffer_rsrc_t rus = make_rsrc(w.up_s + eo, (uint32_t)(I * nb));
+  const uint32_t vq0 = (uint32_t)gi * qrow + 16u * li, vs0 = (uint32_t)(gi * nb + li);
+  uint4 qg[U][J], qu[U][J];
+  uint32_t sg[U][J], su[U][J];
+  auto load_chunk = [&](int it, int u, int j, uint32_t off) {
+    const int n = it * rows_it + u * rpi;
+    const uint32_t bq = (uint32_t)n * qrow + off, bs = (uint32_t)(n * nb) + off;
+    qg[u][j] = load16(rgq, vq0 + bq + 16u * G * j);
+    qu[u][j] = load16(ruq, vq0 + bq + 16u * G * j);
+    sg[u][j] = load1(rgs, vs0 + bs + G * j);
+    su[u][j] = load1(rus, vs0 + bs + G * j);
+  };
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_chunk(it0, u, j, it0 < it1 ? 0u : kPastEnd);
+  auto stage = [&](int c, const uint4& v) { s_x4[(c & 3) * nb + (c >> 2)] = v; };
+  stage(tx, xs0);
+  stage(tx + kThreads, xs1);
+  stage(tx + 2 * kThreads, xs2);
+  if (tx + 3 * kThreads < 4 * NB) stage(tx + 3 * kThreads, xs3);
+  __syncthreads();
+  for (int it = it0; it < it1; it += istep) {
+    const uint32_t next_off = it + istep < it1 ? 0u : kPastEnd;
+    const int n0 = it * rows_it;
+    float ag[U], au[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) ag[u] = au[u] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      uint4 xr[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xr[q] = s_x4[q * nb + li + G * j];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        bf16x2_t wv[16];
+        dequant_bf16(qg[u][j], wv);
+        ag[u] += chunk_dot_bf16_reg(wv, xr) * e8m0_to_f32(sg[u][j]);
+        dequant_bf16(qu[u][j], wv);
+        au[u] += chunk_dot_bf16_reg(wv, xr) * e8m0_to_f32(su[u][j]);
+        load_chunk(it + istep, u, j, next_off);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int n = n0 + u * rpi + gi;
+      const float g = group_sum_last(ag[u], G);
+      const float uu = group_sum_last(au[u], G);
+      if (li == G - 1 && n < I) h[(int64_t)p0 * I + n] = silu_mul(g, uu);
+    }
+  }
+}
+
 constexpr size_t kMaxLds = 65536;
 
 int pick_mt(size_t bytes_per_row) {
@@ -1172,6 +1291,39 @@ hipError_t launch_expert_ffn_combine(const uint16_t* x, int T, int k, const moe_
   if (err != hipSuccess) return err;
   constexpr int kRows = kFIters * 4;  // NB = 48: 16 lanes per row, 4 rows per iteration
   hipLaunchKernelGGL(down_combine_one_kernel<48>, dim3((w.hidden + kRows - 1) / kRows), dim3(kFThreads), 0, s,
+                     (const float*)ws, w, offsets, active, topk_w, row_pos, k, y_rows, out);
+  return hipGetLastError();
+}
+
+bool route_ffn_combine_one_ok(int E, int k, const moe_mxfp4_weights& w) {
+  return w.hidden == 7168 && w.inter == 1536 && k <= kFMaxK && k <= E && E <= kRegExperts;
+}
+
+hipError_t launch_route_ffn_combine_one(const float* logits, int k, const uint16_t* x, const moe_mxfp4_weights& w,
+                                        int32_t* ids, float* topk_w, int32_t* offsets, int32_t* sorted_rows,
+                                        int32_t* row_pos, int32_t* active, float* y_rows, float* out, void* ws,
+                                        hipStream_t s) {
+  const int E = w.num_experts, H = w.hidden, I = w.inter;
+  const GemvShape sg = gemv_shape(H >> 5, true);
+  const int rows_it = (64 >> sg.lg) * sg.U, iters = (I + rows_it - 1) / rows_it;
+  const GemvGrid gg = gemv_grid(iters, k, 4);
+  const dim3 grid(k * gg.blocks_per_expert);
+  float* hbuf = (float*)ws;
+  const size_t lds = (size_t)H * 2;
+#define RG(C)                                                                                                    \
+  hipLaunchKernelGGL((route_gateup_one_kernel<7, kGateU224, 224, C>), grid, dim3(kThreads), lds, s, logits, E, k, \
+                     x, w, hbuf, ids, topk_w, offsets, sorted_rows, row_pos, active, gg.blocks_per_expert)
+  if (E <= 4 * MOE_WAVE * 2)
+    RG(2);
+  else if (E <= 4 * MOE_WAVE * 4)
+    RG(4);
+  else
+    RG(8);
+#undef RG
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  constexpr int kRows = kFIters * 4;
+  hipLaunchKernelGGL(down_combine_one_kernel<48>, dim3((H + kRows - 1) / kRows), dim3(kFThreads), 0, s,
                      (const float*)ws, w, offsets, active, topk_w, row_pos, k, y_rows, out);
   return hipGetLastError();
 }

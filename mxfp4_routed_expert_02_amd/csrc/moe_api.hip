@@ -176,6 +176,38 @@ moe_status moe_expert_ffn_combine_mxfp4(const uint16_t* x, int32_t T, int32_t k,
                                                  row_pos, y_rows, out, workspace, (hipStream_t)stream));
 }
 
+moe_status moe_decode_layer_mxfp4(const float* logits, const uint16_t* x, int32_t k, const moe_mxfp4_weights* w,
+                                  int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                                  int32_t* sorted_rows, int32_t* row_pos, int32_t* active, float* y_rows, float* out,
+                                  void* workspace, size_t workspace_bytes, moe_stream_t stream) {
+  if (!logits || !x || !topk_ids || !topk_weights || !expert_offsets || !sorted_rows || !row_pos || !active ||
+      !y_rows || !out || !workspace)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(y_rows) || !aligned16(out) || !aligned16(workspace)) return MOE_ERR_INVALID_ARG;
+  if (!weights_ok(w) || k < 1 || k > MOE_MAX_TOPK || k > w->num_experts) return MOE_ERR_INVALID_ARG;
+  if (workspace_bytes < moe::expert_ffn_workspace(1, k, w->num_experts, w->hidden, w->inter))
+    return MOE_ERR_WORKSPACE_TOO_SMALL;
+  const moe_status d = check_device();
+  if (d != MOE_OK) return d;
+  const hipStream_t s = (hipStream_t)stream;
+  const int E = w->num_experts;
+  if (moe::route_ffn_combine_one_ok(E, k, *w))
+    return from_hip(moe::launch_route_ffn_combine_one(logits, k, x, *w, topk_ids, topk_weights, expert_offsets,
+                                                      sorted_rows, row_pos, active, y_rows, out, workspace, s));
+  hipError_t err;
+  if (E <= 2048) {
+    err = moe::launch_route_group_one(logits, E, k, topk_ids, topk_weights, expert_offsets, sorted_rows, row_pos,
+                                      active, s);
+  } else {
+    err = moe::launch_route_topk(logits, 1, E, k, topk_ids, topk_weights, s);
+    if (err == hipSuccess)
+      err = moe::launch_group_rows(topk_ids, 1, k, E, expert_offsets, sorted_rows, row_pos, active, nullptr, s);
+  }
+  if (err != hipSuccess) return MOE_ERR_HIP;
+  return from_hip(moe::launch_expert_ffn_combine(x, 1, k, *w, expert_offsets, sorted_rows, active, topk_weights,
+                                                 row_pos, y_rows, out, workspace, s));
+}
+
 moe_status moe_router_logits(const uint16_t* x_bf16, int32_t T, int32_t H, const float* w_router, int32_t E,
                              float* logits, moe_stream_t stream) {
   if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || H < 32 || H > MOE_MAX_DIM || (H & 31) != 0)

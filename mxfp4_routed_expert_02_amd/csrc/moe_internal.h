@@ -113,6 +113,11 @@ hipError_t launch_expert_ffn(const uint16_t* x, int T, int k, const moe_mxfp4_we
                              const int32_t* sorted_rows, const int32_t* active, float* y_rows, void* ws,
                              hipStream_t s);
 size_t expert_ffn_workspace(int T, int k, int E, int H, int I);
+bool route_ffn_combine_one_ok(int E, int k, const moe_mxfp4_weights& w);
+hipError_t launch_route_ffn_combine_one(const float* logits, int k, const uint16_t* x, const moe_mxfp4_weights& w,
+                                        int32_t* ids, float* topk_w, int32_t* offsets, int32_t* sorted_rows,
+                                        int32_t* row_pos, int32_t* active, float* y_rows, float* out, void* ws,
+                                        hipStream_t s);
 hipError_t launch_expert_ffn_combine(const uint16_t* x, int T, int k, const moe_mxfp4_weights& w,
                                      const int32_t* offsets, const int32_t* sorted_rows, const int32_t* active,
                                      const float* topk_w, const int32_t* row_pos, float* y_rows, float* out,

@@ -1,8 +1,8 @@
 """A routed-expert layer object: owns the workspace and output buffers for a
-maximum token count and issues the C-ABI calls on the current stream: route
-and group (for one token the fused route + group call), then the expert FFN
-with the combine (moe_expert_ffn_combine_mxfp4, which for one token runs the
-down projection and the combine in one launch).
+maximum token count and issues the C-ABI calls on the current stream: for one
+token the whole layer in one call (moe_decode_layer_mxfp4); for several,
+route and group, then the expert FFN with the combine
+(moe_expert_ffn_combine_mxfp4).
 Reusing one object across stacked layers reuses its buffers (the buffers of
 one layer template serve every layer)."""
 from __future__ import annotations
@@ -52,11 +52,11 @@ class RoutedExpertLayer:
         if T > self.max_tokens:
             raise ValueError("more tokens than the layer was sized for")
         ids, w, grp, y_rows, o = self._views(T)
+        o = o if out is None else out
+        if T == 1:  # the whole layer in one call (two launches at the decode shape)
+            return B.decode_layer_mxfp4(logits, x, self.k, pool, ids, w, grp, self.workspace, y_rows, o)
         self._route_group(logits, ids, w, grp)
-        # expert FFN and combine (one token: the down projection and the
-        # combine share a launch)
-        return B.expert_ffn_combine_mxfp4(x, self.k, pool, grp, w, self.workspace, y_rows,
-                                          o if out is None else out)
+        return B.expert_ffn_combine_mxfp4(x, self.k, pool, grp, w, self.workspace, y_rows, o)
 
     def _route_group(self, logits, ids, w, grp):
         if logits.shape[0] == 1:  # one token: top-k and grouping in one launch
@@ -74,9 +74,9 @@ class RoutedExpertLayer:
         if T > self.max_tokens:
             raise ValueError("more tokens than the layer was sized for")
         ids, w, grp, y_rows, _ = self._views(T)
-        self._route_group(logits, ids, w, grp)
-        if T == 1:  # down + combine in one launch, then the rescale
-            B.expert_ffn_combine_mxfp4(x, self.k, pool, grp, w, self.workspace, y_rows, out)
+        if T == 1:  # the layer in one call, then the rescale
+            B.decode_layer_mxfp4(logits, x, self.k, pool, ids, w, grp, self.workspace, y_rows, out)
             return B.rms_rescale_bf16(out, eps, x_next)
+        self._route_group(logits, ids, w, grp)
         B.expert_ffn_mxfp4(x, self.k, pool, grp, self.workspace, y_rows)
         return B.combine_rms_bf16(y_rows, w, grp.row_pos, out, x_next, eps)

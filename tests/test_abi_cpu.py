@@ -172,3 +172,21 @@ def test_ffn_combine_rejects_bad_arguments(L):
     args = list(ok)
     args[12] = 16
     assert f(*args) == WS_SMALL
+
+
+def test_decode_layer_rejects_bad_arguments(L):
+    big = 1 << 30
+    w = _weights()
+    f = L.moe_decode_layer_mxfp4
+    ok = [FAKE, FAKE, 2, ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big, None]
+    for i in (0, 1, 4, 5, 6, 7, 8, 9, 10, 11, 12):  # every pointer
+        args = list(ok)
+        args[i] = None
+        assert f(*args) == INVALID, i
+    for i, v in ((1, FAKE + 2), (10, FAKE + 4), (11, FAKE + 8), (2, 0), (2, 9), (2, 33)):  # k > E = 8
+        args = list(ok)
+        args[i] = v
+        assert f(*args) == INVALID, (i, v)
+    args = list(ok)
+    args[13] = 16
+    assert f(*args) == WS_SMALL

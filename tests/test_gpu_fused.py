@@ -141,3 +141,56 @@ def test_ffn_combine_matches_two_calls(case):
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int32), y2.view(torch.int32)), "y_rows bits differ"
     assert torch.equal(out1.view(torch.int32), out2.view(torch.int32)), "out bits differ"
+
+
+# moe_decode_layer_mxfp4 against moe_route_group_one + moe_expert_ffn_combine_mxfp4:
+# routing inside the gate/up launch (register top-k widths 2, 4 and 8, ties,
+# k = 1) and the shapes that run the separate calls
+DECODE_LAYER_CASES = [  # name, E, H, I, k, logits kind
+    ("E896_k16", 896, 7168, 1536, 16, "normal"),
+    ("E96_k16", 96, 7168, 1536, 16, "normal"),
+    ("E2048_k16", 2048, 7168, 1536, 16, "normal"),
+    ("E896_ties", 896, 7168, 1536, 16, "ties"),
+    ("E300_k1", 300, 7168, 1536, 1, "normal"),
+    ("E4096_separate", 4096, 7168, 1536, 16, "normal"),
+    ("k32_separate", 96, 7168, 1536, 32, "normal"),
+    ("small_separate", 8, 256, 128, 2, "normal"),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_LAYER_CASES, ids=[c[0] for c in DECODE_LAYER_CASES])
+def test_decode_layer_matches_calls(case):
+    from mxfp4_routed_expert_02_amd import decode_layer_mxfp4, expert_ffn_combine_mxfp4, workspace_bytes
+    from tests.gpu_common import device_pool
+
+    name, E, H, I, k, kind = case
+    say(f"decode_layer {name}: E={E} H={H} I={I} k={k} {kind}")
+    wl = synth.Workload(name, E=E, H=H, I=I, k=k, T=1, pool=41, sub=41)
+    pool = device_pool(wl)
+    x = torch.from_numpy(synth.activations_bf16(0, wl).view(np.int16)).to(DEV).view(torch.bfloat16)
+    lg = torch.from_numpy(_logits(E, kind, 60 + E % 5)).to(DEV)
+    ws = torch.empty(workspace_bytes(1, k, E, H, I), dtype=torch.uint8, device=DEV)
+    # separate calls
+    ids1 = torch.empty((1, k), dtype=torch.int32, device=DEV)
+    w1 = torch.empty((1, k), dtype=torch.float32, device=DEV)
+    g1 = route_group_one(lg, k, ids1, w1, _grouping(E, k))
+    y1 = torch.empty((k, H), dtype=torch.float32, device=DEV)
+    out1 = torch.empty((1, H), dtype=torch.float32, device=DEV)
+    expert_ffn_combine_mxfp4(x, k, pool, g1, w1, ws, y1, out1)
+    # one call, outputs pre-filled with garbage
+    ids2 = torch.full((1, k), -7, dtype=torch.int32, device=DEV)
+    w2 = torch.full((1, k), float("nan"), dtype=torch.float32, device=DEV)
+    g2 = _grouping(E, k)
+    for t in (g2.expert_offsets, g2.sorted_rows, g2.row_pos, g2.active):
+        t.fill_(-5)
+    y2 = torch.full_like(y1, float("nan"))
+    out2 = torch.full_like(out1, float("nan"))
+    decode_layer_mxfp4(lg, x, k, pool, ids2, w2, g2, ws, y2, out2)
+    torch.cuda.synchronize()
+    assert torch.equal(ids1, ids2), "ids differ"
+    assert torch.equal(w1.view(torch.int32), w2.view(torch.int32)), "weights differ"
+    for nm in ("expert_offsets", "sorted_rows", "row_pos"):
+        assert torch.equal(getattr(g1, nm), getattr(g2, nm)), nm
+    assert torch.equal(g1.active[:1 + k], g2.active[:1 + k]), "active differs"
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32)), "y_rows bits differ"
+    assert torch.equal(out1.view(torch.int32), out2.view(torch.int32)), "out bits differ"
