@@ -360,13 +360,13 @@ def prefill_side(dev, pool, seed, reps, name):
 
 def stack_side(dev, seed, reps):
     """Batch-1 decode through the 92-layer stack (96 experts per layer, 155 GB
-    resident), RMS rescale between layers; the token step (92 x 3 launches:
-    fused route+group, expert FFN, fused combine+rescale) is
+    resident), RMS rescale between layers; the token step (92 x 2 launches:
+    rescale + top-k + gate/up, then down + combine; one final rescale) is
     captured once in a HIP graph and replayed."""
     import numpy as np
     import torch
 
-    from mxfp4_routed_expert_02_amd import ExpertPool, synth
+    from mxfp4_routed_expert_02_amd import ExpertPool, rms_rescale_bf16, synth
     from mxfp4_routed_expert_02_amd.layer import RoutedExpertLayer
 
     wl = synth.WORKLOADS["stack92"]
@@ -382,9 +382,13 @@ def stack_side(dev, seed, reps):
     out = torch.empty((1, wl.H), dtype=torch.float32, device=dev)
 
     def token():
-        x = x0
-        for l in range(wl.layers):  # route+group, FFN, combine+rescale: 3 launches a layer
-            x = layer.step(x, logits[l], pools[l], out, xbuf[l & 1], 1e-6)
+        # layer 0 from the token's bf16 input; layers 1..91 from the previous
+        # layer's output (RMS rescale inside the gate/up launch): 2 launches a
+        # layer, then the rescale that would feed the next token
+        layer(x0, logits[0], pools[0], out)
+        for l in range(1, wl.layers):
+            layer.step_rms(out, logits[l], pools[l], out, xbuf[l & 1], 1e-6)
+        rms_rescale_bf16(out, 1e-6, xbuf[wl.layers & 1])
 
     token()
     torch.cuda.synchronize()

@@ -278,6 +278,25 @@ MOE_API moe_status moe_decode_layer_mxfp4(const float* logits, const uint16_t* x
                                           int32_t* active, float* y_rows, float* out, void* workspace,
                                           size_t workspace_bytes, moe_stream_t stream);
 
+/*
+ * moe_decode_layer_rms_mxfp4 - the next layer of a batch-1 stack straight
+ * from the previous layer's output: x_next = moe_rms_rescale_bf16(y_prev)
+ * (T = 1), then moe_decode_layer_mxfp4(logits, x_next, ...); every output
+ * bit for bit as those two calls write it.  At the decode shape the rescale
+ * runs inside the gate/up launch (each block forms x itself with the
+ * rescale's arithmetic; block 0 writes x_next), so a stacked layer takes
+ * two launches.
+ *   y_prev [H] fp32 and x_next [H] bf16 out, both 16-byte aligned; eps >= 0;
+ *   out may be y_prev's own buffer; the other arguments as moe_decode_layer_mxfp4 takes
+ *   them (MOE_ERR_INVALID_ARG / MOE_ERR_WORKSPACE_TOO_SMALL likewise).
+ */
+MOE_API moe_status moe_decode_layer_rms_mxfp4(const float* logits, const float* y_prev, float eps,
+                                              uint16_t* x_next, int32_t k, const moe_mxfp4_weights* w,
+                                              int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                                              int32_t* sorted_rows, int32_t* row_pos, int32_t* active,
+                                              float* y_rows, float* out, void* workspace, size_t workspace_bytes,
+                                              moe_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

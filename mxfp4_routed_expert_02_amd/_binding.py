@@ -58,13 +58,15 @@ def lib():
                                                    ctypes.c_size_t, _P]
         L.moe_decode_layer_mxfp4.argtypes = [_P, _P, _I32, W, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                              _P]
+        L.moe_decode_layer_rms_mxfp4.argtypes = [_P, _P, ctypes.c_float, _P, _I32, W, _P, _P, _P, _P, _P, _P, _P,
+                                                 _P, _P, ctypes.c_size_t, _P]
         L.moe_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32, _I32]
         L.moe_workspace_bytes.restype = ctypes.c_size_t
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         for f in ("moe_route_topk", "moe_group_rows", "moe_expert_ffn_mxfp4", "moe_combine",
                   "moe_rms_rescale_bf16", "moe_router_logits", "moe_route_group_one", "moe_combine_rms_bf16",
-                  "moe_expert_ffn_combine_mxfp4", "moe_decode_layer_mxfp4"):
+                  "moe_expert_ffn_combine_mxfp4", "moe_decode_layer_mxfp4", "moe_decode_layer_rms_mxfp4"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -204,6 +206,24 @@ def decode_layer_mxfp4(logits: torch.Tensor, x: torch.Tensor, k: int, pool: Expe
         _dev(grp.row_pos, torch.int32, "row_pos"), _dev(grp.active, torch.int32, "active"),
         _dev(y_rows, torch.float32, "y_rows"), _dev(out, torch.float32, "out"),
         _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(x.device)))
+    return out
+
+
+def decode_layer_rms_mxfp4(logits: torch.Tensor, y_prev: torch.Tensor, eps: float, x_next: torch.Tensor, k: int,
+                           pool: ExpertPool, ids: torch.Tensor, weights: torch.Tensor, grp: Grouping,
+                           workspace: torch.Tensor, y_rows: torch.Tensor, out: torch.Tensor) -> torch.Tensor:
+    """The next stacked layer from the previous layer's output: y_prev [1, H] fp32 -> x_next [1, H] bf16 (its RMS
+    rescale), then the layer as decode_layer_mxfp4 on x_next; returns out."""
+    if logits.shape[0] != 1 or y_prev.shape[0] != 1:
+        raise ValueError("decode_layer_rms_mxfp4 takes one token")
+    _check("moe_decode_layer_rms_mxfp4", lib().moe_decode_layer_rms_mxfp4(
+        _dev(logits, torch.float32, "logits"), _dev(y_prev, torch.float32, "y_prev"), eps,
+        _dev(x_next.view(torch.int16), torch.int16, "x_next"), k, ctypes.byref(pool.weights),
+        _dev(ids, torch.int32, "ids"), _dev(weights, torch.float32, "weights"),
+        _dev(grp.expert_offsets, torch.int32, "expert_offsets"), _dev(grp.sorted_rows, torch.int32, "sorted_rows"),
+        _dev(grp.row_pos, torch.int32, "row_pos"), _dev(grp.active, torch.int32, "active"),
+        _dev(y_rows, torch.float32, "y_rows"), _dev(out, torch.float32, "out"),
+        _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(y_prev.device)))
     return out
 
 

@@ -59,8 +59,6 @@ __global__ __launch_bounds__(kThreads) void combine_scalar_kernel(const float* _
 // One block of 1024 threads per token: each thread keeps up to 4 float4 of
 // y in registers (H <= 16384), so y is read once; the sum of squares meets
 // in a wave butterfly and then across the 16 waves in LDS.
-constexpr int kRmsThreads = 1024;
-constexpr int kRmsVec = 4;  // float4 per thread
 
 __global__ __launch_bounds__(kRmsThreads) void rms_rescale_kernel(const float* __restrict__ y, int H, float eps,
                                                                   uint16_t* __restrict__ x_next) {
@@ -76,14 +74,14 @@ __global__ __launch_bounds__(kRmsThreads) void rms_rescale_kernel(const float* _
     v[i] = c < n4 ? yr[c] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   }
 #pragma unroll
-  for (int i = 0; i < kRmsVec; ++i) ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+  for (int i = 0; i < kRmsVec; ++i) ss += sumsq4(v[i]);
   ss = wave_sum(ss);
   if ((threadIdx.x & (MOE_WAVE - 1)) == 0) s_part[threadIdx.x / MOE_WAVE] = ss;
   __syncthreads();
   float tot = 0.0f;
 #pragma unroll
   for (int i = 0; i < kRmsThreads / MOE_WAVE; ++i) tot += s_part[i];
-  const float r = 1.0f / sqrtf(tot / (float)H + eps);
+  const float r = rms_factor(tot, H, eps);
   uint2* xo = (uint2*)(x_next + (int64_t)t * H);
 #pragma unroll
   for (int i = 0; i < kRmsVec; ++i) {
@@ -143,14 +141,14 @@ __global__ __launch_bounds__(kRmsThreads) void combine_rms_kernel(const float* _
     if (c < n4) orow[c] = v[i];
   }
 #pragma unroll
-  for (int i = 0; i < kRmsVec; ++i) ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+  for (int i = 0; i < kRmsVec; ++i) ss += sumsq4(v[i]);
   ss = wave_sum(ss);
   if ((threadIdx.x & (MOE_WAVE - 1)) == 0) s_part[threadIdx.x / MOE_WAVE] = ss;
   __syncthreads();
   float tot = 0.0f;
 #pragma unroll
   for (int i = 0; i < kRmsThreads / MOE_WAVE; ++i) tot += s_part[i];
-  const float r = 1.0f / sqrtf(tot / (float)H + eps);
+  const float r = rms_factor(tot, H, eps);
   uint2* xo = (uint2*)(x_next + (int64_t)t * H);
 #pragma unroll
   for (int i = 0; i < kRmsVec; ++i) {

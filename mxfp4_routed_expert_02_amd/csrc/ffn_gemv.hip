@@ -898,21 +898,46 @@ __global__ __launch_bounds__(kFThreads) void down_combine_one_kernel(
 // route + group kernel does.  The rest is gateup_gemv_one_kernel: the
 // activation loads go out before the top-k, the first weight loads as soon
 // as the expert is known.
-template <int J, int U, int NB, int C>
+//
+// RMS: the input is the previous layer's fp32 output y_prev; every block
+// forms x = bf16_rne(y_prev * rms factor) itself with the RMS rescale's
+// arithmetic and layout (this block's 256 threads stand in for its 1024,
+// four each, so the sums meet in the same order), and block 0 also writes
+// that x to x_next.
+template <int J, int U, int NB, int C, bool RMS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void route_gateup_one_kernel(
-    const float* __restrict__ logits, int E, int k, const uint16_t* __restrict__ x, moe_mxfp4_weights w,
-    float* __restrict__ h, int32_t* __restrict__ ids, float* __restrict__ topk_w, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ sorted_rows, int32_t* __restrict__ row_pos, int32_t* __restrict__ active,
-    int blocks_per_expert) {
+    const float* __restrict__ logits, int E, int k, const uint16_t* __restrict__ x, const float* __restrict__ y_prev,
+    float eps, uint16_t* __restrict__ x_next, moe_mxfp4_weights w, float* __restrict__ h, int32_t* __restrict__ ids,
+    float* __restrict__ topk_w, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_rows,
+    int32_t* __restrict__ row_pos, int32_t* __restrict__ active, int blocks_per_expert) {
   static_assert(kThreads == kRoute4Threads, "the top-k runs on the whole block");
   extern __shared__ uint4 s_x4[];  // [4][NB]
   __shared__ TopkLds s;
   static_assert(4 * NB > 3 * kThreads && 4 * NB <= 4 * kThreads, "x staging assumes 3..4 uint4 per thread");
-  const uint4* x4 = (const uint4*)x;
   const int tx = threadIdx.x;
-  const uint4 xs0 = x4[tx], xs1 = x4[tx + kThreads], xs2 = x4[tx + 2 * kThreads];
-  uint4 xs3 = make_uint4(0u, 0u, 0u, 0u);
-  if (tx + 3 * kThreads < 4 * NB) xs3 = x4[tx + 3 * kThreads];
+  // RMS: float4 i of stand-in thread m (thread tx + 256 m of the rescale's layout)
+  constexpr int kN4 = 8 * NB;                                  // float4 of a row
+  constexpr int kIV = (kN4 + kRmsThreads - 1) / kRmsThreads;  // float4 per stand-in thread, at most
+  constexpr int kStand = kRmsThreads / kThreads;
+  static_assert(kIV <= kRmsVec && kRmsThreads % kThreads == 0, "rescale layout");
+  uint4 xs0, xs1, xs2, xs3 = make_uint4(0u, 0u, 0u, 0u);
+  float4 yv[kStand][kIV];
+  if constexpr (RMS) {
+    const float4* y4 = (const float4*)y_prev;
+#pragma unroll
+    for (int m = 0; m < kStand; ++m)
+#pragma unroll
+      for (int i = 0; i < kIV; ++i) {
+        const int c = tx + kThreads * m + kRmsThreads * i;
+        yv[m][i] = c < kN4 ? y4[c] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      }
+  } else {
+    const uint4* x4 = (const uint4*)x;
+    xs0 = x4[tx];
+    xs1 = x4[tx + kThreads];
+    xs2 = x4[tx + 2 * kThreads];
+    if (tx + 3 * kThreads < 4 * NB) xs3 = x4[tx + 3 * kThreads];
+  }
   topk_block<C, true>(logits, E, k, s);
   if (blockIdx.x == 0) {
     if (tx < MOE_WAVE) {
@@ -969,11 +994,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   for (int j = 0; j < J; ++j)
 #pragma unroll
     for (int u = 0; u < U; ++u) load_chunk(it0, u, j, it0 < it1 ? 0u : kPastEnd);
-  auto stage = [&](int c, const uint4& v) { s_x4[(c & 3) * nb + (c >> 2)] = v; };
-  stage(tx, xs0);
-  stage(tx + kThreads, xs1);
-  stage(tx + 2 * kThreads, xs2);
-  if (tx + 3 * kThreads < 4 * NB) stage(tx + 3 * kThreads, xs3);
+  if constexpr (RMS) {
+    __shared__ float s_part[kRmsThreads / MOE_WAVE];
+#pragma unroll
+    for (int m = 0; m < kStand; ++m) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kIV; ++i) ss += sumsq4(yv[m][i]);  // the layout's later float4 are all zero
+      ss = wave_sum(ss);
+      if (lane == 0) s_part[wave + kWaves * m] = ss;
+    }
+    __syncthreads();
+    float tot = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kRmsThreads / MOE_WAVE; ++i) tot += s_part[i];
+    const float r = rms_factor(tot, H, eps);
+    uint2* sx2 = (uint2*)s_x4;
+#pragma unroll
+    for (int m = 0; m < kStand; ++m)
+#pragma unroll
+      for (int i = 0; i < kIV; ++i) {
+        const int c = tx + kThreads * m + kRmsThreads * i;  // float4 index = elements 4c .. 4c+3
+        if (c < kN4) {
+          const float4 v = yv[m][i];
+          const uint32_t lo = f32_to_bf16_rne_dev(v.x * r) | ((uint32_t)f32_to_bf16_rne_dev(v.y * r) << 16);
+          const uint32_t hi = f32_to_bf16_rne_dev(v.z * r) | ((uint32_t)f32_to_bf16_rne_dev(v.w * r) << 16);
+          const int c8 = c >> 1;  // staged 16-byte piece
+          sx2[2 * ((c8 & 3) * nb + (c8 >> 2)) + (c & 1)] = make_uint2(lo, hi);
+          if (blockIdx.x == 0) ((uint2*)x_next)[c] = make_uint2(lo, hi);
+        }
+      }
+  } else {
+    auto stage = [&](int c, const uint4& v) { s_x4[(c & 3) * nb + (c >> 2)] = v; };
+    stage(tx, xs0);
+    stage(tx + kThreads, xs1);
+    stage(tx + 2 * kThreads, xs2);
+    if (tx + 3 * kThreads < 4 * NB) stage(tx + 3 * kThreads, xs3);
+  }
   __syncthreads();
   for (int it = it0; it < it1; it += istep) {
     const uint32_t next_off = it + istep < it1 ? 0u : kPastEnd;
@@ -1299,10 +1356,10 @@ bool route_ffn_combine_one_ok(int E, int k, const moe_mxfp4_weights& w) {
   return w.hidden == 7168 && w.inter == 1536 && k <= kFMaxK && k <= E && E <= kRegExperts;
 }
 
-hipError_t launch_route_ffn_combine_one(const float* logits, int k, const uint16_t* x, const moe_mxfp4_weights& w,
-                                        int32_t* ids, float* topk_w, int32_t* offsets, int32_t* sorted_rows,
-                                        int32_t* row_pos, int32_t* active, float* y_rows, float* out, void* ws,
-                                        hipStream_t s) {
+hipError_t launch_route_ffn_combine_one(const float* logits, int k, const uint16_t* x, const float* y_prev,
+                                        float eps, uint16_t* x_next, const moe_mxfp4_weights& w, int32_t* ids,
+                                        float* topk_w, int32_t* offsets, int32_t* sorted_rows, int32_t* row_pos,
+                                        int32_t* active, float* y_rows, float* out, void* ws, hipStream_t s) {
   const int E = w.num_experts, H = w.hidden, I = w.inter;
   const GemvShape sg = gemv_shape(H >> 5, true);
   const int rows_it = (64 >> sg.lg) * sg.U, iters = (I + rows_it - 1) / rows_it;
@@ -1310,15 +1367,18 @@ hipError_t launch_route_ffn_combine_one(const float* logits, int k, const uint16
   const dim3 grid(k * gg.blocks_per_expert);
   float* hbuf = (float*)ws;
   const size_t lds = (size_t)H * 2;
-#define RG(C)                                                                                                    \
-  hipLaunchKernelGGL((route_gateup_one_kernel<7, kGateU224, 224, C>), grid, dim3(kThreads), lds, s, logits, E, k, \
-                     x, w, hbuf, ids, topk_w, offsets, sorted_rows, row_pos, active, gg.blocks_per_expert)
-  if (E <= 4 * MOE_WAVE * 2)
-    RG(2);
-  else if (E <= 4 * MOE_WAVE * 4)
-    RG(4);
-  else
-    RG(8);
+#define RG(C, RMS)                                                                                             \
+  hipLaunchKernelGGL((route_gateup_one_kernel<7, kGateU224, 224, C, RMS>), grid, dim3(kThreads), lds, s, logits, \
+                     E, k, x, y_prev, eps, x_next, w, hbuf, ids, topk_w, offsets, sorted_rows, row_pos, active,    \
+                     gg.blocks_per_expert)
+  const bool rms = y_prev != nullptr;
+  if (E <= 4 * MOE_WAVE * 2) {
+    if (rms) RG(2, true); else RG(2, false);
+  } else if (E <= 4 * MOE_WAVE * 4) {
+    if (rms) RG(4, true); else RG(4, false);
+  } else {
+    if (rms) RG(8, true); else RG(8, false);
+  }
 #undef RG
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;

@@ -192,8 +192,9 @@ moe_status moe_decode_layer_mxfp4(const float* logits, const uint16_t* x, int32_
   const hipStream_t s = (hipStream_t)stream;
   const int E = w->num_experts;
   if (moe::route_ffn_combine_one_ok(E, k, *w))
-    return from_hip(moe::launch_route_ffn_combine_one(logits, k, x, *w, topk_ids, topk_weights, expert_offsets,
-                                                      sorted_rows, row_pos, active, y_rows, out, workspace, s));
+    return from_hip(moe::launch_route_ffn_combine_one(logits, k, x, nullptr, 0.0f, nullptr, *w, topk_ids,
+                                                      topk_weights, expert_offsets, sorted_rows, row_pos, active,
+                                                      y_rows, out, workspace, s));
   hipError_t err;
   if (E <= 2048) {
     err = moe::launch_route_group_one(logits, E, k, topk_ids, topk_weights, expert_offsets, sorted_rows, row_pos,
@@ -206,6 +207,42 @@ moe_status moe_decode_layer_mxfp4(const float* logits, const uint16_t* x, int32_
   if (err != hipSuccess) return MOE_ERR_HIP;
   return from_hip(moe::launch_expert_ffn_combine(x, 1, k, *w, expert_offsets, sorted_rows, active, topk_weights,
                                                  row_pos, y_rows, out, workspace, s));
+}
+
+moe_status moe_decode_layer_rms_mxfp4(const float* logits, const float* y_prev, float eps, uint16_t* x_next,
+                                      int32_t k, const moe_mxfp4_weights* w, int32_t* topk_ids,
+                                      float* topk_weights, int32_t* expert_offsets, int32_t* sorted_rows,
+                                      int32_t* row_pos, int32_t* active, float* y_rows, float* out, void* workspace,
+                                      size_t workspace_bytes, moe_stream_t stream) {
+  if (!y_prev || !x_next || !aligned16(y_prev) || !aligned16(x_next) || !(eps >= 0.0f))
+    return MOE_ERR_INVALID_ARG;
+  if (!weights_ok(w)) return MOE_ERR_INVALID_ARG;
+  const int E = w->num_experts;
+  if (!moe::route_ffn_combine_one_ok(E, k, *w)) {
+    // the rescale, then the layer as moe_decode_layer_mxfp4 runs it
+    if (!logits || !topk_ids || !topk_weights || !expert_offsets || !sorted_rows || !row_pos || !active ||
+        !y_rows || !out || !workspace)
+      return MOE_ERR_INVALID_ARG;
+    if (k < 1 || k > MOE_MAX_TOPK || k > E || !aligned16(y_rows) || !aligned16(out) || !aligned16(workspace))
+      return MOE_ERR_INVALID_ARG;
+    if (workspace_bytes < moe::expert_ffn_workspace(1, k, E, w->hidden, w->inter)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    const moe_status d = check_device();
+    if (d != MOE_OK) return d;
+    if (moe::launch_rms_rescale(y_prev, 1, w->hidden, eps, x_next, (hipStream_t)stream) != hipSuccess)
+      return MOE_ERR_HIP;
+    return moe_decode_layer_mxfp4(logits, x_next, k, w, topk_ids, topk_weights, expert_offsets, sorted_rows, row_pos,
+                                  active, y_rows, out, workspace, workspace_bytes, stream);
+  }
+  if (!logits || !topk_ids || !topk_weights || !expert_offsets || !sorted_rows || !row_pos || !active || !y_rows ||
+      !out || !workspace)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(y_rows) || !aligned16(out) || !aligned16(workspace)) return MOE_ERR_INVALID_ARG;
+  if (workspace_bytes < moe::expert_ffn_workspace(1, k, E, w->hidden, w->inter)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  const moe_status d = check_device();
+  if (d != MOE_OK) return d;
+  return from_hip(moe::launch_route_ffn_combine_one(logits, k, nullptr, y_prev, eps, x_next, *w, topk_ids,
+                                                    topk_weights, expert_offsets, sorted_rows, row_pos, active,
+                                                    y_rows, out, workspace, (hipStream_t)stream));
 }
 
 moe_status moe_router_logits(const uint16_t* x_bf16, int32_t T, int32_t H, const float* w_router, int32_t E,

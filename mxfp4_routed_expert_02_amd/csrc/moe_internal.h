@@ -92,6 +92,16 @@ __device__ __forceinline__ uint32_t wave_max_u32_last(uint32_t v) {
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
+// The weightless RMS rescale's arithmetic, shared by every kernel that forms
+// it so that all give the same bits.  Layout: kRmsThreads threads, thread c
+// owning float4 c + kRmsThreads*i of the row; a thread's squares summed
+// float4 by float4 (sumsq4), then a wave butterfly (wave_sum), then the
+// kRmsThreads/64 wave sums in wave order; factor 1/sqrt(mean + eps).
+constexpr int kRmsThreads = 1024;
+constexpr int kRmsVec = 4;  // float4 per thread (H <= 16384)
+__device__ __forceinline__ float sumsq4(const float4& v) { return v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w; }
+__device__ __forceinline__ float rms_factor(float tot, int H, float eps) { return 1.0f / sqrtf(tot / (float)H + eps); }
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne_dev(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u));
@@ -114,10 +124,11 @@ hipError_t launch_expert_ffn(const uint16_t* x, int T, int k, const moe_mxfp4_we
                              hipStream_t s);
 size_t expert_ffn_workspace(int T, int k, int E, int H, int I);
 bool route_ffn_combine_one_ok(int E, int k, const moe_mxfp4_weights& w);
-hipError_t launch_route_ffn_combine_one(const float* logits, int k, const uint16_t* x, const moe_mxfp4_weights& w,
-                                        int32_t* ids, float* topk_w, int32_t* offsets, int32_t* sorted_rows,
-                                        int32_t* row_pos, int32_t* active, float* y_rows, float* out, void* ws,
-                                        hipStream_t s);
+// x from y_prev's RMS rescale (written to x_next) when y_prev is not null
+hipError_t launch_route_ffn_combine_one(const float* logits, int k, const uint16_t* x, const float* y_prev,
+                                        float eps, uint16_t* x_next, const moe_mxfp4_weights& w, int32_t* ids,
+                                        float* topk_w, int32_t* offsets, int32_t* sorted_rows, int32_t* row_pos,
+                                        int32_t* active, float* y_rows, float* out, void* ws, hipStream_t s);
 hipError_t launch_expert_ffn_combine(const uint16_t* x, int T, int k, const moe_mxfp4_weights& w,
                                      const int32_t* offsets, const int32_t* sorted_rows, const int32_t* active,
                                      const float* topk_w, const int32_t* row_pos, float* y_rows, float* out,

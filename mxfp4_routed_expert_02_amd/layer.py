@@ -80,3 +80,15 @@ class RoutedExpertLayer:
         self._route_group(logits, ids, w, grp)
         B.expert_ffn_mxfp4(x, self.k, pool, grp, self.workspace, y_rows)
         return B.combine_rms_bf16(y_rows, w, grp.row_pos, out, x_next, eps)
+
+    def step_rms(self, y_prev: torch.Tensor, logits: torch.Tensor, pool: B.ExpertPool, out: torch.Tensor,
+                 x_used: torch.Tensor, eps: float = 1e-6) -> torch.Tensor:
+        """One stacked layer fed by the previous layer's output: x_used [1, H]
+        bf16 = RMS rescale of y_prev [1, H] fp32, then the layer on it into
+        out [1, H] fp32 (out may be y_prev's own buffer).  One token only; at
+        the decode shape the rescale runs inside the gate/up launch."""
+        if y_prev.shape[0] != 1:
+            raise ValueError("step_rms takes one token")
+        ids, w, grp, y_rows, _ = self._views(1)
+        return B.decode_layer_rms_mxfp4(logits, y_prev, eps, x_used, self.k, pool, ids, w, grp, self.workspace,
+                                        y_rows, out)

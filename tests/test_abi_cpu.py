@@ -190,3 +190,22 @@ def test_decode_layer_rejects_bad_arguments(L):
     args = list(ok)
     args[13] = 16
     assert f(*args) == WS_SMALL
+
+
+def test_decode_layer_rms_rejects_bad_arguments(L):
+    big = 1 << 30
+    w = _weights()
+    f = L.moe_decode_layer_rms_mxfp4
+    ok = [FAKE, FAKE, ctypes.c_float(1e-6), FAKE, 2, ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+          FAKE, big, None]
+    for i in (0, 1, 3, 6, 7, 8, 9, 10, 11, 12, 13, 14):  # every pointer
+        args = list(ok)
+        args[i] = None
+        assert f(*args) == INVALID, i
+    for i, v in ((1, FAKE + 4), (3, FAKE + 8), (2, ctypes.c_float(-1.0)), (4, 0), (4, 9)):
+        args = list(ok)
+        args[i] = v
+        assert f(*args) == INVALID, (i, v)
+    args = list(ok)
+    args[15] = 16
+    assert f(*args) == WS_SMALL

@@ -194,3 +194,51 @@ def test_decode_layer_matches_calls(case):
     assert torch.equal(g1.active[:1 + k], g2.active[:1 + k]), "active differs"
     assert torch.equal(y1.view(torch.int32), y2.view(torch.int32)), "y_rows bits differ"
     assert torch.equal(out1.view(torch.int32), out2.view(torch.int32)), "out bits differ"
+
+
+# moe_decode_layer_rms_mxfp4 against moe_rms_rescale_bf16 + moe_decode_layer_mxfp4,
+# including the stack's use with out in y_prev's own buffer
+DECODE_RMS_CASES = [  # name, E, H, I, k, out aliases y_prev
+    ("E96_k16", 96, 7168, 1536, 16, False),
+    ("E896_k16_in_place", 896, 7168, 1536, 16, True),
+    ("E4096_separate", 4096, 7168, 1536, 16, False),
+    ("small_separate_in_place", 8, 256, 128, 2, True),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_RMS_CASES, ids=[c[0] for c in DECODE_RMS_CASES])
+def test_decode_layer_rms_matches_calls(case):
+    from mxfp4_routed_expert_02_amd import decode_layer_mxfp4, decode_layer_rms_mxfp4, workspace_bytes
+    from tests.gpu_common import device_pool
+
+    name, E, H, I, k, in_place = case
+    say(f"decode_layer_rms {name}: E={E} H={H} I={I} k={k} in_place={in_place}")
+    wl = synth.Workload(name, E=E, H=H, I=I, k=k, T=1, pool=42, sub=42)
+    pool = device_pool(wl)
+    y_prev = torch.from_numpy(synth.normal_f32(synth.key(0, 62), H, stddev=900.0).reshape(1, H)).to(DEV)
+    lg = torch.from_numpy(_logits(E, "normal", 70 + E % 3)).to(DEV)
+    ws = torch.empty(workspace_bytes(1, k, E, H, I), dtype=torch.uint8, device=DEV)
+    # separate calls
+    x1 = rms_rescale_bf16(y_prev, 1e-6)
+    ids1 = torch.empty((1, k), dtype=torch.int32, device=DEV)
+    w1 = torch.empty((1, k), dtype=torch.float32, device=DEV)
+    g1 = _grouping(E, k)
+    y1 = torch.empty((k, H), dtype=torch.float32, device=DEV)
+    out1 = torch.empty((1, H), dtype=torch.float32, device=DEV)
+    decode_layer_mxfp4(lg, x1, k, pool, ids1, w1, g1, ws, y1, out1)
+    # one call
+    x2 = torch.zeros((1, H), dtype=torch.bfloat16, device=DEV)
+    ids2 = torch.full((1, k), -7, dtype=torch.int32, device=DEV)
+    w2 = torch.full((1, k), float("nan"), dtype=torch.float32, device=DEV)
+    g2 = _grouping(E, k)
+    y2 = torch.full_like(y1, float("nan"))
+    yp = y_prev.clone()
+    out2 = yp if in_place else torch.full_like(out1, float("nan"))
+    decode_layer_rms_mxfp4(lg, yp, 1e-6, x2, k, pool, ids2, w2, g2, ws, y2, out2)
+    torch.cuda.synchronize()
+    assert torch.equal(x1.view(torch.int16), x2.view(torch.int16)), "x_next bits differ"
+    assert torch.equal(ids1, ids2) and torch.equal(w1.view(torch.int32), w2.view(torch.int32)), "routing differs"
+    for nm in ("expert_offsets", "sorted_rows", "row_pos"):
+        assert torch.equal(getattr(g1, nm), getattr(g2, nm)), nm
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32)), "y_rows bits differ"
+    assert torch.equal(out1.view(torch.int32), out2.view(torch.int32)), "out bits differ"
