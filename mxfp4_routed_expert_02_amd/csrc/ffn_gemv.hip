@@ -889,56 +889,56 @@ __global__ __launch_bounds__(kFThreads) void down_combine_one_kernel(
   }
 }
 
-// One token routed inside the gate/up launch: every block first runs the
-// token's four-wave top-k (the routing kernels' device code, so the picks are
-// theirs bit for bit) and takes the expert of its slot, the slot-th smallest
-// picked id (the active list the grouping writes; the picks are distinct, so
-// that expert's one row sits at sorted position `slot`).  Block 0 also
-// writes the routing weights and the grouping exactly as the fused
-// route + group kernel does.  The rest is gateup_gemv_one_kernel: the
+// One token routed inside the gate/up launch, in blocks of 16 waves (one
+// block per CU at 4 waves per SIMD): the first four waves run the token's
+// four-wave top-k (the routing kernels' device code, so the picks are theirs
+// bit for bit; one top-k per CU keeps its VALU work off the other waves'
+// SIMD time) while the others wait, then every wave takes the expert of the
+// block's slot, the slot-th smallest picked id (the active list the
+// grouping writes; the picks are distinct, so that expert's one row sits at
+// sorted position `slot`).  The blocks also write the routing weights and
+// the grouping, equal to what the fused route + group kernel writes.  The
+// rest is gateup_gemv_one_kernel's lane layout and arithmetic: the
 // activation loads go out before the top-k, the first weight loads as soon
-// as the expert is known.
+// as the expert is known, rolling prefetch, round-robin row iterations.
 //
 // RMS: the input is the previous layer's fp32 output y_prev; every block
 // forms x = bf16_rne(y_prev * rms factor) itself with the RMS rescale's
-// arithmetic and layout (this block's 256 threads stand in for its 1024,
-// four each, so the sums meet in the same order), and block 0 also writes
-// that x to x_next.
+// arithmetic and thread layout (its 1024 threads are the rescale's), and
+// block 0 also writes that x to x_next.
+constexpr int kRGThreads = 1024;
+constexpr int kRGWaves = kRGThreads / MOE_WAVE;
+
 template <int J, int U, int NB, int C, bool RMS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void route_gateup_one_kernel(
+__global__ __launch_bounds__(kRGThreads) void route_gateup_one_kernel(
     const float* __restrict__ logits, int E, int k, const uint16_t* __restrict__ x, const float* __restrict__ y_prev,
     float eps, uint16_t* __restrict__ x_next, moe_mxfp4_weights w, float* __restrict__ h, int32_t* __restrict__ ids,
     float* __restrict__ topk_w, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_rows,
     int32_t* __restrict__ row_pos, int32_t* __restrict__ active, int blocks_per_expert) {
-  static_assert(kThreads == kRoute4Threads, "the top-k runs on the whole block");
+  static_assert(kRGThreads == kRmsThreads, "the block is the rescale's layout");
   extern __shared__ uint4 s_x4[];  // [4][NB]
   __shared__ TopkLds s;
-  static_assert(4 * NB > 3 * kThreads && 4 * NB <= 4 * kThreads, "x staging assumes 3..4 uint4 per thread");
+  constexpr int kN4 = 8 * NB;  // float4 (and half-uint4) of a row
+  static_assert(4 * NB <= kRGThreads && kN4 <= kRmsVec * kRmsThreads, "x staging layout");
+  constexpr int kIV = (kN4 + kRmsThreads - 1) / kRmsThreads;  // float4 per thread in the rescale's layout
   const int tx = threadIdx.x;
-  // RMS: float4 i of stand-in thread m (thread tx + 256 m of the rescale's layout)
-  constexpr int kN4 = 8 * NB;                                  // float4 of a row
-  constexpr int kIV = (kN4 + kRmsThreads - 1) / kRmsThreads;  // float4 per stand-in thread, at most
-  constexpr int kStand = kRmsThreads / kThreads;
-  static_assert(kIV <= kRmsVec && kRmsThreads % kThreads == 0, "rescale layout");
-  uint4 xs0, xs1, xs2, xs3 = make_uint4(0u, 0u, 0u, 0u);
-  float4 yv[kStand][kIV];
+  uint4 xs = make_uint4(0u, 0u, 0u, 0u);
+  float4 yv[kIV];
   if constexpr (RMS) {
     const float4* y4 = (const float4*)y_prev;
 #pragma unroll
-    for (int m = 0; m < kStand; ++m)
-#pragma unroll
-      for (int i = 0; i < kIV; ++i) {
-        const int c = tx + kThreads * m + kRmsThreads * i;
-        yv[m][i] = c < kN4 ? y4[c] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      }
+    for (int i = 0; i < kIV; ++i) {
+      const int c = tx + kRmsThreads * i;
+      yv[i] = c < kN4 ? y4[c] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
   } else {
-    const uint4* x4 = (const uint4*)x;
-    xs0 = x4[tx];
-    xs1 = x4[tx + kThreads];
-    xs2 = x4[tx + 2 * kThreads];
-    if (tx + 3 * kThreads < 4 * NB) xs3 = x4[tx + 3 * kThreads];
+    if (tx < 4 * NB) xs = ((const uint4*)x)[tx];
   }
-  topk_block<C, true>(logits, E, k, s);
+  topk_block<C, false>(logits, E, k, s);
+  // routing and grouping outputs (the picks are distinct: expert e's offset
+  // is the number of picks below e, a pick's sorted place the number of picks
+  // below its id); block 0 writes the per-pick ones, and the E+1 offsets are
+  // spread over the blocks so that no block's weight stream starts late
   if (blockIdx.x == 0) {
     if (tx < MOE_WAVE) {
       int id;
@@ -947,11 +947,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         ids[tx] = id;
         topk_w[tx] = wv;
       }
-    } else if (k <= 16) {
-      group_one<4>(s, E, k, offsets, sorted_rows, row_pos, active);
-    } else {
-      group_one<8>(s, E, k, offsets, sorted_rows, row_pos, active);
+    } else if (tx < MOE_WAVE + k) {
+      const int t = tx - MOE_WAVE, pid = s.pick_id[t];
+      int r = 0;
+      for (int i = 0; i < k; ++i) r += s.pick_id[i] < pid;
+      sorted_rows[r] = t;
+      row_pos[t] = r;
+      active[1 + r] = pid;
+      if (t == 0) active[0] = k;
     }
+  }
+  for (int e = blockIdx.x + (int)gridDim.x * tx; e <= E; e += (int)gridDim.x * kRGThreads) {
+    int r = 0;
+    for (int i = 0; i < k; ++i) r += s.pick_id[i] < e;
+    offsets[e] = r;
   }
   const int slot = blockIdx.x / blocks_per_expert;
   if (slot >= k) return;
@@ -970,8 +979,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int I = w.inter;
   const int li = lane & (G - 1), gi = lane >> lg;
   const int total_iters = (I + rows_it - 1) / rows_it;
-  const int it0 = (blockIdx.x % blocks_per_expert) * kWaves + wave;
-  const int istep = blocks_per_expert * kWaves;
+  const int it0 = (blockIdx.x % blocks_per_expert) * kRGWaves + wave;
+  const int istep = blocks_per_expert * kRGWaves;
   const int it1 = total_iters;
   constexpr uint32_t qrow = (uint32_t)H >> 1;
   const int64_t eo = (int64_t)e * w.expert_stride;
@@ -996,14 +1005,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int u = 0; u < U; ++u) load_chunk(it0, u, j, it0 < it1 ? 0u : kPastEnd);
   if constexpr (RMS) {
     __shared__ float s_part[kRmsThreads / MOE_WAVE];
+    float ss = 0.0f;
 #pragma unroll
-    for (int m = 0; m < kStand; ++m) {
-      float ss = 0.0f;
-#pragma unroll
-      for (int i = 0; i < kIV; ++i) ss += sumsq4(yv[m][i]);  // the layout's later float4 are all zero
-      ss = wave_sum(ss);
-      if (lane == 0) s_part[wave + kWaves * m] = ss;
-    }
+    for (int i = 0; i < kIV; ++i) ss += sumsq4(yv[i]);  // the layout's later float4 are all zero
+    ss = wave_sum(ss);
+    if (lane == 0) s_part[wave] = ss;
     __syncthreads();
     float tot = 0.0f;
 #pragma unroll
@@ -1011,25 +1017,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const float r = rms_factor(tot, H, eps);
     uint2* sx2 = (uint2*)s_x4;
 #pragma unroll
-    for (int m = 0; m < kStand; ++m)
-#pragma unroll
-      for (int i = 0; i < kIV; ++i) {
-        const int c = tx + kThreads * m + kRmsThreads * i;  // float4 index = elements 4c .. 4c+3
-        if (c < kN4) {
-          const float4 v = yv[m][i];
-          const uint32_t lo = f32_to_bf16_rne_dev(v.x * r) | ((uint32_t)f32_to_bf16_rne_dev(v.y * r) << 16);
-          const uint32_t hi = f32_to_bf16_rne_dev(v.z * r) | ((uint32_t)f32_to_bf16_rne_dev(v.w * r) << 16);
-          const int c8 = c >> 1;  // staged 16-byte piece
-          sx2[2 * ((c8 & 3) * nb + (c8 >> 2)) + (c & 1)] = make_uint2(lo, hi);
-          if (blockIdx.x == 0) ((uint2*)x_next)[c] = make_uint2(lo, hi);
-        }
+    for (int i = 0; i < kIV; ++i) {
+      const int c = tx + kRmsThreads * i;  // float4 index = elements 4c .. 4c+3
+      if (c < kN4) {
+        const float4 v = yv[i];
+        const uint32_t lo = f32_to_bf16_rne_dev(v.x * r) | ((uint32_t)f32_to_bf16_rne_dev(v.y * r) << 16);
+        const uint32_t hi = f32_to_bf16_rne_dev(v.z * r) | ((uint32_t)f32_to_bf16_rne_dev(v.w * r) << 16);
+        const int c8 = c >> 1;  // staged 16-byte piece
+        sx2[2 * ((c8 & 3) * nb + (c8 >> 2)) + (c & 1)] = make_uint2(lo, hi);
+        if (blockIdx.x == 0) ((uint2*)x_next)[c] = make_uint2(lo, hi);
       }
+    }
   } else {
-    auto stage = [&](int c, const uint4& v) { s_x4[(c & 3) * nb + (c >> 2)] = v; };
-    stage(tx, xs0);
-    stage(tx + kThreads, xs1);
-    stage(tx + 2 * kThreads, xs2);
-    if (tx + 3 * kThreads < 4 * NB) stage(tx + 3 * kThreads, xs3);
+    if (tx < 4 * NB) s_x4[(tx & 3) * nb + (tx >> 2)] = xs;
   }
   __syncthreads();
   for (int it = it0; it < it1; it += istep) {
@@ -1363,14 +1363,16 @@ hipError_t launch_route_ffn_combine_one(const float* logits, int k, const uint16
   const int E = w.num_experts, H = w.hidden, I = w.inter;
   const GemvShape sg = gemv_shape(H >> 5, true);
   const int rows_it = (64 >> sg.lg) * sg.U, iters = (I + rows_it - 1) / rows_it;
+  // the one-token gate/up grid (4 waves per SIMD) in blocks of 16 waves
   const GemvGrid gg = gemv_grid(iters, k, 4);
-  const dim3 grid(k * gg.blocks_per_expert);
+  const int bpe = (iters + kRGWaves * gg.ipw - 1) / (kRGWaves * gg.ipw);
+  const dim3 grid(k * bpe);
   float* hbuf = (float*)ws;
   const size_t lds = (size_t)H * 2;
 #define RG(C, RMS)                                                                                             \
-  hipLaunchKernelGGL((route_gateup_one_kernel<7, kGateU224, 224, C, RMS>), grid, dim3(kThreads), lds, s, logits, \
-                     E, k, x, y_prev, eps, x_next, w, hbuf, ids, topk_w, offsets, sorted_rows, row_pos, active,    \
-                     gg.blocks_per_expert)
+  hipLaunchKernelGGL((route_gateup_one_kernel<7, kGateU224, 224, C, RMS>), grid, dim3(kRGThreads), lds, s,      \
+                     logits, E, k, x, y_prev, eps, x_next, w, hbuf, ids, topk_w, offsets, sorted_rows, row_pos,     \
+                     active, bpe)
   const bool rms = y_prev != nullptr;
   if (E <= 4 * MOE_WAVE * 2) {
     if (rms) RG(2, true); else RG(2, false);

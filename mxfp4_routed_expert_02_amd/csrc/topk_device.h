@@ -120,8 +120,9 @@ __device__ __forceinline__ int merge_rank(const TopkLds& s, int wave, int lane, 
          count_above<KQ>(s.key + o2 * kList, ck - (o2 < wave ? 1u : 0u));
 }
 
-// Top-k of one token's logits row by a block of 4 waves.  Every thread must
-// call it (it holds three block barriers); on return s.pick_key/pick_id
+// Top-k of one token's logits row by the first 4 waves of a block (waves
+// past the fourth hold no expert and only meet the barriers).  Every thread
+// must call it (it holds three block barriers); on return s.pick_key/pick_id
 // [0..k) hold the picks in rank order (pick_id padded with INT_MAX up to
 // kList) and, with BITS, s.bits marks the picked experts.
 template <int C, bool BITS>
@@ -160,9 +161,9 @@ __device__ __forceinline__ void topk_block(const float* __restrict__ row, int E,
   if (wave < n_waves)
     for (; j < k; ++j)
       if (wave_round<C>(L, lane, j, tau, list_key, list_id) < tau) break;
-  if (lane >= j && lane < kList) list_key[lane] = 0u;
+  if (wave < 4 && lane >= j && lane < kList) list_key[lane] = 0u;
   __syncthreads();
-  if (lane < k) {
+  if (wave < 4 && lane < k) {
     const uint32_t ck = list_key[lane];
     if (ck != 0u) {
       const int rank = k <= 16 ? merge_rank<4>(s, wave, lane, ck) : merge_rank<8>(s, wave, lane, ck);
