@@ -131,11 +131,17 @@ __device__ __forceinline__ void topk_block(const float* __restrict__ row, int E,
   const int lane = threadIdx.x & (MOE_WAVE - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / MOE_WAVE);  // uniform: wave branches
   const int base = wave * Q + lane * C;
+  // every load unconditional (slots past E re-read the last logit and are
+  // masked below), so the lane's C loads are in flight together instead of
+  // one round trip each
+  float lv[C];
+#pragma unroll
+  for (int i = 0; i < C; ++i) lv[i] = row[min(base + i, E - 1)];
   uint64_t v[C];
 #pragma unroll
   for (int i = 0; i < C; ++i) {
     const int e = base + i;
-    v[i] = pick_word(e < E ? order_key(row[e]) : 0u, e);
+    v[i] = pick_word(e < E ? order_key(lv[i]) : 0u, e);
   }
   if (wave == 0 && lane >= k && lane < kList) s.pick_id[lane] = INT_MAX;
   if (BITS)
