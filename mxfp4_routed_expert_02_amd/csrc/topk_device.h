@@ -18,8 +18,9 @@ __device__ __forceinline__ uint32_t order_key(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Four-wave top-k: wave w holds the keys of experts [w*Q, w*Q + Q),
-// Q = 64*C, lane l those of experts w*Q + l*C + i.
+// Four-wave top-k: wave w holds the keys of experts [w*Qw, w*Qw + Qw),
+// Qw = ceil(E/4) (an even split keeps the waves' thresholds alike, so few
+// rounds follow the first ones), lane l those of experts w*Qw + l*C + i.
 //   1. Each lane sorts its C experts by (key descending, id ascending).
 //   2. Each wave takes picks in rounds; a round only looks at the lane
 //      heads: the wave maximum of the head keys, the lowest lane holding it
@@ -127,10 +128,10 @@ __device__ __forceinline__ int merge_rank(const TopkLds& s, int wave, int lane, 
 // kList) and, with BITS, s.bits marks the picked experts.
 template <int C, bool BITS>
 __device__ __forceinline__ void topk_block(const float* __restrict__ row, int E, int k, TopkLds& s) {
-  constexpr int Q = MOE_WAVE * C;
+  const int Qw = (E + 3) / 4;  // experts per wave (at most 64*C), contiguous ranges
   const int lane = threadIdx.x & (MOE_WAVE - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / MOE_WAVE);  // uniform: wave branches
-  const int base = wave * Q + lane * C;
+  const int base = wave * Qw + lane * C;
   // every load unconditional (slots past E re-read the last logit and are
   // masked below), so the lane's C loads are in flight together instead of
   // one round trip each
@@ -141,7 +142,7 @@ __device__ __forceinline__ void topk_block(const float* __restrict__ row, int E,
 #pragma unroll
   for (int i = 0; i < C; ++i) {
     const int e = base + i;
-    v[i] = pick_word(e < E ? order_key(lv[i]) : 0u, e);
+    v[i] = pick_word(lane * C + i < Qw && e < E ? order_key(lv[i]) : 0u, e);
   }
   if (wave == 0 && lane >= k && lane < kList) s.pick_id[lane] = INT_MAX;
   if (BITS)
@@ -153,7 +154,7 @@ __device__ __forceinline__ void topk_block(const float* __restrict__ row, int E,
     L.kh[i] = (uint32_t)(v[i] >> 32);
     L.ki[i] = (int32_t)~(uint32_t)v[i];
   }
-  const int n_waves = min(4, (E + Q - 1) / Q);  // waves holding an expert
+  const int n_waves = min(4, (E + Qw - 1) / Qw);  // waves holding an expert
   const int R = min(k, (k + n_waves - 1) / n_waves);
   uint32_t* list_key = s.key + wave * kList;
   int32_t* list_id = s.id + wave * kList;
