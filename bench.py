@@ -238,6 +238,7 @@ def main():
         res["prefill4096"] = prefill_side(dev, pool, args.seed, max(2, args.prefill_reps // 4), "prefill4096")
     if args.side_reps > 0:
         res["router"] = router_side(dev, args.seed, args.side_reps)
+        res["decode896_tp8_share"] = tp8_side(dev, args.seed, args.side_reps)
     if args.stack_reps > 0:
         res["stack92"] = stack_side(dev, args.seed, args.stack_reps)
 
@@ -293,6 +294,42 @@ def verify_side(dev, pool, seed, reps):
     log(f"verify8: {np.median(each):.1f} us/layer (median), {gbs:.0f} GB/s over {np.mean(uniq):.1f} unique experts")
     return {"us_per_layer": pct(each), "weight_gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "unique_experts_mean": round(float(np.mean(uniq)), 2), "variants": V}
+
+
+def tp8_side(dev, seed, reps):
+    """One GPU's share of decode896 under an 8-way split of every expert's I
+    (the layer at I = 192): layer time and weight GB/s of that share."""
+    import numpy as np
+    import torch
+
+    from mxfp4_routed_expert_02_amd import ExpertPool, synth
+    from mxfp4_routed_expert_02_amd.layer import RoutedExpertLayer
+
+    wl = synth.WORKLOADS["decode896_tp8"]
+    pool = ExpertPool(synth.device_pool_slabs(seed, wl.pool, 0, wl.E, wl.H, wl.I, dev), wl.H, wl.I)
+    V = 64
+    xs = [torch.from_numpy(synth.activations_bf16(seed, wl, variant=v).view(np.int16)).to(dev).view(torch.bfloat16)
+          for v in range(V)]
+    ls = [torch.from_numpy(synth.router_logits(seed, wl, variant=v)).to(dev) for v in range(V)]
+    layer = RoutedExpertLayer(wl.E, wl.H, wl.I, wl.k, wl.T, dev)
+    for v in range(V):
+        layer(xs[v], ls[v], pool)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(reps):
+        layer(xs[i % V], ls[i % V], pool)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    share_bytes = wl.k * synth.slab_bytes(wl.H, wl.I)
+    gbs = share_bytes / (us * 1e-6) / 1e9
+    log(f"decode896 tp8 share (I {wl.I}): {us:.1f} us/layer, {gbs:.0f} GB/s of its {share_bytes} weight bytes")
+    del pool
+    torch.cuda.empty_cache()
+    return {"us_per_layer": round(us, 2), "weight_bytes": share_bytes, "weight_gbs": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def router_side(dev, seed, reps):

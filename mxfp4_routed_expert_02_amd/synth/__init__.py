@@ -147,6 +147,9 @@ WORKLOADS: Dict[str, Workload] = {
     # auxiliary dense case: every token routes to the same 16 experts (512 rows each)
     "prefill_dense": Workload("prefill_dense", E=896, H=7168, I=1536, k=16, T=512, logits="dense16", pool=0,
                               sub=6),
+    # one GPU's share of decode896 when every expert's I = 1536 is split 8 ways
+    # (gate/up rows and the matching down columns): the same layer at I = 192
+    "decode896_tp8": Workload("decode896_tp8", E=896, H=7168, I=192, k=16, T=1, pool=8, sub=8),
 }
 
 

@@ -270,3 +270,14 @@ def test_decode896_repeated_ids(pool896):
     hpool = host_pool_subset(wl, ids_np.reshape(-1))
     ref = oracle.token_layers_parallel(x_np, ids_np, w_np, hpool, [0], nthreads=NTH)
     assert_close(out.cpu().numpy(), ref, "out")
+
+
+def test_decode896_tp8_share():
+    """One GPU's share of decode896 under an 8-way split of I (the same
+    layer at I = 192, 896 experts): every output against the oracle."""
+    wl = synth.WORKLOADS["decode896_tp8"]
+    say("case decode896_tp8")
+    pool = device_pool(wl)
+    _full_case(wl, pool)
+    del pool
+    torch.cuda.empty_cache()
