@@ -95,8 +95,9 @@ def copy_probe(mib):
 
 
 def stream_read_gbs(dev, gib=4, reps=5):
-    """The box's achievable read bandwidth: a plain streaming-read kernel over
-    a `gib` GiB buffer (synth library), median of `reps` event-timed runs."""
+    """The box's achievable read bandwidth: a plain streaming-read kernel
+    (non-temporal loads, 512 blocks) over a `gib` GiB buffer (synth library),
+    median of `reps` event-timed runs."""
     import numpy as np
     import torch
 
@@ -105,7 +106,7 @@ def stream_read_gbs(dev, gib=4, reps=5):
     L = synth.gpu_lib()
     nbytes = gib << 30
     buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    blocks = 1024
+    blocks = 512
     out = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
 

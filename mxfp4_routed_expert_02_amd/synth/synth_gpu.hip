@@ -52,18 +52,23 @@ __global__ void slab_kernel(uint64_t seed, int pool, int layer, int e0, uint64_t
 
 // Streaming-read probe, measurement context for the bandwidth-bound kernels:
 // every 16-byte word of the buffer is read once by grid-stride loads (four
-// per thread in flight), each thread writing the XOR of what it read so
+// per thread in flight) with the non-temporal cache policy (the fastest
+// plain stream on this GPU), each thread writing the XOR of what it read so
 // the loads are live.  It draws and computes nothing of the layer.
-__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ src, uint64_t n16,
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4_t* __restrict__ src, uint64_t n16,
                                                           uint32_t* __restrict__ out) {
   const uint64_t step = (uint64_t)gridDim.x * 256 * 4;
   uint32_t acc = 0u;
   for (uint64_t i = (uint64_t)blockIdx.x * 256 * 4 + threadIdx.x; i < n16; i += step) {
-    uint4 v[4];
+    u32x4_t v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = i + 256u * u < n16 ? src[i + 256u * u] : make_uint4(0u, 0u, 0u, 0u);
+    for (int u = 0; u < 4; ++u) {
+      v[u] = u32x4_t{0u, 0u, 0u, 0u};
+      if (i + 256u * u < n16) v[u] = __builtin_nontemporal_load(src + i + 256u * u);
+    }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    for (int u = 0; u < 4; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
   out[(uint64_t)blockIdx.x * 256 + threadIdx.x] = acc;
 }
@@ -78,7 +83,7 @@ extern "C" {
 __attribute__((visibility("default"))) int synth_stream_read(const void* src, uint64_t bytes, void* out, int blocks,
                                                              void* stream) {
   if (!src || !out || blocks < 1 || (bytes & 15) || ((uintptr_t)src & 15)) return -1;
-  hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const uint4*)src,
+  hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const u32x4_t*)src,
                      bytes / 16, (uint32_t*)out);
   const hipError_t err = hipGetLastError();
   return err == hipSuccess ? 0 : (int)err;
