@@ -602,7 +602,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
 // One token, rows of a compile-time NB blocks (the decode shape): the lane
 // layout and arithmetic of the MT = 1 kernels above, one work item per
-// block, with two changes to keep HBM busy:
+// block, with three changes to keep HBM busy:
 //  * every routed row belongs to token 0, so nothing the first weight loads
 //    need waits on the routing beyond the expert id (gate/up issues its
 //    activation loads before any routing read); the offsets are read while
@@ -898,8 +898,8 @@ __global__ __launch_bounds__(kFThreads) void down_combine_one_kernel(
 // One token routed inside the gate/up launch, in blocks of 16 waves (one
 // block per CU at 4 waves per SIMD): the first four waves run the token's
 // four-wave top-k (the routing kernels' device code, so the picks are theirs
-// bit for bit; one top-k per CU keeps its VALU work off the other waves'
-// SIMD time) while the others wait, then every wave takes the expert of the
+// bit for bit; one top-k per CU rather than one per 4-wave block) while the
+// others wait, then every wave takes the expert of the
 // block's slot, the slot-th smallest picked id (the active list the
 // grouping writes; the picks are distinct, so that expert's one row sits at
 // sorted position `slot`).  The blocks also write the routing weights and
