@@ -27,6 +27,7 @@ constexpr int kRowsPerBlock = 16;
 // 48-block (I = 1536) rows; the host grid uses the same constants
 constexpr int kGateU224 = 1;
 constexpr int kDownU48 = 2;
+constexpr int kDownOneU48 = 1;  // the one-token down kernel (measured faster at 4 waves per SIMD)
 
 // 16 bytes = 32 E2M1 codes -> 16 bf16 pairs; pair j holds elements 2j, 2j+1.
 __device__ __forceinline__ void dequant_bf16(const uint4 q, bf16x2_t (&v)[16]) {
@@ -1292,15 +1293,16 @@ hipError_t expert_ffn_impl(const uint16_t* x, int T, int k, const moe_mxfp4_weig
 
   if (reg_d) {
     const int rows_it = (64 >> sd.lg) * sd.U, iters = (H + rows_it - 1) / rows_it;
-    if (T == 1) {
-      // the one-token down kernel holds 2 waves per SIMD (188 VGPRs)
+    if (T == 1 && I == 1536) {
+      // the one-token down kernel: one row group per iteration (94 VGPRs),
+      // a grid for 4 waves per SIMD
+      const int rows_one = (64 >> sd.lg) * kDownOneU48, iters_one = (H + rows_one - 1) / rows_one;
+      const GemvGrid gd = gemv_grid(iters_one, max_active, 4);
+      hipLaunchKernelGGL((down_gemv_one_kernel<3, kDownOneU48, 48>), dim3(max_active * gd.blocks_per_expert),
+                         dim3(kThreads), (size_t)I * 4, s, hbuf, w, offsets, active, y_rows, gd.blocks_per_expert);
+    } else if (T == 1) {
       const GemvGrid gd = gemv_grid(iters, max_active, 2);
-      if (I == 1536)
-        hipLaunchKernelGGL((down_gemv_one_kernel<3, kDownU48, 48>), dim3(max_active * gd.blocks_per_expert),
-                           dim3(kThreads), (size_t)I * 4, s, hbuf, w, offsets, active, y_rows,
-                           gd.blocks_per_expert);
-      else
-        down_reg<1>(ga, sd, gd, dim3(max_active * gd.blocks_per_expert), nullptr, 1, INT32_MAX);
+      down_reg<1>(ga, sd, gd, dim3(max_active * gd.blocks_per_expert), nullptr, 1, INT32_MAX);
     } else {
       const GemvGrid gd = multi_grid(iters);
       down_reg<1>(ga, sd, gd, multi(n1_max, gd), l1, 1, 1);
