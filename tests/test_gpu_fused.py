@@ -242,3 +242,53 @@ def test_decode_layer_rms_matches_calls(case):
         assert torch.equal(getattr(g1, nm), getattr(g2, nm)), nm
     assert torch.equal(y1.view(torch.int32), y2.view(torch.int32)), "y_rows bits differ"
     assert torch.equal(out1.view(torch.int32), out2.view(torch.int32)), "out bits differ"
+
+
+def test_decode_layer_graph_replays_match_eager():
+    """A stacked step (moe_decode_layer_rms_mxfp4 then moe_decode_layer_mxfp4)
+    captured in a HIP graph: every replay, with eager work and
+    synchronizations between them, gives the eager bits."""
+    from mxfp4_routed_expert_02_amd import decode_layer_mxfp4, decode_layer_rms_mxfp4, workspace_bytes
+    from tests.gpu_common import device_pool
+
+    E, H, I, k = 96, 7168, 1536, 16
+    wl = synth.Workload("graph", E=E, H=H, I=I, k=k, T=1, pool=43, sub=43)
+    pool = device_pool(wl)
+    y_prev = torch.from_numpy(synth.normal_f32(synth.key(0, 63), H, stddev=900.0).reshape(1, H)).to(DEV)
+    lg0 = torch.from_numpy(_logits(E, "normal", 80)).to(DEV)
+    lg1 = torch.from_numpy(_logits(E, "normal", 81)).to(DEV)
+    ws = torch.empty(workspace_bytes(1, k, E, H, I), dtype=torch.uint8, device=DEV)
+    ids = torch.empty((1, k), dtype=torch.int32, device=DEV)
+    w = torch.empty((1, k), dtype=torch.float32, device=DEV)
+    g = _grouping(E, k)
+    y = torch.empty((k, H), dtype=torch.float32, device=DEV)
+    x1 = torch.empty((1, H), dtype=torch.bfloat16, device=DEV)
+    out1 = torch.empty((1, H), dtype=torch.float32, device=DEV)
+    out2 = torch.empty((1, H), dtype=torch.float32, device=DEV)
+
+    def step():
+        decode_layer_rms_mxfp4(lg0, y_prev, 1e-6, x1, k, pool, ids, w, g, ws, y, out1)
+        decode_layer_mxfp4(lg1, x1, k, pool, ids, w, g, ws, y, out2)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (x1.clone(), out1.clone(), out2.clone(), ids.clone())
+    stream = torch.cuda.Stream(DEV)
+    stream.wait_stream(torch.cuda.current_stream(DEV))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            step()
+    torch.cuda.current_stream(DEV).wait_stream(stream)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in (x1, out1, out2):
+            t.zero_()  # eager work between replays
+        ids.fill_(-1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(x1.view(torch.int16), ref[0].view(torch.int16)), f"replay {rep}: x_next"
+        assert torch.equal(out1.view(torch.int32), ref[1].view(torch.int32)), f"replay {rep}: out of layer 1"
+        assert torch.equal(out2.view(torch.int32), ref[2].view(torch.int32)), f"replay {rep}: out of layer 2"
+        assert torch.equal(ids, ref[3]), f"replay {rep}: ids"
