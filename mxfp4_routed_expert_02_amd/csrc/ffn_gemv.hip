@@ -942,6 +942,11 @@ __global__ __launch_bounds__(kRGThreads) void route_gateup_one_kernel(
     if (tx < 4 * NB) xs = ((const uint4*)x)[tx];
   }
   topk_block<C, false>(logits, E, k, s);
+  // the k <= 16 pick ids (padded with INT_MAX) in registers: 4 LDS reads
+  static_assert(kFMaxK == 16, "four int4 of pick ids");
+  int4 pv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pv[i] = ((const int4*)s.pick_id)[i];
   // routing and grouping outputs (the picks are distinct: expert e's offset
   // is the number of picks below e, a pick's sorted place the number of picks
   // below its id); block 0 writes the per-pick ones, and the E+1 offsets are
@@ -956,19 +961,15 @@ __global__ __launch_bounds__(kRGThreads) void route_gateup_one_kernel(
       }
     } else if (tx < MOE_WAVE + k) {
       const int t = tx - MOE_WAVE, pid = s.pick_id[t];
-      int r = 0;
-      for (int i = 0; i < k; ++i) r += s.pick_id[i] < pid;
+      const int r = picks_below<4>(pv, pid);
       sorted_rows[r] = t;
       row_pos[t] = r;
       active[1 + r] = pid;
       if (t == 0) active[0] = k;
     }
   }
-  for (int e = blockIdx.x + (int)gridDim.x * tx; e <= E; e += (int)gridDim.x * kRGThreads) {
-    int r = 0;
-    for (int i = 0; i < k; ++i) r += s.pick_id[i] < e;
-    offsets[e] = r;
-  }
+  for (int e = blockIdx.x + (int)gridDim.x * tx; e <= E; e += (int)gridDim.x * kRGThreads)
+    offsets[e] = picks_below<4>(pv, e);
   const int slot = blockIdx.x / blocks_per_expert;
   if (slot >= k) return;
   const int lane = tx & (MOE_WAVE - 1), wave = tx / MOE_WAVE;
@@ -976,8 +977,7 @@ __global__ __launch_bounds__(kRGThreads) void route_gateup_one_kernel(
   int pid = INT_MAX, prank = -1;
   if (lane < k) {
     pid = s.pick_id[lane];
-    prank = 0;
-    for (int i = 0; i < k; ++i) prank += s.pick_id[i] < pid;
+    prank = picks_below<4>(pv, pid);
   }
   const int src = __ffsll((unsigned long long)__ballot(prank == slot)) - 1;
   const int e = __builtin_amdgcn_readlane(pid, src);
