@@ -39,9 +39,10 @@
 // instead (2 or 4 blocks each, gate blocks kept with their up blocks) and a
 // deeper ring of smaller slots, so MFMA work follows the routed rows rather
 // than the padded tile.  The plan orders (expert, token tile) pairs
-// heaviest first and deals them to the 8 XCDs in turn; each XCD runs its
-// pairs' weight tiles consecutively, so tiles sharing a token tile share
-// that XCD's L2.
+// heaviest first, an expert's full token tiles next to each other, and
+// deals them to the 8 XCDs in runs of four; each XCD steps through the
+// weight tiles of its run with all four token tiles at each, so the token
+// tiles of one expert read each weight tile into that XCD's L2 together.
 #include <climits>
 #include <type_traits>
 
@@ -53,6 +54,7 @@ constexpr int kThreads = 256;
 constexpr int kTileRows = 256;    // weight rows per block
 constexpr int kTileTok = 128;     // tokens per block
 constexpr int kStageK = 128;      // K values per LDS stage
+constexpr int kBand = 4;          // consecutive plan pairs per XCD
 
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef float v16f_t __attribute__((ext_vector_type(16)));
@@ -364,12 +366,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int nsb = K >> 5;               // scale bytes per weight row
   const int nst = K / kStageK;
 
-  // tile: XCD x = blockIdx % 8 runs pairs g = x, x + 8, ... of the plan
-  // (heaviest first), each as m_tiles consecutive weight tiles
-  const int bx = blockIdx.x;
-  const int q8 = (bx >> 3) / m_tiles, mt = (bx >> 3) - q8 * m_tiles;
-  const int pair = (bx & 7) + 8 * q8;
-  if (pair >= plan[0]) return;
+  // tile: block b runs on XCD b % 8.  The plan's pairs (heaviest first) go
+  // in bands of 8 * kBand: XCD x takes pairs x * kBand .. x * kBand + kBand - 1
+  // of each band, weight tile major, so the token tiles of one expert that
+  // land there read each weight tile into that XCD's L2 together; pairs
+  // past the last whole band go to XCD g % 8, one weight tile after another.
+  const int bx = blockIdx.x, xcd = bx & 7, q = bx >> 3;
+  const int npairs = plan[0];
+  const int bands = npairs / (8 * kBand);
+  const int q_bands = bands * kBand * m_tiles;  // blocks per XCD in whole bands
+  int pair, mt;
+  if (q < q_bands) {
+    const int b = q / (kBand * m_tiles), qi = q - b * (kBand * m_tiles);
+    mt = qi / kBand;
+    pair = b * 8 * kBand + xcd * kBand + (qi - mt * kBand);
+  } else {
+    const int r = (q - q_bands) / m_tiles;
+    mt = (q - q_bands) - r * m_tiles;
+    pair = bands * 8 * kBand + xcd + 8 * r;
+  }
+  if (pair >= npairs) return;
   const int slot = plan[1 + 2 * pair], ntile = plan[2 + 2 * pair];
   const int e = active[1 + slot];
   const int p0 = offsets[e], cnt = offsets[e + 1] - p0;
