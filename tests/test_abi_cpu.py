@@ -209,3 +209,15 @@ def test_decode_layer_rms_rejects_bad_arguments(L):
     args = list(ok)
     args[15] = 16
     assert f(*args) == WS_SMALL
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py times one GPU; asked for more it exits with status 2 and a
+    message, before touching a device."""
+    import subprocess
+    import sys
+
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
