@@ -1361,7 +1361,7 @@ hipError_t launch_expert_ffn_combine(const uint16_t* x, int T, int k, const moe_
 }
 
 bool route_ffn_combine_one_ok(int E, int k, const moe_mxfp4_weights& w) {
-  return w.hidden == 7168 && w.inter == 1536 && k <= kFMaxK && k <= E && E <= kRegExperts;
+  return w.hidden == 7168 && w.inter == 1536 && k >= 1 && k <= kFMaxK && k <= E && E <= kRegExperts;
 }
 
 hipError_t launch_route_ffn_combine_one(const float* logits, int k, const uint16_t* x, const float* y_prev,

@@ -218,13 +218,13 @@ moe_status moe_decode_layer_rms_mxfp4(const float* logits, const float* y_prev, 
     return MOE_ERR_INVALID_ARG;
   if (!weights_ok(w)) return MOE_ERR_INVALID_ARG;
   const int E = w->num_experts;
+  if (k < 1 || k > MOE_MAX_TOPK || k > E) return MOE_ERR_INVALID_ARG;
   if (!moe::route_ffn_combine_one_ok(E, k, *w)) {
     // the rescale, then the layer as moe_decode_layer_mxfp4 runs it
     if (!logits || !topk_ids || !topk_weights || !expert_offsets || !sorted_rows || !row_pos || !active ||
         !y_rows || !out || !workspace)
       return MOE_ERR_INVALID_ARG;
-    if (k < 1 || k > MOE_MAX_TOPK || k > E || !aligned16(y_rows) || !aligned16(out) || !aligned16(workspace))
-      return MOE_ERR_INVALID_ARG;
+    if (!aligned16(y_rows) || !aligned16(out) || !aligned16(workspace)) return MOE_ERR_INVALID_ARG;
     if (workspace_bytes < moe::expert_ffn_workspace(1, k, E, w->hidden, w->inter)) return MOE_ERR_WORKSPACE_TOO_SMALL;
     const moe_status d = check_device();
     if (d != MOE_OK) return d;

@@ -9,7 +9,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe_mxfp4.h")
-LIB = os.path.join(ROOT, "mxfp4_routed_expert_02_amd", "lib", "libmoe_mxfp4.so")
+from mxfp4_routed_expert_02_amd._binding import LIB_PATH as LIB  # noqa: E402 (the sanitized build under MOE_SANITIZE=1)
 
 OK, INVALID, UNSUPPORTED, WS_SMALL, HIPERR = 0, 1, 2, 3, 4
 
@@ -221,3 +221,30 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, timeout=300)
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
+
+
+@pytest.mark.parametrize("k", [0, -1, 33, 897])
+def test_decode_shape_rejects_bad_k(L, k):
+    """At the decode shape (H 7168, I 1536, E 896) the fused one-token calls
+    take their own launch path; a k outside 1..min(E, 32) must still be
+    rejected before anything is enqueued (here: INVALID, not the HIP error
+    a valid call gets on a host without a GPU)."""
+    big = 1 << 34
+    w = _weights(H=7168, I=1536, E=896)
+    dl = L.moe_decode_layer_mxfp4
+    args = [FAKE, FAKE, k, ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big, None]
+    assert dl(*args) == INVALID
+    args[2] = 16
+    assert dl(*args) == HIPERR  # the same call with a valid k passes validation
+    rms = L.moe_decode_layer_rms_mxfp4
+    args = [FAKE, FAKE, ctypes.c_float(1e-6), FAKE, k, ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+            FAKE, FAKE, big, None]
+    assert rms(*args) == INVALID
+    args[4] = 16
+    assert rms(*args) == HIPERR
+    fc = L.moe_expert_ffn_combine_mxfp4
+    args = [FAKE, 1, k, ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big, None]
+    assert fc(*args) == INVALID
+    args[2] = 16
+    assert fc(*args) == HIPERR
+    assert L.moe_route_group_one(FAKE, 896, k, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == INVALID
