@@ -15,6 +15,7 @@ import pytest
 
 import oracle
 from mxfp4_routed_expert_02_amd import synth
+from tests import bf16_patterns as bf16p
 from tests import np_reference as npr
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -312,6 +313,37 @@ def test_rms_rescale_matches_float64_within_one_bf16_ulp():
     got = npr.bf16_bits_to_f64(x)
     assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-30)
 
+
+
+def test_rms_rescale_rounds_to_bf16_exactly_as_torch():
+    """The rescale's last step, fp32 -> bf16 round-to-nearest-even, against
+    torch's own float32 -> bfloat16 cast bit for bit.  Each row holds one
+    anchor 2^20 and 63 test values v = t * 2^17 with |v| < 32: their squares
+    sum to less than half an ulp of 2^40 in any order, so the fp32 sum of squares is exactly 2^40,
+    the mean over H = 64 is 2^34 and the factor exactly 2^-17; the rescaled
+    values are then exactly the patterns t, and only the rounding is tested."""
+    import torch
+
+    y, tt = bf16p.anchored_rows()
+    for eps in (0.0, 1e-6):  # eps = 1e-6 vanishes next to a mean of 2^34
+        x = oracle.rms_rescale_bf16(y, eps)
+        assert np.all(x[:, 0] == 0x4100)  # 2^20 * 2^-17 = 8.0
+        want = torch.from_numpy(tt.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        bad = np.nonzero(x[:, 1:] != want)
+        assert bad[0].size == 0, [(hex(tt.view(np.uint32)[r, c]), hex(x[r, 1 + c]), hex(want[r, c]))
+                                  for r, c in zip(*bad)][:8]
+
+
+def test_bf16_rounding_pin_catches_truncation():
+    """The patterns above tell round-to-nearest-even from truncation and from
+    ties away from zero (a planted rounding mistake fails the pin)."""
+    import torch
+
+    t = bf16p.rounding_patterns()
+    want = torch.from_numpy(t.view(np.float32).copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    trunc = (t >> 16).astype(np.uint16)
+    away = ((t + 0x8000) >> 16).astype(np.uint16)
+    assert np.any(trunc != want) and np.any(away != want)
 
 # ------------------------------------------------------------- byte model ---
 def test_byte_model_matches_pages():
