@@ -9,7 +9,9 @@ from typing import Optional, Tuple
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "lib", "libmoe_mxfp4.so")
+# MOE_SANITIZE=1 loads the build with host-side AddressSanitizer + UBSan
+LIB_PATH = os.path.join(_PKG, "lib", "libmoe_mxfp4_san.so" if os.environ.get("MOE_SANITIZE") == "1"
+                        else "libmoe_mxfp4.so")
 
 MAX_EXPERTS = 4096
 MAX_TOPK = 32

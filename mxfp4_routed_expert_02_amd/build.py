@@ -27,15 +27,25 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build_library(verbose: bool = False) -> str:
+# host-only sanitizers for the checking build: each -fsanitize= applies to the host pass alone
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-Xarch_host", "-shared-libsan", "-Xarch_host", "-fno-omit-frame-pointer"]
+SAN_LIB_PATH = os.path.join(LIB_DIR, "libmoe_mxfp4_san.so")
+
+
+def build_library(verbose: bool = False, sanitize: bool = False) -> str:
+    """hipcc build of every csrc/*.hip into lib/libmoe_mxfp4.so.  sanitize=True
+    builds lib/libmoe_mxfp4_san.so with AddressSanitizer and UBSan on the
+    host code (argument validation, launch set-up); device code is the same."""
     os.makedirs(LIB_DIR, exist_ok=True)
-    tmp = LIB_PATH + ".tmp"
-    cmd = [HIPCC] + HIP_FLAGS + ["-I", os.path.join(ROOT, "include")] + sources() + ["-o", tmp]
+    path = SAN_LIB_PATH if sanitize else LIB_PATH
+    tmp = path + ".tmp"
+    cmd = [HIPCC] + HIP_FLAGS + (HOST_SANITIZE if sanitize else []) + ["-I", os.path.join(ROOT, "include")] + \
+        sources() + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, path)
+    return path
 
 
 def build_all(verbose: bool = False) -> None:

@@ -22,7 +22,9 @@ from typing import Dict, Optional
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe_synth.so")
+# MOE_SANITIZE=1 loads the AddressSanitizer + UBSan build of the host generator
+SANITIZE = os.environ.get("MOE_SANITIZE") == "1"
+LIB_PATH = os.path.join(_HERE, "libmoe_synth_san.so" if SANITIZE else "libmoe_synth.so")
 GPU_LIB_PATH = os.path.join(_HERE, "libmoe_synth_gpu.so")  # device twin of the slab generator
 
 # array ids of the tag field (weights use 1..6 inside moe_synth.c)
@@ -36,17 +38,24 @@ _lib = None
 _gpu_lib = None
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, sanitize: bool = False) -> str:
     """Compile moe_synth.c into libmoe_synth.so with gcc (host code) and
-    synth_gpu.hip into libmoe_synth_gpu.so with hipcc (gfx950)."""
+    synth_gpu.hip into libmoe_synth_gpu.so with hipcc (gfx950).
+    sanitize=True builds only the host generator, with clang's
+    AddressSanitizer and UBSan, into libmoe_synth_san.so."""
     import subprocess
 
-    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC",
-           os.path.join(_HERE, "moe_synth.c"), "-o", LIB_PATH + ".tmp", "-lm", "-lpthread"]
+    path = os.path.join(_HERE, "libmoe_synth_san.so" if sanitize else "libmoe_synth.so")
+    cc = ["/opt/rocm/llvm/bin/clang", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+          "-fno-omit-frame-pointer", "-g", "-shared-libsan"] if sanitize else ["gcc"]
+    cmd = cc + ["-O2", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC",
+                os.path.join(_HERE, "moe_synth.c"), "-o", path + ".tmp", "-lm", "-lpthread"]
     if verbose:
         print(" ".join(cmd))
     subprocess.check_call(cmd)
-    os.replace(LIB_PATH + ".tmp", LIB_PATH)
+    os.replace(path + ".tmp", path)
+    if sanitize:
+        return path
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     cmd = [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-fvisibility=hidden",

@@ -14,7 +14,10 @@ from typing import Dict, Optional, Tuple
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# MOE_SANITIZE=1 loads the AddressSanitizer + UBSan build (liboracle_san.so;
+# the process must preload clang's ASan runtime, tests/run_sanitized.py does)
+SANITIZE = os.environ.get("MOE_SANITIZE") == "1"
+LIB_PATH = os.path.join(_HERE, "liboracle_san.so" if SANITIZE else "liboracle.so")
 _lib = None
 
 _P = ctypes.c_void_p
@@ -26,14 +29,19 @@ class OracleWeights(ctypes.Structure):
                 ("expert_stride", ctypes.c_int64), ("num_experts", _I32), ("hidden", _I32), ("inter", _I32)]
 
 
-def build(verbose: bool = False) -> str:
-    cmd = ["g++", "-O2", "-std=c++17", "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra", "-shared",
-           "-fPIC", "-pthread", os.path.join(_HERE, "moe_oracle.cpp"), "-o", LIB_PATH + ".tmp"]
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """g++ build of moe_oracle.cpp; sanitize=True builds liboracle_san.so with
+    clang's AddressSanitizer and UBSan instead (same flags otherwise)."""
+    path = os.path.join(_HERE, "liboracle_san.so" if sanitize else "liboracle.so")
+    cxx = ["/opt/rocm/llvm/bin/clang++", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-fno-omit-frame-pointer", "-g", "-shared-libsan"] if sanitize else ["g++"]
+    cmd = cxx + ["-O2", "-std=c++17", "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra", "-shared",
+                 "-fPIC", "-pthread", os.path.join(_HERE, "moe_oracle.cpp"), "-o", path + ".tmp"]
     if verbose:
         print(" ".join(cmd))
     subprocess.check_call(cmd)
-    os.replace(LIB_PATH + ".tmp", LIB_PATH)
-    return LIB_PATH
+    os.replace(path + ".tmp", path)
+    return path
 
 
 def lib():
