@@ -4,7 +4,9 @@ grouping; moe_combine_rms_bf16 against the separate moe_combine +
 moe_rms_rescale_bf16 and against the oracle's combine and rescale.
 
 Against the separate GPU calls the fused outputs must be bit for bit the
-same.  Against the oracle: ids and grouping bit for bit, routing weights
+same.  The fused expert-FFN and decode-layer calls are also compared with
+the oracle directly: routing bit for bit, y_rows and out at the parity bar
+(the RMS variant on the GPU's own bf16 input, its rescale within one ulp).  Against the oracle: ids and grouping bit for bit, routing weights
 within 1e-6; the combine within the layer's tolerance (the GPU sums with
 fused multiply-adds, the oracle without), the rescale within one bf16 ulp of
 the oracle's rescale of the GPU's own combine.
@@ -16,7 +18,7 @@ import torch
 import oracle
 from mxfp4_routed_expert_02_amd import (Grouping, combine, combine_rms_bf16, group_rows, rms_rescale_bf16,
                                         route_group_one, route_topk, synth)
-from tests.gpu_common import say
+from tests.gpu_common import assert_close, oracle_outputs, say
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda", 0)
@@ -141,6 +143,28 @@ def test_ffn_combine_matches_two_calls(case):
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int32), y2.view(torch.int32)), "y_rows bits differ"
     assert torch.equal(out1.view(torch.int32), out2.view(torch.int32)), "out bits differ"
+    # against the oracle on the same ids and weights
+    ids_np, w_np = ids.cpu().numpy(), w.cpu().numpy()
+    ref_g = oracle.group_rows(ids_np, E)
+    np.testing.assert_array_equal(g.sorted_rows.cpu().numpy(), ref_g["sorted_rows"])
+    out_ref, y_ref = oracle_outputs(synth.activations_bf16(0, wl), ids_np, w_np, ref_g["sorted_rows"], wl)
+    assert_close(y2.cpu().numpy(), y_ref, "y_rows vs oracle")
+    assert_close(out2.cpu().numpy(), out_ref, "out vs oracle")
+
+
+def _against_oracle(lg_np, x_np, k, wl, ids, w, g, y_rows, out):
+    """One token's fused-call outputs against the oracle: top-k ids and
+    grouping bit for bit, routing weights within 1e-6, y_rows and out at the
+    parity bar."""
+    rid, rw = oracle.route_topk(lg_np.reshape(1, -1), k)
+    rg = oracle.group_rows(rid, wl.E)
+    np.testing.assert_array_equal(ids.cpu().numpy(), rid)
+    assert np.abs(w.cpu().numpy() - rw).max() <= 1e-6
+    for nm in ("expert_offsets", "sorted_rows", "row_pos"):
+        np.testing.assert_array_equal(getattr(g, nm).cpu().numpy(), rg[nm])
+    out_ref, y_ref = oracle_outputs(x_np.reshape(1, -1), rid, rw, rg["sorted_rows"], wl)
+    assert_close(y_rows.cpu().numpy(), y_ref, "y_rows vs oracle")
+    assert_close(out.cpu().numpy(), out_ref, "out vs oracle")
 
 
 # moe_decode_layer_mxfp4 against moe_route_group_one + moe_expert_ffn_combine_mxfp4:
@@ -194,6 +218,8 @@ def test_decode_layer_matches_calls(case):
     assert torch.equal(g1.active[:1 + k], g2.active[:1 + k]), "active differs"
     assert torch.equal(y1.view(torch.int32), y2.view(torch.int32)), "y_rows bits differ"
     assert torch.equal(out1.view(torch.int32), out2.view(torch.int32)), "out bits differ"
+    # against the oracle: routing bit for bit, then the layer on its ids and weights
+    _against_oracle(lg.cpu().numpy(), synth.activations_bf16(0, wl), k, wl, ids2, w2, g2, y2, out2)
 
 
 # moe_decode_layer_rms_mxfp4 against moe_rms_rescale_bf16 + moe_decode_layer_mxfp4,
@@ -242,6 +268,12 @@ def test_decode_layer_rms_matches_calls(case):
         assert torch.equal(getattr(g1, nm), getattr(g2, nm)), nm
     assert torch.equal(y1.view(torch.int32), y2.view(torch.int32)), "y_rows bits differ"
     assert torch.equal(out1.view(torch.int32), out2.view(torch.int32)), "out bits differ"
+    # against the oracle: the rescale within one bf16 ulp of the oracle's, then
+    # the layer on the GPU's own bf16 input
+    x_gpu = x2.view(torch.int16).cpu().numpy().view(np.uint16)
+    x_ref = oracle.rms_rescale_bf16(y_prev.cpu().numpy(), 1e-6)
+    assert np.abs(x_gpu.astype(np.int32) - x_ref.astype(np.int32)).max() <= 1, "rescale more than one ulp off"
+    _against_oracle(lg.cpu().numpy(), x_gpu, k, wl, ids2, w2, g2, y2, out2)
 
 
 def test_decode_layer_graph_replays_match_eager():
