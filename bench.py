@@ -9,9 +9,11 @@ decode on one layer of 896 resident experts (hidden 7168, intermediate
 the routed experts differ from step to step and the 256 MB last-level cache
 cannot serve them.
 
-Prints one JSON line: value = routed-expert weight GB/s of the whole layer,
-plus the roofline of the expert-FFN call (HIP events on the launch stream)
-and the CPU oracle's rate on the host cores as a reported baseline.
+Prints one JSON line: value = routed-expert weight GB/s of the whole layer
+(its own fraction of the HBM peak in layer_roofline), the roofline of the
+expert-FFN call (HIP events on the launch stream), and the CPU oracle's rate
+on the host cores as a reported baseline (threads used, the host's core
+count and a single-thread rate beside it).
 """
 from __future__ import annotations
 
@@ -222,6 +224,9 @@ def main():
         "vs_baseline": None, "dtype": "mxfp4", "data": "synthetic",
         "config": {"workload": "decode896", "experts": wl.E, "hidden": wl.H, "inter": wl.I, "topk": wl.k,
                    "tokens": wl.T, "variants": V, "weight_bytes_per_step": weight_bytes},
+        "layer_roofline": {"bound": "hbm", "what": "whole decode layer (value / peak)", "achieved": round(value, 1),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(value / HBM_PEAK_GBS, 4),
+                           "algorithmic_bytes": weight_bytes, "us_per_step": round(ms_step * 1e3, 2)},
         "roofline": {"bound": "hbm", "kernel": "moe_expert_ffn_mxfp4 call", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": profiled_traffic(), "launch_us": round(ffn_us, 2),
@@ -451,35 +456,48 @@ def stack_side(dev, seed, reps):
 
 def cpu_baseline(args, wl):
     """The CPU oracle (as it stands) on the host cores: whole decode896 layers
-    for successive variants until about --cpu-seconds have passed."""
+    for successive variants until about --cpu-seconds have passed on
+    --cpu-threads threads, then one more layer on a single thread."""
     import numpy as np
 
     import oracle
     from mxfp4_routed_expert_02_amd import synth
 
-    threads = max(1, min(args.cpu_threads, os.cpu_count() or 1))
-    done, t_acc, nbytes = 0, 0.0, 0
-    v = 0
-    while t_acc < args.cpu_seconds and v < args.variants:
+    host_cores = os.cpu_count() or 1
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = host_cores
+    threads = max(1, min(args.cpu_threads, affinity))
+    sb = synth.slab_bytes(wl.H, wl.I)
+
+    def one_layer(v, nthreads):
         x = synth.activations_bf16(args.seed, wl, variant=v)
         logits = synth.router_logits(args.seed, wl, variant=v)
         ids, _ = oracle.route_topk(logits, wl.k)
-        sb = synth.slab_bytes(wl.H, wl.I)
         slabs = np.zeros((wl.E, sb), np.uint8)
         for e in ids.reshape(-1):
             synth.expert_slabs(args.seed, wl.pool, 0, int(e), 1, wl.H, wl.I, out=slabs[e:e + 1])
         hp = oracle.Pool(slabs, wl.H, wl.I)
         t = time.perf_counter()
-        oracle.layer(x, logits, wl.k, hp, nthreads=threads)
-        t_acc += time.perf_counter() - t
-        nbytes += wl.T * wl.k * sb
+        oracle.layer(x, logits, wl.k, hp, nthreads=nthreads)
+        return time.perf_counter() - t
+
+    done, t_acc = 0, 0.0
+    while t_acc < args.cpu_seconds and done < args.variants:
+        t_acc += one_layer(done, threads)
         done += 1
-        v += 1
-    gbs = nbytes / t_acc / 1e9
-    log(f"cpu oracle: {done} decode896 layers in {t_acc:.1f} s on {threads} threads, {gbs:.3f} GB/s")
+    gbs = done * wl.T * wl.k * sb / t_acc / 1e9
+    t1 = one_layer(done % args.variants, 1)
+    gbs1 = wl.T * wl.k * sb / t1 / 1e9
+    log(f"cpu oracle: {done} decode896 layers in {t_acc:.1f} s on {threads} threads, {gbs:.3f} GB/s; "
+        f"1 thread {gbs1:.4f} GB/s; host has {host_cores} cores ({affinity} in this process's affinity mask)")
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{done} whole decode896 layers (1 token, 16 of 896 experts each, variants 0..{done - 1}), "
-                      f"{t_acc:.1f} s of oracle time"}
+                      f"{t_acc:.1f} s of oracle time on {threads} threads",
+            "threads_used": threads, "host_cores": host_cores, "affinity_cpus": affinity,
+            "single_thread": {"value": round(gbs1, 5), "unit": "GB/s", "threads": 1,
+                              "sample": f"1 whole decode896 layer (variant {done % args.variants}), {t1:.1f} s"}}
 
 
 if __name__ == "__main__":
