@@ -24,9 +24,13 @@
  *   - T = 0 is a valid empty batch; arrays whose size is a multiple of T may
  *     then be NULL (moe_group_rows still writes expert_offsets and active).
  *   - The current HIP device must be a gfx950 GPU (MOE_ERR_UNSUPPORTED_DEVICE
- *     otherwise).  The library keeps no other state and is re-entrant.
+ *     otherwise).  The library keeps no other state (apart from the static
+ *     scratch of moe_decode_layer_mxfp4_noalloc) and is re-entrant.
  *   - Preconditions not checked on the device: logits are finite, the ids
- *     handed to moe_group_rows lie in [0, E), scale bytes are not 0xFF.
+ *     handed to moe_group_rows lie in [0, E), and every dequantized weight
+ *     E2M1 * 2^(s-127) is a finite fp32 value (always so for scale bytes
+ *     up to 252; at 253 and 254 codes of magnitude 2 or more exceed the
+ *     fp32 range, and 0xFF is NaN in E8M0).
  *   - Results are deterministic: the same inputs give the same bits on every
  *     run (no atomics decide any order or any sum).
  *
@@ -65,7 +69,9 @@ typedef enum {
   MOE_ERR_INVALID_ARG = 1,         /* a null/misaligned pointer or a size out of range */
   MOE_ERR_UNSUPPORTED_DEVICE = 2,  /* the current device is not gfx950 */
   MOE_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes < moe_workspace_bytes(...) */
-  MOE_ERR_HIP = 4                  /* the HIP runtime refused a launch */
+  MOE_ERR_HIP = 4,                 /* the HIP runtime refused a launch */
+  MOE_ERR_SCRATCH_TOO_SMALL = 5    /* moe_decode_layer_mxfp4_noalloc: the shape needs more than
+                                      MOE_NOALLOC_SCRATCH_BYTES of scratch */
 } moe_status;
 
 #define MOE_MAX_EXPERTS 4096 /* E */
@@ -296,6 +302,33 @@ MOE_API moe_status moe_decode_layer_rms_mxfp4(const float* logits, const float* 
                                               int32_t* sorted_rows, int32_t* row_pos, int32_t* active,
                                               float* y_rows, float* out, void* workspace, size_t workspace_bytes,
                                               moe_stream_t stream);
+
+/*
+ * moe_decode_layer_mxfp4_noalloc - moe_decode_layer_mxfp4 for callers that
+ * cannot allocate or hand over device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments and
+ * the same outputs bit for bit, without the workspace: its scratch (h, the
+ * k x I fp32 gate/up results) lives in a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES in the library, one per GPU, held until the
+ * process ends.  The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); the first call on a device looks up that
+ * device's array address once.
+ *   k * I * 4 bytes (rounded up to 256) must fit in the scratch, i.e.
+ *   k * I <= 262144 (the decode shape k = 16, I = 1536 takes 96 KiB);
+ *   larger shapes return MOE_ERR_SCRATCH_TOO_SMALL before anything is
+ *   enqueued.  Other errors as moe_decode_layer_mxfp4.
+ * Every call on one GPU shares that GPU's scratch: calls that may overlap on
+ * one device (on different streams without ordering between them, or from
+ * several threads) race and must be serialized by the caller.  Nothing in
+ * the scratch needs to start at zero; its contents between calls mean
+ * nothing.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (1u << 20)
+MOE_API moe_status moe_decode_layer_mxfp4_noalloc(const float* logits, const uint16_t* x, int32_t k,
+                                                  const moe_mxfp4_weights* w, int32_t* topk_ids,
+                                                  float* topk_weights, int32_t* expert_offsets, int32_t* sorted_rows,
+                                                  int32_t* row_pos, int32_t* active, float* y_rows, float* out,
+                                                  moe_stream_t stream);
 
 #ifdef __cplusplus
 }

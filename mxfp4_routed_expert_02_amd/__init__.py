@@ -28,6 +28,7 @@ from ._binding import (  # noqa: F401
     combine,
     combine_rms_bf16,
     decode_layer_mxfp4,
+    decode_layer_mxfp4_noalloc,
     decode_layer_rms_mxfp4,
     expert_ffn_combine_mxfp4,
     expert_ffn_mxfp4,

@@ -21,7 +21,8 @@ _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 
 _STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED_DEVICE",
-           3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP"}
+           3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP", 5: "MOE_ERR_SCRATCH_TOO_SMALL"}
+NOALLOC_SCRATCH_BYTES = 1 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 
 
 class MoeError(RuntimeError):
@@ -62,13 +63,15 @@ def lib():
                                              _P]
         L.moe_decode_layer_rms_mxfp4.argtypes = [_P, _P, ctypes.c_float, _P, _I32, W, _P, _P, _P, _P, _P, _P, _P,
                                                  _P, _P, ctypes.c_size_t, _P]
+        L.moe_decode_layer_mxfp4_noalloc.argtypes = [_P, _P, _I32, W, _P, _P, _P, _P, _P, _P, _P, _P, _P]
         L.moe_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32, _I32]
         L.moe_workspace_bytes.restype = ctypes.c_size_t
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         for f in ("moe_route_topk", "moe_group_rows", "moe_expert_ffn_mxfp4", "moe_combine",
                   "moe_rms_rescale_bf16", "moe_router_logits", "moe_route_group_one", "moe_combine_rms_bf16",
-                  "moe_expert_ffn_combine_mxfp4", "moe_decode_layer_mxfp4", "moe_decode_layer_rms_mxfp4"):
+                  "moe_expert_ffn_combine_mxfp4", "moe_decode_layer_mxfp4", "moe_decode_layer_rms_mxfp4",
+                  "moe_decode_layer_mxfp4_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -208,6 +211,23 @@ def decode_layer_mxfp4(logits: torch.Tensor, x: torch.Tensor, k: int, pool: Expe
         _dev(grp.row_pos, torch.int32, "row_pos"), _dev(grp.active, torch.int32, "active"),
         _dev(y_rows, torch.float32, "y_rows"), _dev(out, torch.float32, "out"),
         _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(x.device)))
+    return out
+
+
+def decode_layer_mxfp4_noalloc(logits: torch.Tensor, x: torch.Tensor, k: int, pool: ExpertPool, ids: torch.Tensor,
+                               weights: torch.Tensor, grp: Grouping, y_rows: torch.Tensor,
+                               out: torch.Tensor) -> torch.Tensor:
+    """decode_layer_mxfp4 without a workspace: the library's static device scratch serves instead (nothing is
+    allocated; calls that may overlap on one GPU race)."""
+    if logits.shape[0] != 1 or x.shape[0] != 1:
+        raise ValueError("decode_layer_mxfp4_noalloc takes one token")
+    xb = x.view(torch.int16) if x.dtype == torch.bfloat16 else x
+    _check("moe_decode_layer_mxfp4_noalloc", lib().moe_decode_layer_mxfp4_noalloc(
+        _dev(logits, torch.float32, "logits"), _dev(xb, torch.int16, "x"), k, ctypes.byref(pool.weights),
+        _dev(ids, torch.int32, "ids"), _dev(weights, torch.float32, "weights"),
+        _dev(grp.expert_offsets, torch.int32, "expert_offsets"), _dev(grp.sorted_rows, torch.int32, "sorted_rows"),
+        _dev(grp.row_pos, torch.int32, "row_pos"), _dev(grp.active, torch.int32, "active"),
+        _dev(y_rows, torch.float32, "y_rows"), _dev(out, torch.float32, "out"), _stream(x.device)))
     return out
 
 

@@ -4,6 +4,7 @@
 #include <atomic>
 #include <climits>
 #include <cstring>
+#include <mutex>
 
 #include "moe_internal.h"
 
@@ -31,6 +32,32 @@ moe_status check_device() {
 
 moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// Device scratch of moe_decode_layer_mxfp4_noalloc: one copy per GPU, held
+// until the process ends.  Host code never uses the array's name as an
+// address; it uses the per-device pointer hipGetSymbolAddress returns.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// The current device's scratch address, looked up once per device (with
+// that device current) and kept.
+moe_status scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MOE_ERR_HIP;
+  if (dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED_DEVICE;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return MOE_OK;
+}
+
 bool rows_fit(int32_t T, int32_t k) { return T >= 0 && k >= 1 && (int64_t)T * k <= INT32_MAX / 2; }
 
 bool weights_ok(const moe_mxfp4_weights* w) {
@@ -45,6 +72,40 @@ bool weights_ok(const moe_mxfp4_weights* w) {
   return true;
 }
 
+bool decode_args_ok(const float* logits, const uint16_t* x, int32_t k, const moe_mxfp4_weights* w,
+                    const int32_t* topk_ids, const float* topk_weights, const int32_t* expert_offsets,
+                    const int32_t* sorted_rows, const int32_t* row_pos, const int32_t* active, const float* y_rows,
+                    const float* out) {
+  if (!logits || !x || !topk_ids || !topk_weights || !expert_offsets || !sorted_rows || !row_pos || !active ||
+      !y_rows || !out)
+    return false;
+  if (!aligned16(x) || !aligned16(y_rows) || !aligned16(out)) return false;
+  return weights_ok(w) && k >= 1 && k <= MOE_MAX_TOPK && k <= w->num_experts;
+}
+
+moe_status decode_layer_launch(const float* logits, const uint16_t* x, int32_t k, const moe_mxfp4_weights* w,
+                               int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                               int32_t* sorted_rows, int32_t* row_pos, int32_t* active, float* y_rows, float* out,
+                               void* ws, hipStream_t s) {
+  const int E = w->num_experts;
+  if (moe::route_ffn_combine_one_ok(E, k, *w))
+    return from_hip(moe::launch_route_ffn_combine_one(logits, k, x, nullptr, 0.0f, nullptr, *w, topk_ids,
+                                                      topk_weights, expert_offsets, sorted_rows, row_pos, active,
+                                                      y_rows, out, ws, s));
+  hipError_t err;
+  if (E <= 2048) {
+    err = moe::launch_route_group_one(logits, E, k, topk_ids, topk_weights, expert_offsets, sorted_rows, row_pos,
+                                      active, s);
+  } else {
+    err = moe::launch_route_topk(logits, 1, E, k, topk_ids, topk_weights, s);
+    if (err == hipSuccess)
+      err = moe::launch_group_rows(topk_ids, 1, k, E, expert_offsets, sorted_rows, row_pos, active, nullptr, s);
+  }
+  if (err != hipSuccess) return MOE_ERR_HIP;
+  return from_hip(moe::launch_expert_ffn_combine(x, 1, k, *w, expert_offsets, sorted_rows, active, topk_weights,
+                                                 row_pos, y_rows, out, ws, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -56,6 +117,9 @@ const char* moe_status_string(moe_status s) {
     case MOE_ERR_UNSUPPORTED_DEVICE: return "MOE_ERR_UNSUPPORTED_DEVICE: the current HIP device is not gfx950";
     case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL: workspace_bytes below moe_workspace_bytes()";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: the HIP runtime reported an error";
+    case MOE_ERR_SCRATCH_TOO_SMALL:
+      return "MOE_ERR_SCRATCH_TOO_SMALL: the shape needs more than the library's static scratch "
+             "(MOE_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown moe_status";
 }
@@ -180,33 +244,34 @@ moe_status moe_decode_layer_mxfp4(const float* logits, const uint16_t* x, int32_
                                   int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
                                   int32_t* sorted_rows, int32_t* row_pos, int32_t* active, float* y_rows, float* out,
                                   void* workspace, size_t workspace_bytes, moe_stream_t stream) {
-  if (!logits || !x || !topk_ids || !topk_weights || !expert_offsets || !sorted_rows || !row_pos || !active ||
-      !y_rows || !out || !workspace)
+  if (!decode_args_ok(logits, x, k, w, topk_ids, topk_weights, expert_offsets, sorted_rows, row_pos, active, y_rows,
+                      out))
     return MOE_ERR_INVALID_ARG;
-  if (!aligned16(x) || !aligned16(y_rows) || !aligned16(out) || !aligned16(workspace)) return MOE_ERR_INVALID_ARG;
-  if (!weights_ok(w) || k < 1 || k > MOE_MAX_TOPK || k > w->num_experts) return MOE_ERR_INVALID_ARG;
+  if (!workspace || !aligned16(workspace)) return MOE_ERR_INVALID_ARG;
   if (workspace_bytes < moe::expert_ffn_workspace(1, k, w->num_experts, w->hidden, w->inter))
     return MOE_ERR_WORKSPACE_TOO_SMALL;
   const moe_status d = check_device();
   if (d != MOE_OK) return d;
-  const hipStream_t s = (hipStream_t)stream;
-  const int E = w->num_experts;
-  if (moe::route_ffn_combine_one_ok(E, k, *w))
-    return from_hip(moe::launch_route_ffn_combine_one(logits, k, x, nullptr, 0.0f, nullptr, *w, topk_ids,
-                                                      topk_weights, expert_offsets, sorted_rows, row_pos, active,
-                                                      y_rows, out, workspace, s));
-  hipError_t err;
-  if (E <= 2048) {
-    err = moe::launch_route_group_one(logits, E, k, topk_ids, topk_weights, expert_offsets, sorted_rows, row_pos,
-                                      active, s);
-  } else {
-    err = moe::launch_route_topk(logits, 1, E, k, topk_ids, topk_weights, s);
-    if (err == hipSuccess)
-      err = moe::launch_group_rows(topk_ids, 1, k, E, expert_offsets, sorted_rows, row_pos, active, nullptr, s);
-  }
-  if (err != hipSuccess) return MOE_ERR_HIP;
-  return from_hip(moe::launch_expert_ffn_combine(x, 1, k, *w, expert_offsets, sorted_rows, active, topk_weights,
-                                                 row_pos, y_rows, out, workspace, s));
+  return decode_layer_launch(logits, x, k, w, topk_ids, topk_weights, expert_offsets, sorted_rows, row_pos, active,
+                             y_rows, out, workspace, (hipStream_t)stream);
+}
+
+moe_status moe_decode_layer_mxfp4_noalloc(const float* logits, const uint16_t* x, int32_t k,
+                                          const moe_mxfp4_weights* w, int32_t* topk_ids, float* topk_weights,
+                                          int32_t* expert_offsets, int32_t* sorted_rows, int32_t* row_pos,
+                                          int32_t* active, float* y_rows, float* out, moe_stream_t stream) {
+  if (!decode_args_ok(logits, x, k, w, topk_ids, topk_weights, expert_offsets, sorted_rows, row_pos, active, y_rows,
+                      out))
+    return MOE_ERR_INVALID_ARG;
+  if (moe::expert_ffn_workspace(1, k, w->num_experts, w->hidden, w->inter) > MOE_NOALLOC_SCRATCH_BYTES)
+    return MOE_ERR_SCRATCH_TOO_SMALL;
+  const moe_status d = check_device();
+  if (d != MOE_OK) return d;
+  void* ws = nullptr;
+  const moe_status sp = scratch_ptr(&ws);
+  if (sp != MOE_OK) return sp;
+  return decode_layer_launch(logits, x, k, w, topk_ids, topk_weights, expert_offsets, sorted_rows, row_pos, active,
+                             y_rows, out, ws, (hipStream_t)stream);
 }
 
 moe_status moe_decode_layer_rms_mxfp4(const float* logits, const float* y_prev, float eps, uint16_t* x_next,

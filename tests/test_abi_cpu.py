@@ -11,7 +11,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe_mxfp4.h")
 from mxfp4_routed_expert_02_amd._binding import LIB_PATH as LIB  # noqa: E402 (the sanitized build under MOE_SANITIZE=1)
 
-OK, INVALID, UNSUPPORTED, WS_SMALL, HIPERR = 0, 1, 2, 3, 4
+OK, INVALID, UNSUPPORTED, WS_SMALL, HIPERR, SCRATCH_SMALL = 0, 1, 2, 3, 4, 5
 
 
 def declared_functions():
@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for s in range(5):
+    for s in range(6):
         assert L.moe_status_string(s).startswith(b"MOE_")
 
 
@@ -248,3 +248,32 @@ def test_decode_shape_rejects_bad_k(L, k):
     args[2] = 16
     assert fc(*args) == HIPERR
     assert L.moe_route_group_one(FAKE, 896, k, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == INVALID
+
+
+def test_decode_layer_noalloc_validation(L):
+    """The allocation-free decode call: the same argument checks as
+    moe_decode_layer_mxfp4, and shapes whose scratch (k * I fp32) exceeds the
+    library's static buffer are refused with their own status, before any
+    device call."""
+    f = L.moe_decode_layer_mxfp4_noalloc
+    w = _weights(H=7168, I=1536, E=896)
+    ok = [FAKE, FAKE, 16, ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None]
+    assert f(*ok) == HIPERR  # valid: only the missing device stops it
+    for i in (0, 1, 4, 5, 6, 7, 8, 9, 10, 11):  # every pointer
+        args = list(ok)
+        args[i] = None
+        assert f(*args) == INVALID, i
+    for k in (0, -1, 33, 897):
+        args = list(ok)
+        args[2] = k
+        assert f(*args) == INVALID, k
+    args = list(ok)
+    args[10] = FAKE + 4  # y_rows misaligned
+    assert f(*args) == INVALID
+    big = _weights(H=7168, I=16384, E=896)  # 32 * 16384 * 4 bytes = 2 MiB of scratch
+    args = list(ok)
+    args[2], args[3] = 32, ctypes.byref(big)
+    assert f(*args) == SCRATCH_SMALL
+    args[2] = 16  # 1 MiB: fits exactly
+    assert f(*args) == HIPERR
+    assert L.moe_status_string(SCRATCH_SMALL).startswith(b"MOE_ERR_SCRATCH_TOO_SMALL")
