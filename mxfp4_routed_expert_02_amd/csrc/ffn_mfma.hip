@@ -96,6 +96,91 @@ __device__ __forceinline__ int e4m3_block_exp(float amax) {
   return e < -126 ? -126 : (e > 126 ? 126 : e);  // 2^e and 2^-e stay normal floats
 }
 
+// Round |a| <= 7.5 to E2M3 (FP6: sign, 2 exponent bits with bias 1, 3
+// mantissa bits; ties to even); returns the 6-bit code and the rounded value.
+__device__ __forceinline__ uint32_t e2m3_rne(float a, float& qv) {
+  const float x = fabsf(a);
+  uint32_t code;
+  if (x < 1.0f) {  // the subnormal grid m / 8 (m = 8 is 1.0, code 8)
+    const float m = rintf(x * 8.0f);
+    code = (uint32_t)m;
+    qv = m * 0.125f;
+  } else {
+    uint32_t b = __float_as_uint(x);
+    b += 0x7FFFFu + ((b >> 20) & 1u);  // keep 3 mantissa bits
+    b &= 0xFFF00000u;
+    code = (b >> 20) - (126u << 3);    // exponent bias 127 -> 1
+    qv = __uint_as_float(b);
+  }
+  if (a < 0.0f) {
+    code |= 0x20u;
+    qv = -qv;
+  }
+  return code;
+}
+
+// E8M0 exponent e with amax / 2^e <= 7.5, e = ceil(log2(amax / 7.5)); 0 for amax = 0
+__device__ __forceinline__ int e2m3_block_exp(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  const uint32_t b = __float_as_uint(amax);
+  const int E = (int)((b >> 23) & 0xFF) - 127;
+  int e = ((b & 0x7FFFFFu) <= 0x700000u) ? E - 2 : E - 1;  // 7.5 = 1.875 * 2^2
+  return e < -126 ? -126 : (e > 126 ? 126 : e);  // 2^e and 2^-e stay normal floats
+}
+
+// Quantizes rows of a [rows][K] bf16 matrix into two E2M3 (FP6) terms,
+//     a = q1 * 2^e1 + q2 * 2^e2,  q1 = rne_e2m3(a / 2^e1),  q2 = rne_e2m3((a - q1 2^e1) / 2^e2),
+// e = ceil(log2(amax / 7.5)) per 32-value block and term.  Stored stage-major
+// as records of 128 bytes per (128-value K stage, row, term):
+//   bytes 48 s .. 48 s + 47 (MFMA step s = 0, 1 of the stage): the 16 low
+//     bytes of block 2s, the 16 low bytes of block 2s+1, the 8 high bytes of
+//     block 2s, the 8 high bytes of block 2s+1 (a block = 32 codes packed 6
+//     bits each, code i at bits 6i .. 6i+5 of its 24 bytes)
+//   bytes 96 + 4h + 2s: the E8M0 scale of block 2s + h
+// so that MFMA lane-half h reads 16 + 8 aligned bytes and one scale word
+// whose bytes 0 and 2 serve steps 0 and 1.  One thread per (row, 32-block).
+__device__ __forceinline__ void quantize_block_fp6(const uint16_t* __restrict__ src, int row, int rows, int blk,
+                                                   int K, uint8_t* __restrict__ q) {
+  float v[32];
+  const uint4* p = (const uint4*)(src + (int64_t)row * K + 32 * blk);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 w = p[i];
+    const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * i + 2 * j] = __uint_as_float(d[j] << 16);
+      v[8 * i + 2 * j + 1] = __uint_as_float(d[j] & 0xFFFF0000u);
+    }
+  }
+  const int st = blk >> 2, s = (blk >> 1) & 1, h = blk & 1;
+  uint8_t* rec = q + ((int64_t)st * rows + row) * 256;
+#pragma unroll
+  for (int term = 0; term < 2; ++term) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    const int e = e2m3_block_exp(amax);
+    const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e
+    const float scl = __uint_as_float((uint32_t)(127 + e) << 23);  // 2^e
+    uint32_t pk[6];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) pk[i] = 0u;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      float qv;
+      const uint32_t c = e2m3_rne(v[i] * inv, qv);
+      pk[(6 * i) >> 5] |= c << ((6 * i) & 31);
+      if (((6 * i) & 31) > 26) pk[((6 * i) >> 5) + 1] |= c >> (32 - ((6 * i) & 31));
+      v[i] -= qv * scl;  // residual for the next term (exact)
+    }
+    uint8_t* r = rec + term * 128;
+    *(uint4*)(r + 48 * s + 16 * h) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    *(uint2*)(r + 48 * s + 32 + 8 * h) = make_uint2(pk[4], pk[5]);
+    r[96 + 4 * h + 2 * s] = (uint8_t)(e + 127);
+  }
+}
+
 // Quantizes rows of a [rows][K] matrix (bf16 bits or fp32) into two E4M3
 // terms, stored stage-major so that one 128-value K stage of every row is
 // one contiguous block (whatever rows a GEMM tile gathers, its loads of a
@@ -158,14 +243,14 @@ __device__ __forceinline__ void quantize_block(const void* src, int row, int row
   }
 }
 
-// x [T][H] bf16 -> two E4M3 terms; block 0 also writes the tile plan: one
+// x [T][H] bf16 -> two E2M3 terms; block 0 also writes the tile plan: one
 // (slot, token tile) pair per token tile of every active expert with more
 // than reg_max rows, and the pair count in plan[0].
 __global__ __launch_bounds__(kThreads) void mfma_prep_kernel(const uint16_t* __restrict__ x, int T, int H,
                                                             const int32_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ active,
-                                                            uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
-                                                            int32_t* __restrict__ plan, int reg_max) {
+                                                            uint8_t* __restrict__ xq, int32_t* __restrict__ plan,
+                                                            int reg_max) {
   if (blockIdx.x == 0) {
     // Tile plan: the (slot, token tile) pairs of experts with more than
     // reg_max rows, heaviest first: tiles with 4 token groups (65..128
@@ -248,7 +333,7 @@ __global__ __launch_bounds__(kThreads) void mfma_prep_kernel(const uint16_t* __r
   const int nblk = H >> 5;
   const int64_t i = (int64_t)(blockIdx.x - 1) * kThreads + threadIdx.x;
   if (i >= (int64_t)T * nblk) return;
-  quantize_block<true>(x, (int)(i / nblk), T, (int)(i % nblk), H, xq, xs);
+  quantize_block_fp6(x, (int)(i / nblk), T, (int)(i % nblk), H, xq);
 }
 
 // h [R][I] fp32 -> two E4M3 terms, for every row
@@ -281,12 +366,12 @@ __global__ __launch_bounds__(kThreads) void quantize_h_kernel(const float* __res
 constexpr int kLdsBytes = 160 * 1024;
 constexpr int kScaleBuf = kTileRows * 16;
 
-template <int TG>
+template <int TG, bool FP6>
 struct Ring {
   static constexpr int kTok = 32 * TG;
   static constexpr int kA = kTileRows * 64;
   static constexpr int kB = 2 * kTok * 128;
-  static constexpr int kBS = 2 * kTok * 4;
+  static constexpr int kBS = FP6 ? 0 : 2 * kTok * 4;  // FP6 records carry their scales
   static constexpr int kStage = kA + kB + kBS;
   static constexpr int kSlots = TG == 1 ? 5 : TG == 2 ? 4 : 3;
   // a scale block is refilled only after the barrier that follows its last
@@ -294,12 +379,12 @@ struct Ring {
   static constexpr int kScaleBufs = (kSlots + 7 + 3) / 4;
   static constexpr int kScaleBase = kSlots * kStage;
   static constexpr int kBytes = kScaleBase + kScaleBufs * kScaleBuf;
-  static constexpr int kOps = 4 + 1 + 2 * TG + 1;  // DMA loads per wave per stage
+  static constexpr int kOps = 4 + 1 + 2 * TG + (FP6 ? 0 : 1);  // DMA loads per wave per stage
   static_assert(kStage % 16 == 0, "16-byte aligned slots");
   static_assert(kBytes <= kLdsBytes, "ring fits in LDS");
 };
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
-constexpr int kRingBytes = cmax(cmax(Ring<1>::kBytes, Ring<2>::kBytes), Ring<4>::kBytes);
+constexpr int kRingBytes = cmax(cmax(Ring<1, false>::kBytes, Ring<2, false>::kBytes), Ring<4, false>::kBytes);
 
 // LDS DMA loads of 16 and 4 bytes per lane to the wave-uniform LDS address
 // `lds` (lane l at lds + size*l).  Issued from asm, so the compiler neither
@@ -427,7 +512,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
   auto body = [&](auto tg_c) {
     constexpr int TG = decltype(tg_c)::value;
-    using G = Ring<TG>;
+    constexpr bool FP6 = GATEUP;  // gate/up: x in two E2M3 terms; down: h in two E4M3 terms
+    using G = Ring<TG, FP6>;
     constexpr int R = G::kSlots;
     constexpr int RBW = 2 * TG;  // row blocks of this wave
     const int tgi = wave % TG;
@@ -476,7 +562,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       else if constexpr (o == 4) issue_scales((st >> 2) + 1, st & 3);
       else if constexpr (o < 5 + 2 * TG)
         lds_dma16(bsrc[o - 5] + st * bq_stage, sb + G::kA + (wave + 4 * (o - 5)) * 1024);
-      else lds_dma4(bssrc + st * bs_stage, sb + G::kA + G::kB + tgi * 256);
+      else if constexpr (!FP6) lds_dma4(bssrc + st * bs_stage, sb + G::kA + G::kB + tgi * 256);
     };
     auto issue = [&](int st, int sl) { static_for<0, G::kOps>([&](auto o) { issue_op(st, sl, o); }); };
 
@@ -486,13 +572,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const uint32_t a_off[2] = {(uint32_t)((32 * rb_base + n) * 64 + 16 * ((0 + half) ^ ((n >> 2) & 3))),
                                (uint32_t)((32 * rb_base + n) * 64 + 16 * ((2 + half) ^ ((n >> 2) & 3)))};
     const uint32_t as_off = (uint32_t)((32 * rb_base + n) * 16);  // within a scale buffer
+    // E4M3: two 16-byte pieces 4s + 2 half + i; E2M3: the 16 bytes of piece
+    // 3s + half and the 8 bytes at 8 half in piece 3s + 2; its scale word at
+    // 4 half in piece 6 of the same record (bytes 0 and 2 for steps 0 and 1)
+    const int bsw = (n >> 1) & 7;
     uint32_t b_off[2][2];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        b_off[s][i] = (uint32_t)(G::kA + tt * 128 + 16 * ((4 * s + 2 * half + i) ^ ((n >> 1) & 7)));
-    const uint32_t bs_off = (uint32_t)(G::kA + G::kB + tt * 4);
+        b_off[s][i] = FP6 ? (uint32_t)(G::kA + tt * 128 + (i == 0 ? 16 * ((3 * s + half) ^ bsw)
+                                                                     : 16 * ((3 * s + 2) ^ bsw) + 8 * half))
+                          : (uint32_t)(G::kA + tt * 128 + 16 * ((4 * s + 2 * half + i) ^ bsw));
+    const uint32_t bs_off = FP6 ? (uint32_t)(G::kA + tt * 128 + 16 * (6 ^ bsw) + 4 * half)
+                                : (uint32_t)(G::kA + G::kB + tt * 4);
+    constexpr int kBSTerm = FP6 ? G::kTok * 128 : G::kTok * 4;  // scale words of term 1 after term 0's
+    constexpr int kBSShift = FP6 ? 0 : 1;  // E4M3 scale words need byte 2s + half moved to 2s
+    // one B fragment: E4M3 32 bytes, E2M3 24 (the high half's last 8 bytes zero)
+    auto ld_b = [&](const uint8_t* p, int i) -> uint4 {
+      if (FP6 && i == 1) {
+        const uint2 v = *(const uint2*)p;
+        return make_uint4(v.x, v.y, 0u, 0u);
+      }
+      return *(const uint4*)p;
+    };
 
     auto read_a = [&](int sl, int s, uint4 (&a)[RBW]) {
       const uint8_t* base = s_ring + sl * G::kStage + a_off[s];
@@ -503,7 +606,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int i = 0; i < 2; ++i) b[u][i] = *(const uint4*)(s_ring + sl * G::kStage + b_off[s][i] + u * G::kTok * 128);
+        for (int i = 0; i < 2; ++i) b[u][i] = ld_b(s_ring + sl * G::kStage + b_off[s][i] + u * G::kTok * 128, i);
     };
     // weight-scale words of stage st in LDS
     auto sa_base = [&](int st) -> const uint8_t* {
@@ -516,7 +619,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       for (int j = 0; j < RBW; ++j) sa[j] = *(const uint32_t*)(ab + 32 * rel(j) * 16) >> (8 * half);
 #pragma unroll
       for (int u = 0; u < 2; ++u)
-        sb[u] = *(const uint32_t*)(s_ring + sl * G::kStage + bs_off + u * G::kTok * 4) >> (8 * half);
+        sb[u] = *(const uint32_t*)(s_ring + sl * G::kStage + bs_off + u * kBSTerm) >> (8 * half * kBSShift);
     };
 
     v16f_t acc[RBW];
@@ -525,20 +628,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[j][i] = 0.0f;
 
-    // One 64-deep step: FP4 weights (format 4) times the two E4M3 terms
-    // (format 0), byte 2s of the scale words.
+    // One 64-deep step: FP4 weights (format 4) times the two activation
+    // terms (E2M3 format 2 or E4M3 format 0), byte 2s of the scale words.
+    constexpr int kBFmt = FP6 ? 2 : 0;
     auto mma = [&](auto s_c, const uint4 (&a)[RBW], const uint4 (&b)[2][2], const uint32_t (&sa)[RBW],
                    const uint32_t (&sb)[2]) {
       constexpr int OP = 2 * decltype(s_c)::value;
       const v8i_t B0 = pack_b(b[0][0], b[0][1]), B1 = pack_b(b[1][0], b[1][1]);
 #pragma unroll
-      for (int j = 0; j < RBW; ++j) {
-        v8i_t A;
-        A[0] = a[j].x; A[1] = a[j].y; A[2] = a[j].z; A[3] = a[j].w;
-        A[4] = 0; A[5] = 0; A[6] = 0; A[7] = 0;
-        acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B0, acc[j], 4, 0, OP, sa[j], OP, sb[0]);
-        acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B1, acc[j], 4, 0, OP, sa[j], OP, sb[1]);
-      }
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < RBW; ++j) {
+          v8i_t A;
+          A[0] = a[j].x; A[1] = a[j].y; A[2] = a[j].z; A[3] = a[j].w;
+          A[4] = 0; A[5] = 0; A[6] = 0; A[7] = 0;
+          acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, u == 0 ? B0 : B1, acc[j], 4, kBFmt, OP, sa[j],
+                                                                   OP, sb[u]);
+        }
     };
 
     // Pipeline over stages st (slot st % R).  The ring is filled R stages
@@ -563,38 +669,41 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     read_a(0, 0, a0);
     read_b(0, 0, b0);
     int st = 0, sl = 0;
-    // one MFMA pair (both terms) of row block j at step s
-    auto mma_j = [&](auto s_c, auto j_c, const uint4& a, const v8i_t& B0, const v8i_t& B1, uint32_t sa_j,
-                     const uint32_t (&sbw)[2]) {
+    // one MFMA of row block j at step s with activation term u
+    auto mma_ju = [&](auto s_c, auto j_c, auto u_c, const uint4& a, const v8i_t& Bu, uint32_t sa_j, uint32_t sb_u) {
       constexpr int OP = 2 * decltype(s_c)::value;
       constexpr int j = decltype(j_c)::value;
       v8i_t A;
       A[0] = a.x; A[1] = a.y; A[2] = a.z; A[3] = a.w;
       A[4] = 0; A[5] = 0; A[6] = 0; A[7] = 0;
-      acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B0, acc[j], 4, 0, OP, sa_j, OP, sbw[0]);
-      acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B1, acc[j], 4, 0, OP, sa_j, OP, sbw[1]);
+      acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, Bu, acc[j], 4, kBFmt, OP, sa_j, OP, sb_u);
     };
-    // Steady stage (a stage R ahead left to load).  Issue order, fixed by
-    // scheduling fences between row-block groups: step 0's MFMA pairs each
-    // followed by a share of the step-1 fragment reads; the wait and the
-    // barrier; step 1's MFMA pairs each followed by a share of the refill
-    // loads and of the next stage's step-0 and scale reads.  Vector-memory
-    // issues spread over the MFMAs this way never back up the address path
-    // far enough to hold up the next MFMA.
+    // Steady stage (a stage R ahead left to load).  A step's MFMAs run term
+    // major (term 0 of every row block, then term 1), so the two MFMAs that
+    // accumulate into one row block are RBW issues apart.  Issue order, fixed
+    // by scheduling fences between MFMAs: step 0's MFMAs each followed by a
+    // share of the step-1 fragment reads; the wait and the barrier; step 1's
+    // MFMAs each followed by a share of the refill loads and of the next
+    // stage's step-0 and scale reads.  Vector-memory issues spread over the
+    // MFMAs this way never back up the address path far enough to hold up
+    // the next MFMA.
     auto steady_stage = [&]() {
+      constexpr int kM = 2 * RBW;             // MFMAs per step
       constexpr int kReads1 = RBW + 4;        // step-1 fragments: RBW of A, 4 of B
       constexpr int kReadsN = RBW + 4 + RBW + 2;  // next stage: A, B fragments and scale words
       uint4 a1[RBW], b1[2][2];
       const v8i_t B0 = pack_b(b0[0][0], b0[0][1]), B1 = pack_b(b0[1][0], b0[1][1]);
       const uint8_t* a1_base = s_ring + sl * G::kStage + a_off[1];
-      static_for<0, RBW>([&](auto j_c) {
-        constexpr int j = decltype(j_c)::value;
-        mma_j(std::integral_constant<int, 0>(), j_c, a0[j], B0, B1, sa[j], sb);
-        static_for<j * kReads1 / RBW, (j + 1) * kReads1 / RBW>([&](auto r_c) {
+      static_for<0, kM>([&](auto i_c) {
+        constexpr int i = decltype(i_c)::value;
+        constexpr int u = i / RBW;
+        mma_ju(std::integral_constant<int, 0>(), std::integral_constant<int, i % RBW>(),
+               std::integral_constant<int, u>(), a0[i % RBW], u == 0 ? B0 : B1, sa[i % RBW], sb[u]);
+        static_for<i * kReads1 / kM, (i + 1) * kReads1 / kM>([&](auto r_c) {
           constexpr int r = decltype(r_c)::value;
           if constexpr (r < RBW) a1[r] = *(const uint4*)(a1_base + 32 * rel(r) * 64);
           else b1[(r - RBW) / 2][(r - RBW) % 2] =
-                   *(const uint4*)(s_ring + sl * G::kStage + b_off[1][(r - RBW) % 2] + ((r - RBW) / 2) * G::kTok * 128);
+                   ld_b(s_ring + sl * G::kStage + b_off[1][(r - RBW) % 2] + ((r - RBW) / 2) * G::kTok * 128, (r - RBW) % 2);
         });
         __builtin_amdgcn_sched_barrier(0);
       });
@@ -610,20 +719,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       const uint8_t* an_base = s_ring + nsl * G::kStage + a_off[0];
       const uint8_t* sn_base = s_ring + nsl * G::kStage;
       const uint8_t* san_base = sa_base(st + 1);
-      static_for<0, RBW>([&](auto j_c) {
-        constexpr int j = decltype(j_c)::value;
-        mma_j(std::integral_constant<int, 1>(), j_c, a1[j], C0, C1, sa1[j], sb1);
-        static_for<j * G::kOps / RBW, (j + 1) * G::kOps / RBW>([&](auto o_c) { issue_op(st + R, sl, o_c); });
-        static_for<j * kReadsN / RBW, (j + 1) * kReadsN / RBW>([&](auto r_c) {
+      static_for<0, kM>([&](auto i_c) {
+        constexpr int i = decltype(i_c)::value;
+        constexpr int u = i / RBW;
+        mma_ju(std::integral_constant<int, 1>(), std::integral_constant<int, i % RBW>(),
+               std::integral_constant<int, u>(), a1[i % RBW], u == 0 ? C0 : C1, sa1[i % RBW], sb1[u]);
+        static_for<i * G::kOps / kM, (i + 1) * G::kOps / kM>([&](auto o_c) { issue_op(st + R, sl, o_c); });
+        static_for<i * kReadsN / kM, (i + 1) * kReadsN / kM>([&](auto r_c) {
           constexpr int r = decltype(r_c)::value;
           if constexpr (r < RBW) a0[r] = *(const uint4*)(an_base + 32 * rel(r) * 64);
           else if constexpr (r < RBW + 4)
             b0[(r - RBW) / 2][(r - RBW) % 2] =
-                *(const uint4*)(sn_base + b_off[0][(r - RBW) % 2] + ((r - RBW) / 2) * G::kTok * 128);
+                ld_b(sn_base + b_off[0][(r - RBW) % 2] + ((r - RBW) / 2) * G::kTok * 128, (r - RBW) % 2);
           else if constexpr (r < 2 * RBW + 4)
             sa[r - RBW - 4] = *(const uint32_t*)(san_base + 32 * rel(r - RBW - 4) * 16) >> (8 * half);
           else
-            sb[r - 2 * RBW - 4] = *(const uint32_t*)(sn_base + bs_off + (r - 2 * RBW - 4) * G::kTok * 4) >> (8 * half);
+            sb[r - 2 * RBW - 4] = *(const uint32_t*)(sn_base + bs_off + (r - 2 * RBW - 4) * kBSTerm) >> (8 * half * kBSShift);
         });
         __builtin_amdgcn_sched_barrier(0);
       });
@@ -734,7 +845,7 @@ hipError_t launch_mfma_gateup(const uint16_t* x, int T, int k, const moe_mxfp4_w
   (void)hs;
   const int64_t nq = (int64_t)T * (H / 32);
   hipLaunchKernelGGL(mfma_prep_kernel, dim3(1 + (unsigned)((nq + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
-                     x, T, H, offsets, active, xq, xs, plan, reg_rows_max(T));
+                     x, T, H, offsets, active, xq, plan, reg_rows_max(T));
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int m_tiles = I / (kTileRows / 2);
