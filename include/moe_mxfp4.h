@@ -153,12 +153,12 @@ MOE_API moe_status moe_group_rows(const int32_t* topk_ids, int32_t T, int32_t k,
  *                  16-byte aligned
  *   workspace      device scratch, moe_workspace_bytes(T, k, E, H, I) bytes
  * Accumulation is fp32; the result agrees with the exact dequantized
- * product to well within rel-L2 2e-3.  In batches of up to 16 tokens a
- * token's rows for experts holding at most 4 of the batch's rows are bitwise
- * the same as when the token runs alone (a speculative-verify batch
- * reproduces the decode results); experts with more rows, or larger
- * batches, take the grouped MFMA GEMM, whose activations travel as two E4M3
- * terms per 32-value block (same bar, different rounding).
+ * product to well within rel-L2 2e-3.  In batches of up to 16 tokens every
+ * token's rows are bitwise the same as when the token runs alone (a
+ * speculative-verify batch reproduces the decode results).  In larger
+ * batches experts with more than one row take the grouped MFMA GEMM, whose
+ * activations travel as block-scaled terms per 32-value block (x in two
+ * E2M3 terms, h in two E4M3 terms: same bar, different rounding).
  */
 MOE_API moe_status moe_expert_ffn_mxfp4(const uint16_t* x, int32_t T, int32_t k, const moe_mxfp4_weights* w,
                                 const int32_t* expert_offsets, const int32_t* sorted_rows, const int32_t* active,

@@ -1229,8 +1229,11 @@ hipError_t expert_ffn_impl(const uint16_t* x, int T, int k, const moe_mxfp4_weig
   // (more than 8 blocks per lane) run on the LDS GEMV throughout.
   const GemvShape sg = gemv_shape(H >> 5, true), sd = gemv_shape(I >> 5, false);
   const bool reg_g = sg.ok, reg_d = sd.ok;
-  const bool use_mfma = T > 1 && reg_g && reg_d && mfma_shape_ok(H, I);
-  const int reg_max = use_mfma ? reg_rows_max(T) : kRegRows;
+  // up to kInvariantTokens tokens every expert stays on the register GEMVs
+  // (rows in passes of kRegRows), so no grouped-GEMM launch is made at all
+  const bool all_reg = T <= kInvariantTokens && reg_g && reg_d;
+  const bool use_mfma = !all_reg && T > 1 && reg_g && reg_d && mfma_shape_ok(H, I);
+  const int reg_max = all_reg ? INT32_MAX : use_mfma ? reg_rows_max(T) : kRegRows;
 
   hipError_t err = hipSuccess;
   const GemvArgs ga{x, k, &w, offsets, sorted_rows, active, hbuf, y_rows, s};
@@ -1265,7 +1268,7 @@ hipError_t expert_ffn_impl(const uint16_t* x, int T, int k, const moe_mxfp4_weig
       const GemvGrid gg = multi_grid(iters);
       gateup_reg<1>(ga, sg, gg, multi(n1_max, gg), l1, 1, 1);
       if ((err = hipGetLastError()) != hipSuccess) return err;
-      if (reg_max > 1) gateup_reg<kRegRows>(ga, sg, gg, multi(n4_max, gg), l4, 2, kRegRows);
+      if (reg_max > 1) gateup_reg<kRegRows>(ga, sg, gg, multi(n4_max, gg), l4, 2, reg_max);
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
@@ -1274,7 +1277,7 @@ hipError_t expert_ffn_impl(const uint16_t* x, int T, int k, const moe_mxfp4_weig
   if (use_mfma) {
     if ((err = launch_mfma_gateup(x, T, k, w, offsets, sorted_rows, active, hbuf, mfma_ws, s)) != hipSuccess)
       return err;
-  } else if (!reg_g || T > 1) {
+  } else if (!reg_g || (T > 1 && !all_reg)) {
     const int mt_g = pick_mt((size_t)H * 2);
     dim3 grid_g((I + kRowsPerBlock - 1) / kRowsPerBlock, max_active);
     const size_t lds_g = (size_t)mt_g * H * 2;
@@ -1307,14 +1310,14 @@ hipError_t expert_ffn_impl(const uint16_t* x, int T, int k, const moe_mxfp4_weig
       const GemvGrid gd = multi_grid(iters);
       down_reg<1>(ga, sd, gd, multi(n1_max, gd), l1, 1, 1);
       if ((err = hipGetLastError()) != hipSuccess) return err;
-      if (reg_max > 1) down_reg<kRegRows>(ga, sd, gd, multi(n4_max, gd), l4, 2, kRegRows);
+      if (reg_max > 1) down_reg<kRegRows>(ga, sd, gd, multi(n4_max, gd), l4, 2, reg_max);
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (use_mfma) {
     if ((err = launch_mfma_down(T, k, w, offsets, sorted_rows, active, hbuf, y_rows, mfma_ws, s)) != hipSuccess)
       return err;
-  } else if (!reg_d || T > 1) {
+  } else if (!reg_d || (T > 1 && !all_reg)) {
     const int mt_d = pick_mt((size_t)I * 4);
     dim3 grid_d((H + kRowsPerBlock - 1) / kRowsPerBlock, max_active);
     const size_t lds_d = (size_t)mt_d * I * 4;

@@ -13,12 +13,13 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 #define MOE_WAVE 64
 
-// Experts with at most reg_rows_max(T) routed rows run on the register GEMV
-// kernels; more rows per expert take the grouped GEMM (MFMA) path.  Up to
-// kInvariantTokens tokens the GEMV keeps experts of up to kRegRows rows, so
-// a token's rows come out bitwise the same alone or in such a batch; larger
-// batches keep only one-row experts there, since applying a weight chunk to
-// 2..4 rows makes the GEMV compute-bound while the GEMM stays memory-bound.
+// Up to kInvariantTokens tokens every expert runs on the register GEMV
+// kernels (rows in passes of kRegRows, each row with the arithmetic a single
+// row gets), so a token's rows come out bitwise the same alone or in such a
+// batch.  In larger batches experts with more than reg_rows_max(T) routed
+// rows take the grouped GEMM (MFMA) path: only one-row experts stay on the
+// GEMV, since applying a weight chunk to 2..4 rows makes the GEMV
+// compute-bound while the GEMM stays memory-bound.
 constexpr int kRegRows = 4;
 constexpr int kInvariantTokens = 16;
 inline int reg_rows_max(int T) { return T > kInvariantTokens ? 1 : kRegRows; }

@@ -199,9 +199,35 @@ def test_verify8(pool896):
     gpu, ref, x, logits = _full_case(wl, pool896)
     # each token alone (batch 1) gives the same bits as inside the batch
     one = synth.Workload("verify8_single", E=wl.E, H=wl.H, I=wl.I, k=wl.k, T=1, pool=wl.pool)
-    for t in (0, 5):
+    for t in range(wl.T):
         single = run_gpu_layer(one, pool896, x[t:t + 1], logits[t:t + 1])
         assert np.array_equal(single["out"][0], gpu["out"][t]), f"token {t}: batch-1 bits differ from batch-8"
+
+
+def test_batch_invariance_with_shared_experts():
+    """Up to 16 tokens every expert stays on the register GEMVs, rows in
+    passes of four: with 12 tokens all routed to the same 16 experts (12 rows
+    each, three passes) every token's output equals its batch-1 bits, and the
+    batch matches the oracle."""
+    wl = synth.Workload("shared12", E=32, H=7168, I=1536, k=16, T=12, logits="dense16", pool=37, sub=37)
+    say(f"case {wl.name}: E={wl.E} k={wl.k} T={wl.T}, every token on experts 0..15")
+    pool = device_pool(wl)
+    x = synth.activations_bf16(0, wl)
+    logits = synth.router_logits(0, wl)
+    gpu = run_gpu_layer(wl, pool, x, logits)
+    rt = _ref_routing(wl, logits)
+    check_routing(gpu, rt, wl.E)
+    assert np.diff(rt["expert_offsets"])[:16].min() == 12  # every expert of the 16: three passes of four rows
+    hpool = host_pool_subset(wl, rt["ids"].reshape(-1))
+    ref = oracle.layer(x, logits, wl.k, hpool, nthreads=NTH)
+    assert_close(gpu["y_rows"], ref["y_rows"], "y_rows")
+    assert_close(gpu["out"], ref["out"], "out")
+    one = synth.Workload("shared12_single", E=wl.E, H=wl.H, I=wl.I, k=wl.k, T=1, pool=wl.pool)
+    for t in range(wl.T):
+        single = run_gpu_layer(one, pool, x[t:t + 1], logits[t:t + 1])
+        assert np.array_equal(single["out"][0], gpu["out"][t]), f"token {t}: batch-1 bits differ from batch-12"
+    del pool
+    torch.cuda.empty_cache()
 
 
 def _sample_tokens(ref, T, k, n_hot=4, n_cold=4):
