@@ -296,7 +296,7 @@ constexpr uint32_t kPastEnd = 0x80000000u;
 __global__ __launch_bounds__(kThreads) void small_lists_kernel(const int32_t* __restrict__ offsets,
                                                               const int32_t* __restrict__ active,
                                                               int32_t* __restrict__ l1, int32_t* __restrict__ l4,
-                                                              int reg_max) {
+                                                              int lo4, int reg_max) {
   __shared__ int s_part[2][kWaves];
   const int na = active[0];
   const int lane = threadIdx.x & (MOE_WAVE - 1), wave = threadIdx.x / MOE_WAVE;
@@ -307,8 +307,8 @@ __global__ __launch_bounds__(kThreads) void small_lists_kernel(const int32_t* __
     if (a < na) {
       const int e = active[1 + a];
       const int cnt = offsets[e + 1] - offsets[e];
-      f1 = cnt == 1;
-      f4 = cnt >= 2 && cnt <= reg_max;
+      f1 = cnt == 1 && lo4 > 1;
+      f4 = cnt >= lo4 && cnt <= reg_max;
     }
     int v1 = f1, v4 = f4;
 #pragma unroll
@@ -1234,6 +1234,9 @@ hipError_t expert_ffn_impl(const uint16_t* x, int T, int k, const moe_mxfp4_weig
   const bool all_reg = T <= kInvariantTokens && reg_g && reg_d;
   const bool use_mfma = !all_reg && T > 1 && reg_g && reg_d && mfma_shape_ok(H, I);
   const int reg_max = all_reg ? INT32_MAX : use_mfma ? reg_rows_max(T) : kRegRows;
+  // fewest rows of the multi-row class: with every expert on the GEMVs one
+  // launch per projection takes them all (one-row experts get a single pass)
+  const int lo4 = all_reg ? 1 : 2;
 
   hipError_t err = hipSuccess;
   const GemvArgs ga{x, k, &w, offsets, sorted_rows, active, hbuf, y_rows, s};
@@ -1244,8 +1247,8 @@ hipError_t expert_ffn_impl(const uint16_t* x, int T, int k, const moe_mxfp4_weig
     l1 = (int32_t*)((uint8_t*)ws + off);
     l4 = l1 + 1 + max_active;
     off += lists_bytes(T, k, E);
-    if (reg_g || reg_d) {
-      hipLaunchKernelGGL(small_lists_kernel, dim3(1), dim3(kThreads), 0, s, offsets, active, l1, l4, reg_max);
+    if ((reg_g || reg_d) && !all_reg) {  // with every expert on the GEMVs the active list is the class list
+      hipLaunchKernelGGL(small_lists_kernel, dim3(1), dim3(kThreads), 0, s, offsets, active, l1, l4, lo4, reg_max);
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
   }
@@ -1254,7 +1257,7 @@ hipError_t expert_ffn_impl(const uint16_t* x, int T, int k, const moe_mxfp4_weig
     const long b = (long)n_max * gg.blocks_per_expert;
     return dim3((unsigned)(b < kMultiGridCap ? b : kMultiGridCap));
   };
-  const int n1_max = max_active, n4_max = R / 2 < max_active ? R / 2 : max_active;
+  const int n1_max = lo4 > 1 ? max_active : 0, n4_max = lo4 > 1 && R / 2 < max_active ? R / 2 : max_active;
   if (reg_g) {
     const int rows_it = (64 >> sg.lg) * sg.U, iters = (I + rows_it - 1) / rows_it;
     if (T == 1) {
@@ -1266,9 +1269,12 @@ hipError_t expert_ffn_impl(const uint16_t* x, int T, int k, const moe_mxfp4_weig
         gateup_reg<1>(ga, sg, gg, dim3(max_active * gg.blocks_per_expert), nullptr, 1, INT32_MAX);
     } else {
       const GemvGrid gg = multi_grid(iters);
-      gateup_reg<1>(ga, sg, gg, multi(n1_max, gg), l1, 1, 1);
+      if (n1_max > 0) gateup_reg<1>(ga, sg, gg, multi(n1_max, gg), l1, 1, 1);
       if ((err = hipGetLastError()) != hipSuccess) return err;
-      if (reg_max > 1) gateup_reg<kRegRows>(ga, sg, gg, multi(n4_max, gg), l4, 2, reg_max);
+      if (all_reg)  // one block per (active slot, block of the expert), no list
+        gateup_reg<kRegRows>(ga, sg, gg, dim3(max_active * gg.blocks_per_expert), nullptr, 1, reg_max);
+      else if (reg_max > 1)
+        gateup_reg<kRegRows>(ga, sg, gg, multi(n4_max, gg), l4, lo4, reg_max);
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
@@ -1308,9 +1314,12 @@ hipError_t expert_ffn_impl(const uint16_t* x, int T, int k, const moe_mxfp4_weig
       down_reg<1>(ga, sd, gd, dim3(max_active * gd.blocks_per_expert), nullptr, 1, INT32_MAX);
     } else {
       const GemvGrid gd = multi_grid(iters);
-      down_reg<1>(ga, sd, gd, multi(n1_max, gd), l1, 1, 1);
+      if (n1_max > 0) down_reg<1>(ga, sd, gd, multi(n1_max, gd), l1, 1, 1);
       if ((err = hipGetLastError()) != hipSuccess) return err;
-      if (reg_max > 1) down_reg<kRegRows>(ga, sd, gd, multi(n4_max, gd), l4, 2, reg_max);
+      if (all_reg)
+        down_reg<kRegRows>(ga, sd, gd, dim3(max_active * gd.blocks_per_expert), nullptr, 1, reg_max);
+      else if (reg_max > 1)
+        down_reg<kRegRows>(ga, sd, gd, multi(n4_max, gd), l4, lo4, reg_max);
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
