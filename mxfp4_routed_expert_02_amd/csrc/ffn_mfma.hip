@@ -254,8 +254,9 @@ __global__ __launch_bounds__(kThreads) void mfma_prep_kernel(const uint16_t* __r
   if (blockIdx.x == 0) {
     // Tile plan: the (slot, token tile) pairs of experts with more than
     // reg_max rows, heaviest first: tiles with 4 token groups (65..128
-    // rows), then 2 (33..64), then 1 (5..32).  The GEMM deals pair g to XCD
-    // g % 8, so every XCD gets a near-equal share of each class and starts
+    // rows), then 2 (33..64), then 1 (up to 32).  The GEMM deals the pairs to
+    // the XCDs in bands of eight runs of kBand neighbours (the rest one by
+    // one), so every XCD gets a near-equal share of each class and starts
     // with its heaviest tiles.  Within a class pairs keep slot order, so
     // the plan is deterministic.
     __shared__ int s_part[3][kThreads / 64];
