@@ -782,14 +782,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 // One token, I = 32*NB, k <= kFMaxK: the down projection of every routed
 // expert and the weighted combine in one launch (the step after gate/up at
 // decode).  Block b owns output rows [kRows*b, kRows*b + kRows) of every
-// active expert.  The h rows of all active experts sit in LDS; each wave
-// takes (expert, 4-row iteration) items round robin with the rolling
-// prefetch of the kernels above, and every row's y (the arithmetic of the
-// down GEMVs: G lanes per row, per-block scaled partial sums, DPP
-// reduction) goes to y_rows and to an LDS tile indexed by sorted row.  After
-// one barrier, kRows threads form out[n] = sum_j w[j] * y[row_pos[j]][n]
-// with j ascending, the combine kernel's arithmetic, so both outputs equal
-// the separate down and combine launches bit for bit.
+// active expert.  Each wave serves one slot (16 / na waves per slot, na the
+// number of active experts, rounded down): it stages that slot's h row in
+// its own LDS planes and starts on its rows as soon as they are in, with no
+// block barrier before the first dot, so a wave whose h arrives early is not
+// held by the rest of the block's h rows.  Every row's y (the arithmetic of
+// the down GEMVs: G lanes per row, per-block scaled partial sums, DPP
+// reduction, rolling prefetch of the wave's next row iteration) goes to
+// y_rows and to an LDS tile indexed by sorted row.  After one barrier, kRows
+// threads form out[n] = sum_j w[j] * y[row_pos[j]][n] with j ascending, the
+// combine kernel's arithmetic, so both outputs equal the separate down and
+// combine launches bit for bit.
 constexpr int kFThreads = 1024;
 constexpr int kFWaves = kFThreads / MOE_WAVE;
 constexpr int kFIters = 7;  // 4-row iterations per block and expert
@@ -802,86 +805,76 @@ __global__ __launch_bounds__(kFThreads) void down_combine_one_kernel(
     int k, float* __restrict__ y_rows, float* __restrict__ out) {
   constexpr int nb = NB, I = 32 * NB, lg = ctz_const(NB), G = 1 << lg, J = NB / G, rpi = MOE_WAVE >> lg;
   constexpr int kRows = kFIters * rpi;  // output rows per block
+  constexpr int kH4 = 8 * NB;           // float4 of an h row
   static_assert(J * G == NB && J <= 8, "register lane layout");
+  static_assert(kH4 % MOE_WAVE == 0, "h row in whole wave loads");
   constexpr uint32_t qrow = (uint32_t)I >> 1;
-  __shared__ float4 s_h4[kFMaxK][8 * NB];  // h of each active expert, planes [8][NB]
-  __shared__ float s_y[kFMaxK][kRows];     // y of this block's rows, by sorted row
+  __shared__ float4 s_h4[kFWaves][kH4];  // h of each wave's slot, planes [8][NB]
+  __shared__ float s_y[kFMaxK][kRows];   // y of this block's rows, by sorted row
   const int H = w.hidden;
   const int na = active[0];
-  const int lane = threadIdx.x & (MOE_WAVE - 1), wave = threadIdx.x / MOE_WAVE;
+  const int lane = threadIdx.x & (MOE_WAVE - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / MOE_WAVE);
   const int li = lane & (G - 1), gi = lane >> lg;
   const int n_base = blockIdx.x * kRows;
-  const int n_items = na * kFIters;
-  // lane s < na holds slot s's expert id, first sorted row and row count
-  int e_l = 0, p0_l = 0, cnt_l = 0;
-  if (lane < na) {
-    e_l = active[1 + lane];
-    p0_l = offsets[e_l];
-    cnt_l = offsets[e_l + 1] - p0_l;
-  }
-  uint4 q[J];
-  uint32_t sc[J];
-  __amdgpu_buffer_rsrc_t rq, rs;
-  uint32_t bq = 0, bs = 0;
-  // rsrc and row offsets of an item (wave-uniform); items past the last get
-  // the last slot's matrix and kPastEnd, so their loads touch no memory
-  auto set_item = [&](int item) {
-    const int slot = min(item / kFIters, na - 1), itr = item - (item / kFIters) * kFIters;
-    const int e = __builtin_amdgcn_readlane(e_l, slot);
+  // the waves split evenly over the slots: wave w takes slot w / wps and
+  // that slot's row iterations w % wps, w % wps + wps, ...
+  const int wps = kFWaves / na;
+  const int slot = wave / wps;
+  int itr = wave - slot * wps;  // the wave's first row iteration
+  if (slot < na && itr < kFIters) {
+    const int e = active[1 + slot];
+    const int p0 = offsets[e], cnt = offsets[e + 1] - p0;
     const int64_t eo = (int64_t)e * w.expert_stride;
-    rq = make_rsrc(w.down_q + eo, (uint32_t)H * qrow);
-    rs = make_rsrc(w.down_s + eo, (uint32_t)(H * nb));
-    const int n = n_base + itr * rpi + gi;
-    const uint32_t off = item < n_items ? 0u : kPastEnd;
-    bq = (uint32_t)n * qrow + 16u * li + off;
-    bs = (uint32_t)(n * nb + li) + off;
-  };
-  auto load_chunk = [&](int j) {
-    q[j] = load16(rq, bq + 16u * G * j);
-    sc[j] = load1(rs, bs + G * j);
-  };
-  set_item(wave);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(w.down_q + eo, (uint32_t)H * qrow);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(w.down_s + eo, (uint32_t)(H * nb));
+    const uint32_t vq0 = 16u * li, vs0 = (uint32_t)li;
+    uint4 q[J];
+    uint32_t sc[J];
+    // chunk j of row iteration itr (past the last: no memory access)
+    auto load_chunk = [&](int itr, int j) {
+      const int n = n_base + itr * rpi + gi;
+      const uint32_t off = itr < kFIters ? 0u : kPastEnd;
+      q[j] = load16(rq, vq0 + (uint32_t)n * qrow + off + 16u * G * j);
+      sc[j] = load1(rs, vs0 + (uint32_t)(n * nb) + off + G * j);
+    };
 #pragma unroll
-  for (int j = 0; j < J; ++j) load_chunk(j);
-  // all h loads of a thread in flight together (slots past na re-read the
-  // last slot's row and are not stored)
-  constexpr int kHPer = (kFMaxK * 8 * NB + kFThreads - 1) / kFThreads;
-  float4 hv[kHPer];
+    for (int j = 0; j < J; ++j) load_chunk(itr, j);
+    const float4* h4 = (const float4*)(h + (int64_t)p0 * I);
+    float4 hv[kH4 / MOE_WAVE];
 #pragma unroll
-  for (int i = 0; i < kHPer; ++i) {
-    const int c = threadIdx.x + kFThreads * i;
-    const int s = min(c / (8 * NB), na - 1), cc = c % (8 * NB);
-    hv[i] = ((const float4*)(h + (int64_t)__shfl(p0_l, s, MOE_WAVE) * I))[cc];
-  }
+    for (int i = 0; i < kH4 / MOE_WAVE; ++i) hv[i] = h4[lane + MOE_WAVE * i];
+    float4* sh = s_h4[wave];
 #pragma unroll
-  for (int i = 0; i < kHPer; ++i) {
-    const int c = threadIdx.x + kFThreads * i;
-    const int s = c / (8 * NB), cc = c % (8 * NB);
-    if (s < na) s_h4[s][(cc & 7) * nb + (cc >> 3)] = hv[i];
-  }
-  __syncthreads();
-  for (int item = wave; item < n_items; item += kFWaves) {
-    const int slot = item / kFIters, itr = item - slot * kFIters;
-    const int n = n_base + itr * rpi + gi;
-    set_item(item + kFWaves);
-    float acc = 0.0f;
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      float4 hr[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) hr[i] = s_h4[slot][i * nb + li + G * j];
-      f32x2_t wv[16];
-      dequant_f32(q[j], wv);
-      acc += chunk_dot_f32_reg(wv, hr) * e8m0_to_f32(sc[j]);
-      load_chunk(j);  // chunk j of the wave's next item
-      __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < kH4 / MOE_WAVE; ++i) {
+      const int c = lane + MOE_WAVE * i;
+      sh[(c & 7) * nb + (c >> 3)] = hv[i];
     }
-    const float v = group_sum_last(acc, G);
-    const int p0 = __builtin_amdgcn_readlane(p0_l, slot), cnt = __builtin_amdgcn_readlane(cnt_l, slot);
-    if (li == G - 1 && n < H) {
-      for (int r = 0; r < cnt; ++r) {
-        y_rows[(int64_t)(p0 + r) * H + n] = v;
-        s_y[p0 + r][n - n_base] = v;
+    // the wave reads only what its own lanes wrote: LDS keeps a wave's
+    // accesses in order, so only the compiler's order needs the fence
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (; itr < kFIters; itr += wps) {
+      const int n = n_base + itr * rpi + gi;
+      float acc = 0.0f;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        float4 hr[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hr[i] = sh[i * nb + li + G * j];
+        f32x2_t wv[16];
+        dequant_f32(q[j], wv);
+        acc += chunk_dot_f32_reg(wv, hr) * e8m0_to_f32(sc[j]);
+        load_chunk(itr + wps, j);  // chunk j of the wave's next iteration
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const float v = group_sum_last(acc, G);
+      if (li == G - 1 && n < H) {
+        for (int r = 0; r < cnt; ++r) {
+          y_rows[(int64_t)(p0 + r) * H + n] = v;
+          s_y[p0 + r][n - n_base] = v;
+        }
       }
     }
   }
