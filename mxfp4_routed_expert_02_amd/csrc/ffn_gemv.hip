@@ -890,11 +890,11 @@ __global__ __launch_bounds__(kFThreads) void down_combine_one_kernel(
 }
 
 // One token routed inside the gate/up launch, in blocks of 16 waves (one
-// block per CU at 4 waves per SIMD): the first four waves run the token's
-// four-wave top-k (the routing kernels' device code, so the picks are theirs
-// bit for bit; one top-k per CU rather than one per 4-wave block) while the
-// others wait, then every wave takes the expert of the
-// block's slot, the slot-th smallest picked id (the active list the
+// block per CU at 4 waves per SIMD): the block first runs the token's top-k
+// (topk_block_wide: its first four waves hold the logits; the picks equal
+// the routing kernels' bit for bit, the top k being unique; one top-k per
+// CU rather than one per 4-wave block), then every wave takes the expert of
+// the block's slot, the slot-th smallest picked id (the active list the
 // grouping writes; the picks are distinct, so that expert's one row sits at
 // sorted position `slot`).  The blocks also write the routing weights and
 // the grouping, equal to what the fused route + group kernel writes.  The
@@ -917,7 +917,7 @@ __global__ __launch_bounds__(kRGThreads) void route_gateup_one_kernel(
     int32_t* __restrict__ row_pos, int32_t* __restrict__ active, int blocks_per_expert) {
   static_assert(kRGThreads == kRmsThreads, "the block is the rescale's layout");
   extern __shared__ uint4 s_x4[];  // [4][NB]
-  __shared__ TopkLds s;
+  __shared__ TopkWideLds<C> s;
   constexpr int kN4 = 8 * NB;  // float4 (and half-uint4) of a row
   static_assert(4 * NB <= kRGThreads && kN4 <= kRmsVec * kRmsThreads, "x staging layout");
   constexpr int kIV = (kN4 + kRmsThreads - 1) / kRmsThreads;  // float4 per thread in the rescale's layout
@@ -934,7 +934,22 @@ __global__ __launch_bounds__(kRGThreads) void route_gateup_one_kernel(
   } else {
     if (tx < 4 * NB) xs = ((const uint4*)x)[tx];
   }
-  topk_block<C, false>(logits, E, k, s);
+  // x (non-RMS) or the RMS partial sums go into LDS while the logits loads
+  // are in flight, before the top-k's first barrier
+  __shared__ float s_part[kRmsThreads / MOE_WAVE];
+  const int lane = tx & (MOE_WAVE - 1), wave = tx / MOE_WAVE;
+  auto pre = [&]() {
+    if constexpr (RMS) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kIV; ++i) ss += sumsq4(yv[i]);  // the layout's later float4 are all zero
+      ss = wave_sum(ss);
+      if (lane == 0) s_part[wave] = ss;
+    } else {
+      if (tx < 4 * NB) s_x4[(tx & 3) * NB + (tx >> 2)] = xs;
+    }
+  };
+  topk_block_wide<C>(logits, E, k, s, pre);
   // the k <= 16 pick ids (padded with INT_MAX) in registers: 4 LDS reads
   static_assert(kFMaxK == 16, "four int4 of pick ids");
   int4 pv[4];
@@ -965,7 +980,6 @@ __global__ __launch_bounds__(kRGThreads) void route_gateup_one_kernel(
     offsets[e] = picks_below<4>(pv, e);
   const int slot = blockIdx.x / blocks_per_expert;
   if (slot >= k) return;
-  const int lane = tx & (MOE_WAVE - 1), wave = tx / MOE_WAVE;
   // lane j < k: pick j's id and its rank among the picks by id
   int pid = INT_MAX, prank = -1;
   if (lane < k) {
@@ -1003,14 +1017,7 @@ __global__ __launch_bounds__(kRGThreads) void route_gateup_one_kernel(
   for (int j = 0; j < J; ++j)
 #pragma unroll
     for (int u = 0; u < U; ++u) load_chunk(it0, u, j, it0 < it1 ? 0u : kPastEnd);
-  if constexpr (RMS) {
-    __shared__ float s_part[kRmsThreads / MOE_WAVE];
-    float ss = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kIV; ++i) ss += sumsq4(yv[i]);  // the layout's later float4 are all zero
-    ss = wave_sum(ss);
-    if (lane == 0) s_part[wave] = ss;
-    __syncthreads();
+  if constexpr (RMS) {  // x = bf16(y_prev * factor) into LDS while the first weight loads are in flight
     float tot = 0.0f;
 #pragma unroll
     for (int i = 0; i < kRmsThreads / MOE_WAVE; ++i) tot += s_part[i];
@@ -1028,10 +1035,8 @@ __global__ __launch_bounds__(kRGThreads) void route_gateup_one_kernel(
         if (blockIdx.x == 0) ((uint2*)x_next)[c] = make_uint2(lo, hi);
       }
     }
-  } else {
-    if (tx < 4 * NB) s_x4[(tx & 3) * nb + (tx >> 2)] = xs;
+    __syncthreads();
   }
-  __syncthreads();
   for (int it = it0; it < it1; it += istep) {
     const uint32_t next_off = it + istep < it1 ? 0u : kPastEnd;
     const int n0 = it * rows_it;
@@ -1387,9 +1392,12 @@ hipError_t launch_route_ffn_combine_one(const float* logits, int k, const uint16
                      logits, E, k, x, y_prev, eps, x_next, w, hbuf, ids, topk_w, offsets, sorted_rows, row_pos,     \
                      active, bpe)
   const bool rms = y_prev != nullptr;
-  if (E <= 4 * MOE_WAVE * 2) {
+  static_assert(kWideThreads * 8 >= kRegExperts, "C <= 8 covers every fused E");
+  if (E <= kWideThreads) {
+    if (rms) RG(1, true); else RG(1, false);
+  } else if (E <= 2 * kWideThreads) {
     if (rms) RG(2, true); else RG(2, false);
-  } else if (E <= 4 * MOE_WAVE * 4) {
+  } else if (E <= 4 * kWideThreads) {
     if (rms) RG(4, true); else RG(4, false);
   } else {
     if (rms) RG(8, true); else RG(8, false);

@@ -1,7 +1,8 @@
-// topk_device.h - the four-wave top-k of one token's router logits and the
-// grouping of its k distinct picks, as device functions shared by the
-// routing kernels and the one-token kernel that routes inside the expert-FFN
-// launch (gfx950).  Included by HIP sources only, after moe_internal.h.
+// topk_device.h - the top-k of one token's router logits (a four-wave form
+// for the routing kernels, a wide form for the one-token kernel that routes
+// inside the expert-FFN launch) and the grouping of its k distinct picks, as
+// device functions (gfx950).  Included by HIP sources only, after
+// moe_internal.h.
 #pragma once
 
 #include <climits>
@@ -38,7 +39,7 @@ __device__ __forceinline__ uint32_t order_key(float v) {
 // Keys of absent experts are 0, below every finite logit, and never picked.
 constexpr int kRoute4Threads = 256;
 constexpr int kList = MOE_MAX_TOPK;  // LDS stride of one wave's list
-constexpr int kRegExperts = 4 * MOE_WAVE * 8;  // widest register top-k (C = 8)
+constexpr int kRegExperts = 4 * MOE_WAVE * 8;  // widest register top-k (four waves of C = 8; eight of C = 4)
 
 // (key, id) in one word: a larger word is a larger key, then a lower id.
 __device__ __forceinline__ uint64_t pick_word(uint32_t key, int id) {
@@ -185,9 +186,149 @@ __device__ __forceinline__ void topk_block(const float* __restrict__ row, int E,
   __syncthreads();
 }
 
+// One token's top-k for the one-token kernels, where the selection's
+// latency is on every block's critical path.  The first four waves (one per
+// SIMD, so no SIMD interleaves two selections) hold the experts, 16-lane row
+// r (thread t = 16r + j) experts r + 16j + 256i, i < C, so that from E = 16
+// on every row holds one:
+//   1. each 16-lane row's largest key; tau, the smallest of the 16 row
+//      maxima, has at least 16 keys at or above it (one per row; with fewer
+//      than k rows holding an expert, tau = 1 and every expert qualifies),
+//      so for k <= 16 every top-k expert is among the keys >= tau;
+//   2. each wave compacts its experts with key >= tau (absent experts have
+//      key 0 and never qualify) into its own LDS region of (key, ~id)
+//      words, by ballots;
+//   3. a candidate's rank is the number of candidate words above its own
+//      (larger key first, then the lower id): its wave gives it 4 lanes,
+//      lane p counting in wave p's region, so ranks 0..k-1 are the top k in
+//      order and each pick lands in its slot.
+// The picks are those of topk_block bit for bit: the top k under this order
+// is unique.  The candidate count is a few times k for spread-out logits and
+// at most E (many equal logits); step 3 costs its square in word compares.
+// pre() runs in every thread once the logits loads are in flight and before
+// the first block barrier (the caller's own staging, overlapping their
+// latency); three block barriers in all.
+constexpr int kWideThreads = 4 * MOE_WAVE;  // threads holding experts
+
+template <int C>
+struct TopkWideLds {
+  static constexpr int kRegion = MOE_WAVE * C + 2;  // a wave's candidates, a zero pad and a spare word
+  static_assert(kRegion >= 16, "the ranking reads 16 words of every region at once");
+  alignas(16) uint32_t rmax[16];  // largest key of each 16-lane row (0: the row holds none)
+  alignas(16) uint32_t cnt[4];    // candidates per wave
+  alignas(16) uint2 cand[4 * kRegion];  // (~id, key): the word's low and high halves
+  uint32_t pick_key[kList];            // picks in rank order
+  alignas(16) int32_t pick_id[kList];  // padded with INT_MAX
+};
+
+template <int C, class Pre>
+__device__ __forceinline__ void topk_block_wide(const float* __restrict__ row, int E, int k, TopkWideLds<C>& s,
+                                                Pre pre) {
+  constexpr int kRegion = TopkWideLds<C>::kRegion;
+  const int tid = threadIdx.x;
+  const int lane = tid & (MOE_WAVE - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / MOE_WAVE);  // uniform: wave branches
+  const bool holder = wave < 4;
+  const int eb = 16 * (tid & 15) + (tid >> 4);  // this thread's first expert
+  float lv[C];
+  if (holder) {
+#pragma unroll
+    for (int i = 0; i < C; ++i) lv[i] = row[min(eb + kWideThreads * i, E - 1)];
+  }
+  pre();
+  uint64_t v[C];
+  if (holder) {
+    uint32_t m = 0u;
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+      const int e = eb + kWideThreads * i;
+      v[i] = pick_word(e < E ? order_key(lv[i]) : 0u, e);
+      m = max(m, (uint32_t)(v[i] >> 32));
+    }
+    m = max(m, dpp_u32<0x111>(m));  // row maxima land in each row's last lane
+    m = max(m, dpp_u32<0x112>(m));
+    m = max(m, dpp_u32<0x114>(m));
+    m = max(m, dpp_u32<0x118>(m));
+    if ((lane & 15) == 15) s.rmax[4 * wave + (lane >> 4)] = m;
+    if (wave == 0 && lane >= k && lane < kList) s.pick_id[lane] = INT_MAX;
+  }
+  __syncthreads();
+  if (holder) {
+    uint32_t tau = ~0u;
+    int rows = 0;  // rows holding an expert
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 r4 = ((const uint4*)s.rmax)[q];
+      const uint32_t r[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        tau = r[i] != 0u ? min(tau, r[i]) : tau;
+        rows += r[i] != 0u;
+      }
+    }
+    if (rows < k) tau = 1u;
+    int pos = 0, total = 0;  // candidates of the lanes below this one, of the whole wave
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+      const uint64_t bal = __ballot((uint32_t)(v[i] >> 32) >= tau);
+      pos += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+      total += __popcll(bal);
+    }
+    uint2* reg = s.cand + wave * kRegion;
+    // the lane's candidates follow those of the lanes below, in i order; a
+    // non-candidate goes to the region's spare last word, which nothing reads
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+      const bool c = (uint32_t)(v[i] >> 32) >= tau;
+      reg[c ? pos : kRegion - 1] = make_uint2((uint32_t)v[i], (uint32_t)(v[i] >> 32));
+      pos += c;
+    }
+    if (lane == 0) {
+      reg[total] = make_uint2(0u, 0u);  // pads the region's last pair: below every word
+      s.cnt[wave] = (uint32_t)total;
+    }
+  }
+  __syncthreads();
+  if (holder) {
+    const int q = lane >> 2, p = lane & 3;
+    const int nc = (int)s.cnt[wave];  // this wave's candidates, sixteen at a time
+    const int np = (int)s.cnt[p];     // entries of the region lane p counts in
+    const uint2* mine = s.cand + wave * kRegion;
+    const uint4* other = (const uint4*)(s.cand + p * kRegion);
+    for (int i = q; i - q < nc; i += 16) {  // the same trip count in the whole wave
+      const uint2 w2 = mine[min(i, nc)];
+      const uint64_t W = (uint64_t)w2.y << 32 | w2.x;
+      // the region's first 16 entries in one batch of independent reads (the
+      // region holds at least 66 words, so they stay inside it; words past
+      // np are not counted), then any further ones pair by pair
+      uint4 o8[8];
+#pragma unroll
+      for (int b = 0; b < 8; ++b) o8[b] = other[b];
+      int r = 0;
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        r += (2 * b < np && ((uint64_t)o8[b].y << 32 | o8[b].x) > W) +
+             (2 * b + 1 < np && ((uint64_t)o8[b].w << 32 | o8[b].z) > W);
+      }
+      for (int e = 16; e < np; e += 2) {
+        const uint4 o = other[e >> 1];
+        r += (((uint64_t)o.y << 32 | o.x) > W) + (((uint64_t)o.w << 32 | o.z) > W);
+      }
+      r += (int)dpp_u32<0x111>((uint32_t)r);  // quad sums land in each quad's last lane
+      r += (int)dpp_u32<0x112>((uint32_t)r);
+      if (p == 3 && i < nc && r < k) {
+        s.pick_key[r] = w2.y;
+        s.pick_id[r] = (int32_t)~w2.x;
+      }
+    }
+  }
+  __syncthreads();
+}
+
 // Softmax over the k picks in wave 0: lanes j < k get pick j's id and
 // weight; exponentials in parallel, the sum in rank order.
-__device__ __forceinline__ bool topk_softmax(const TopkLds& s, int k, int lane, int& out_id, float& out_w) {
+template <class Lds>
+__device__ __forceinline__ bool topk_softmax(const Lds& s, int k, int lane, int& out_id, float& out_w) {
   float my_val = 0.0f;
   int my_id = 0;
   if (lane < k) {
