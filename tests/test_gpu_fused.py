@@ -34,6 +34,9 @@ def _logits(E, kind, seed):
     lg = synth.router_logits(0, wl)
     if kind == "ties":
         lg = np.floor(np.abs(lg) * 2.0).astype(np.float32) % 4  # values in {0, 1, 2, 3}
+    elif kind == "stride16":  # experts 0, 16, 32, ... far above the rest: the top k share one residue mod 16
+        lg = lg.copy()
+        lg.reshape(-1)[::16] += 10.0
     return np.ascontiguousarray(lg, dtype=np.float32)
 
 
@@ -168,14 +171,21 @@ def _against_oracle(lg_np, x_np, k, wl, ids, w, g, y_rows, out):
 
 
 # moe_decode_layer_mxfp4 against moe_route_group_one + moe_expert_ffn_combine_mxfp4:
-# routing inside the gate/up launch (register top-k widths 2, 4 and 8, ties,
-# k = 1) and the shapes that run the separate calls
+# routing inside the gate/up launch (the wide top-k at 1, 2, 4 and 8 experts
+# per thread; ties; the top k all in one 16-lane row; fewer experts than the
+# 16 rows, where every expert is a candidate; k = 1) and the shapes that run
+# the separate calls
 DECODE_LAYER_CASES = [  # name, E, H, I, k, logits kind
     ("E896_k16", 896, 7168, 1536, 16, "normal"),
     ("E96_k16", 96, 7168, 1536, 16, "normal"),
     ("E2048_k16", 2048, 7168, 1536, 16, "normal"),
     ("E896_ties", 896, 7168, 1536, 16, "ties"),
+    ("E896_stride16", 896, 7168, 1536, 16, "stride16"),
     ("E300_k1", 300, 7168, 1536, 1, "normal"),
+    ("E40_k16", 40, 7168, 1536, 16, "normal"),
+    ("E16_k16", 16, 7168, 1536, 16, "normal"),
+    ("E8_k4", 8, 7168, 1536, 4, "normal"),
+    ("E5_k5_ties", 5, 7168, 1536, 5, "ties"),
     ("E4096_separate", 4096, 7168, 1536, 16, "normal"),
     ("k32_separate", 96, 7168, 1536, 32, "normal"),
     ("small_separate", 8, 256, 128, 2, "normal"),
@@ -226,6 +236,7 @@ def test_decode_layer_matches_calls(case):
 # including the stack's use with out in y_prev's own buffer
 DECODE_RMS_CASES = [  # name, E, H, I, k, out aliases y_prev
     ("E96_k16", 96, 7168, 1536, 16, False),
+    ("E16_k16", 16, 7168, 1536, 16, False),
     ("E896_k16_in_place", 896, 7168, 1536, 16, True),
     ("E4096_separate", 4096, 7168, 1536, 16, False),
     ("small_separate_in_place", 8, 256, 128, 2, True),
