@@ -4,24 +4,32 @@
 //
 // A operand = the expert's MXFP4 weights exactly as stored (E2M1 codes with
 // their own E8M0 scale per 32 values); B operand = the activations split in
-// two E4M3 terms, each with an E8M0 scale per 32 values:
-//     a = q1 * 2^e1 + q2 * 2^e2,   q1 = rne_e4m3(a / 2^e1), q2 = rne_e4m3((a - q1 2^e1) / 2^e2)
-// with e = ceil(log2(amax / 448)) per block and term.  A bf16 value has 8
-// significant bits and each E4M3 term carries 4, so for x the two terms are
-// exact; for the fp32 h they carry the leading ~8 bits.  D accumulates both
-// terms in fp32.
+// two terms, each with an E8M0 scale per 32 values:
+//     a = q1 * 2^e1 + q2 * 2^e2,   q1 = rne(a / 2^e1), q2 = rne((a - q1 2^e1) / 2^e2)
+// gate/up: x in two E2M3 (FP6) terms, e = ceil(log2(amax / 7.5)) per block
+// and term, so the MFMA runs at the FP4/FP6 rate; the two terms carry the
+// leading ~8 bits of each value (not always all of a bf16 x).  down: the
+// fp32 h in two E4M3 terms, e = ceil(log2(amax / 448)), the leading ~8 bits.
+// D accumulates both terms in fp32.
 //
 // Operand layout of one 32x32x64 step (64 K values; lane-group h = lane / 32
 // of the FP4 operand holds K values 32h .. 32h+31 and lane l gives the E8M0
 // scale of 32-block l / 32 of its operand):
 //   A lane (m, h): weight row m, the 16 bytes (32 E2M1 codes) of block h of
 //                  the step, exactly as stored; that block's scale byte.
-//   B lane (n, h): token n, 32 E4M3 bytes holding K values 16h .. 16h+15 and
-//                  32 + 16h .. 32 + 16h + 15 (the FP8 operand's lane-groups
-//                  split K in 16-value halves); the scale byte of K values
-//                  32h .. 32h+31.  The quantizer stores the terms with the
-//                  middle two 16-value quarters of every 64 values swapped, so
-//                  that these 32 bytes are contiguous.
+//   B lane (n, h), down (E4M3): token n, 32 bytes holding K values
+//                  16h .. 16h+15 and 32 + 16h .. 32 + 16h + 15 (the FP8
+//                  operand's lane-groups split K in 16-value halves); the
+//                  scale byte of K values 32h .. 32h+31.  The quantizer stores
+//                  the terms with the middle two 16-value quarters of every 64
+//                  values swapped, so that these 32 bytes are contiguous.
+//   B lane (n, h), gate/up (E2M3): token n, 24 bytes holding K values
+//                  32h .. 32h+31 as 6-bit codes packed densely (value i in
+//                  bits 6i .. 6i+5); the scale byte of those 32 values.  A
+//                  term's 128 values of a stage form one 128-byte record per
+//                  token: per 64-value step s, bytes 48s + 16h hold half h's
+//                  first 16 bytes and bytes 48s + 32 + 8h its last 8; the
+//                  scale bytes sit at 96 + 4h + 2s.
 //   D lane l, register r: token l % 32, weight row 8*(r/4) + 4*(l/32) + r%4.
 //
 // Tiles: 256 weight rows x 128 tokens per block of 4 waves, one block per
