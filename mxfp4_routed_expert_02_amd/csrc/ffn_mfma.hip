@@ -251,16 +251,18 @@ __device__ __forceinline__ void quantize_block(const void* src, int row, int row
   }
 }
 
-// x [T][H] bf16 -> two E2M3 terms; block 0 also writes the tile plan: one
-// (slot, token tile) pair per token tile of every active expert with more
-// than reg_max rows, and the pair count in plan[0].
+// x [T][H] bf16 -> two E2M3 terms; block 0 also writes the tile plan: the
+// pair count in plan[0], and from int4 1 on one record per token tile of
+// every active expert with more than reg_max rows: (expert, its first
+// sorted row, its row count, the tile's first token), so a GEMM block finds
+// its work with one load after the count.
 __global__ __launch_bounds__(kThreads) void mfma_prep_kernel(const uint16_t* __restrict__ x, int T, int H,
                                                             const int32_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ active,
                                                             uint8_t* __restrict__ xq, int32_t* __restrict__ plan,
                                                             int reg_max) {
   if (blockIdx.x == 0) {
-    // Tile plan: the (slot, token tile) pairs of experts with more than
+    // Tile plan: the (expert, token tile) pairs of experts with more than
     // reg_max rows, heaviest first: tiles with 4 token groups (65..128
     // rows), then 2 (33..64), then 1 (up to 32).  The GEMM deals the pairs to
     // the XCDs in bands of eight runs of kBand neighbours (the rest one by
@@ -330,8 +332,7 @@ __global__ __launch_bounds__(kThreads) void mfma_prep_kernel(const uint16_t* __r
           const int r = min(cnt - j * kTileTok, kTileTok);
           const int q = r > 64 ? 0 : r > 32 ? 1 : 2;
           const int g = base[q] + bf[q]++;
-          plan[1 + 2 * g] = a;
-          plan[2 + 2 * g] = j;
+          ((int4*)plan)[1 + g] = make_int4(e, offsets[e], cnt, j * kTileTok);
         }
       }
       for (int q = 0; q < 3; ++q) base[q] += t[q];
@@ -445,8 +446,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 template <bool GATEUP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void mfma_ffn_kernel(
-    moe_mxfp4_weights w, int k, const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_rows,
-    const int32_t* __restrict__ active, const int32_t* __restrict__ plan,
+    moe_mxfp4_weights w, int k, const int32_t* __restrict__ sorted_rows, const int32_t* __restrict__ plan,
     const uint8_t* __restrict__ bq,  // B terms [K/128][brows][2][128]
     const uint8_t* __restrict__ bs,  // B scales [K/128][brows][2][4]
     int brows, float* __restrict__ out, int m_tiles) {
@@ -480,10 +480,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     pair = bands * 8 * kBand + xcd + 8 * r;
   }
   if (pair >= npairs) return;
-  const int slot = plan[1 + 2 * pair], ntile = plan[2 + 2 * pair];
-  const int e = active[1 + slot];
-  const int p0 = offsets[e], cnt = offsets[e + 1] - p0;
-  const int tok0 = ntile * kTileTok;
+  const int4 rec = ((const int4*)plan)[1 + pair];  // (expert, first sorted row, row count, first token)
+  const int e = rec.x, p0 = rec.y, cnt = rec.z, tok0 = rec.w;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -774,34 +772,49 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     for (; st + R < nst; ++st) steady_stage();
     for (; st < nst; ++st) drain_stage();
 
-    const int tok = tok0 + tgi * 32 + n;
-    if (tok >= cnt) return;
-    float* orow = out + (int64_t)(p0 + tok) * out_cols;
+    // Epilogue: the tile's outputs pass through LDS (the ring is free once
+    // every wave is past its last fragment reads), so that each store
+    // instruction writes whole output rows (1 KB contiguous) instead of 64
+    // scattered 16-byte pieces of 32 token rows.  LDS rows are padded by 4
+    // floats: a 16-lane group's float4 writes then hit 64 distinct banks.
+    constexpr int kCols = GATEUP ? kTileRows / 2 : kTileRows;  // output columns of the tile
+    constexpr int kPitch = kCols + 4;                           // floats per LDS row
+    static_assert(G::kTok * kPitch * 4 <= kRingBytes, "the output tile fits in the ring's LDS");
+    float* so = (float*)s_ring;
+    wait_vm<0>();  // no LDS DMA of this wave still in flight (the last scale prefetch)
+    __syncthreads();
+    float* srow = so + tt * kPitch;  // this lane's token
     if (GATEUP) {
       // j < RBW/2: gate block rb_of(j); j + RBW/2: the matching up block
 #pragma unroll
       for (int j = 0; j < RBW / 2; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int m = row0 + 32 * rb_of(j) + 8 * g + 4 * half;
+          const int c = 32 * rb_of(j) + 8 * g + 4 * half;
           float4 v;
           v.x = silu_mul(acc[j][4 * g + 0], acc[j + RBW / 2][4 * g + 0]);
           v.y = silu_mul(acc[j][4 * g + 1], acc[j + RBW / 2][4 * g + 1]);
           v.z = silu_mul(acc[j][4 * g + 2], acc[j + RBW / 2][4 * g + 2]);
           v.w = silu_mul(acc[j][4 * g + 3], acc[j + RBW / 2][4 * g + 3]);
-          *(float4*)(orow + m) = v;
+          *(float4*)(srow + c) = v;
         }
     } else {
 #pragma unroll
       for (int j = 0; j < RBW; ++j) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int m = row0 + 32 * rb_of(j) + 8 * g + 4 * half;
-          *(float4*)(orow + m) =
-              make_float4(acc[j][4 * g + 0], acc[j][4 * g + 1], acc[j][4 * g + 2], acc[j][4 * g + 3]);
+          const int c = 32 * rb_of(j) + 8 * g + 4 * half;
+          *(float4*)(srow + c) = make_float4(acc[j][4 * g + 0], acc[j][4 * g + 1], acc[j][4 * g + 2], acc[j][4 * g + 3]);
         }
       }
     }
+    __syncthreads();
+    constexpr int kLanesPerRow = kCols / 4;           // float4 of an output row: 64 (down) or 32 (gate/up)
+    constexpr int kRowsPerOp = MOE_WAVE / kLanesPerRow;  // output rows per store instruction
+    const int nrow = min(G::kTok, cnt - tok0);        // tokens of the tile with routed rows
+    const int c4 = lane % kLanesPerRow;
+    for (int t = wave * kRowsPerOp + lane / kLanesPerRow; t < nrow; t += 4 * kRowsPerOp)
+      *(float4*)(out + (int64_t)(p0 + tok0 + t) * out_cols + row0 + 4 * c4) = *(const float4*)(so + t * kPitch + 4 * c4);
   };
   if (tg == 1) body(std::integral_constant<int, 1>());
   else if (tg == 2) body(std::integral_constant<int, 2>());
@@ -829,7 +842,7 @@ size_t mfma_workspace(int T, int k, int E, int H, int I) {
   const size_t per = (size_t)reg_rows_max(T) + 1;  // fewest rows of a GEMM expert
   const size_t pairs = R / kTileTok + (mx < R / per ? mx : R / per) + 1;
   return align256((size_t)T * 2 * H) + align256((size_t)T * 2 * (H / 32)) + align256(R * 2 * I) +
-         align256(R * 2 * (I / 32)) + align256((1 + 2 * pairs) * sizeof(int32_t));
+         align256(R * 2 * (I / 32)) + align256((1 + pairs) * 4 * sizeof(int32_t));
 }
 
 size_t mfma_max_pairs(int T, int k, int E) {
@@ -859,8 +872,8 @@ hipError_t launch_mfma_gateup(const uint16_t* x, int T, int k, const moe_mxfp4_w
   if (err != hipSuccess) return err;
   const int m_tiles = I / (kTileRows / 2);
   const unsigned grid = (unsigned)(8 * ((mfma_max_pairs(T, k, w.num_experts) + 7) / 8) * m_tiles);
-  hipLaunchKernelGGL((mfma_ffn_kernel<true>), dim3(grid), dim3(kThreads), 0, s, w, k, offsets, sorted_rows, active,
-                     plan, xq, xs, T, h, m_tiles);
+  hipLaunchKernelGGL((mfma_ffn_kernel<true>), dim3(grid), dim3(kThreads), 0, s, w, k, sorted_rows, plan, xq, xs, T,
+                     h, m_tiles);
   return hipGetLastError();
 }
 
@@ -882,8 +895,8 @@ hipError_t launch_mfma_down(int T, int k, const moe_mxfp4_weights& w, const int3
   if (err != hipSuccess) return err;
   const int m_tiles = H / kTileRows;
   const unsigned grid = (unsigned)(8 * ((mfma_max_pairs(T, k, w.num_experts) + 7) / 8) * m_tiles);
-  hipLaunchKernelGGL((mfma_ffn_kernel<false>), dim3(grid), dim3(kThreads), 0, s, w, k, offsets, sorted_rows, active,
-                     plan, hq, hs, (int)R, y_rows, m_tiles);
+  hipLaunchKernelGGL((mfma_ffn_kernel<false>), dim3(grid), dim3(kThreads), 0, s, w, k, sorted_rows, plan, hq, hs,
+                     (int)R, y_rows, m_tiles);
   return hipGetLastError();
 }
 
