@@ -265,9 +265,9 @@ __global__ __launch_bounds__(kThreads) void mfma_prep_kernel(const uint16_t* __r
     // Tile plan: the (expert, token tile) pairs of experts with more than
     // reg_max rows, heaviest first: tiles with 4 token groups (65..128
     // rows), then 2 (33..64), then 1 (up to 32).  The GEMM deals the pairs to
-    // the XCDs in bands of eight runs of kBand neighbours (the rest one by
-    // one), so every XCD gets a near-equal share of each class and starts
-    // with its heaviest tiles.  Within a class pairs keep slot order, so
+    // the XCDs in bands of eight runs of kBand neighbours, serpentine (the
+    // rest one by one), so every XCD gets a near-equal share of each class
+    // and starts with its heaviest tiles.  Within a class pairs keep slot order, so
     // the plan is deterministic.
     __shared__ int s_part[3][kThreads / 64];
     const int na = active[0];
@@ -461,10 +461,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int nst = K / kStageK;
 
   // tile: block b runs on XCD b % 8.  The plan's pairs (heaviest first) go
-  // in bands of 8 * kBand: XCD x takes pairs x * kBand .. x * kBand + kBand - 1
-  // of each band, weight tile major, so the token tiles of one expert that
-  // land there read each weight tile into that XCD's L2 together; pairs
-  // past the last whole band go to XCD g % 8, one weight tile after another.
+  // in bands of 8 * kBand, one run of kBand neighbours per XCD, weight tile
+  // major, so the token tiles of one expert that land on an XCD read each
+  // weight tile into its L2 together.  The runs are dealt serpentine (even
+  // bands XCD 0 first, odd bands XCD 7 first), so no XCD takes the heaviest
+  // run of every band; pairs past the last whole band go one by one in the
+  // next band's direction, one weight tile after another.
   const int bx = blockIdx.x, xcd = bx & 7, q = bx >> 3;
   const int npairs = plan[0];
   const int bands = npairs / (8 * kBand);
@@ -473,11 +475,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   if (q < q_bands) {
     const int b = q / (kBand * m_tiles), qi = q - b * (kBand * m_tiles);
     mt = qi / kBand;
-    pair = b * 8 * kBand + xcd * kBand + (qi - mt * kBand);
+    pair = b * 8 * kBand + ((b & 1) ? 7 - xcd : xcd) * kBand + (qi - mt * kBand);
   } else {
     const int r = (q - q_bands) / m_tiles;
     mt = (q - q_bands) - r * m_tiles;
-    pair = bands * 8 * kBand + xcd + 8 * r;
+    pair = bands * 8 * kBand + ((bands & 1) ? 7 - xcd : xcd) + 8 * r;
   }
   if (pair >= npairs) return;
   const int4 rec = ((const int4*)plan)[1 + pair];  // (expert, first sorted row, row count, first token)
