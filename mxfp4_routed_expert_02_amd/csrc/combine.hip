@@ -12,7 +12,8 @@ constexpr int kThreads = 256;
 constexpr int kCombineThreads = 64;
 
 // a thread's loads are issued before its sums, 16 rows at a time (k <= 32),
-// so the usual k = 16 takes one round trip
+// so the usual k = 16 takes one round trip; they carry the non-temporal
+// hint (prefill4096's combine streams 1.9 GB of y rows it reads once)
 __global__ __launch_bounds__(kCombineThreads) void combine_vec4_kernel(const float* __restrict__ y_rows,
                                                                        const float* __restrict__ w,
                                                                        const int32_t* __restrict__ row_pos, int k,
@@ -27,7 +28,10 @@ __global__ __launch_bounds__(kCombineThreads) void combine_vec4_kernel(const flo
     float4 y[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u)
-      if (j0 + u < k) y[u] = ((const float4*)(y_rows + (int64_t)rp[j0 + u] * H))[i];
+      if (j0 + u < k) {  // each y row is read once: non-temporal loads
+        const f32x4_t v = __builtin_nontemporal_load((const f32x4_t*)(y_rows + (int64_t)rp[j0 + u] * H) + i);
+        y[u] = make_float4(v.x, v.y, v.z, v.w);
+      }
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       if (j0 + u < k) {
