@@ -270,6 +270,42 @@ __device__ __forceinline__ uint32_t load1(__amdgpu_buffer_rsrc_t r, uint32_t off
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, kStreamPolicy);
 }
 
+__device__ __forceinline__ uint32_t load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kStreamPolicy);
+}
+
+// Scale bytes of the one-token gate/up GEMVs (G lanes per row, lane li of
+// row group gi takes blocks li + G*j, j < J).  A lane's J bytes lie G bytes
+// apart, so instead of J byte loads per matrix each lane loads dwords
+// li + G*r (r < (J+3)/4) of its row's scales, and the byte of block li + G*j
+// (dword li/4 + (G/4)*j) comes from register j/4 of lane gi*G + li/4 +
+// (G/4)*(j%4) by ds_bpermute (measured: the decode FFN call 0.75 us faster).
+template <int J>
+constexpr int scale_dwords() { return (J + 3) / 4; }
+
+template <int U, int J, int G>
+__device__ __forceinline__ void load_scale_dwords(__amdgpu_buffer_rsrc_t rs, uint32_t row_off, uint32_t u_step, int li,
+                                                  uint32_t (&d)[U][scale_dwords<J>()]) {
+  static_assert(G >= 4 && G % 4 == 0 && scale_dwords<J>() <= 2, "scale dwords of the register GEMV layout");
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int r = 0; r < scale_dwords<J>(); ++r) d[u][r] = load4(rs, row_off + u * u_step + 4u * (uint32_t)(li + G * r));
+}
+
+template <int U, int J, int G>
+__device__ __forceinline__ void spread_scale_bytes(const uint32_t (&d)[U][scale_dwords<J>()], int gi, int li,
+                                                   uint32_t (&sc)[U][J]) {
+  const uint32_t sh = 8u * (uint32_t)(li & 3);
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int src = 4 * (gi * G + (li >> 2) + (G / 4) * (j & 3));
+      sc[u][j] = ((uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)d[u][j >> 2]) >> sh) & 0xFFu;
+    }
+}
+
 // Lane layout: G = 2^lg lanes share one weight row (G divides nb, the row's
 // count of 32-value blocks) and lane l takes blocks (l % G) + G*j, j < J = nb/G,
 // of row l / G; a wave instruction covers 64/G rows and an iteration U such
@@ -646,23 +682,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const __amdgpu_buffer_rsrc_t ruq = make_rsrc(w.up_q + eo, (uint32_t)I * qrow);
   const __amdgpu_buffer_rsrc_t rgs = make_rsrc(w.gate_s + eo, (uint32_t)(I * nb));
   const __amdgpu_buffer_rsrc_t rus = make_rsrc(w.up_s + eo, (uint32_t)(I * nb));
-  const uint32_t vq0 = (uint32_t)gi * qrow + 16u * li, vs0 = (uint32_t)(gi * nb + li);
+  const uint32_t vq0 = (uint32_t)gi * qrow + 16u * li;
   uint4 qg[U][J], qu[U][J];
   uint32_t sg[U][J], su[U][J];
   // chunk j of row group u of iteration it; `off` = kPastEnd turns the loads
   // into out-of-range buffer reads, which return 0 and touch no memory
   auto load_chunk = [&](int it, int u, int j, uint32_t off) {
     const int n = it * rows_it + u * rpi;
-    const uint32_t bq = (uint32_t)n * qrow + off, bs = (uint32_t)(n * nb) + off;
+    const uint32_t bq = (uint32_t)n * qrow + off;
     qg[u][j] = load16(rgq, vq0 + bq + 16u * G * j);
     qu[u][j] = load16(ruq, vq0 + bq + 16u * G * j);
-    sg[u][j] = load1(rgs, vs0 + bs + G * j);
-    su[u][j] = load1(rus, vs0 + bs + G * j);
+  };
+  uint32_t dg[U][scale_dwords<J>()], du[U][scale_dwords<J>()];  // the scale dwords of an iteration
+  auto load_sc = [&](int it, uint32_t off) {
+    const uint32_t row_off = (uint32_t)((it * rows_it + gi) * nb) + off;
+    load_scale_dwords<U, J, G>(rgs, row_off, (uint32_t)(rpi * nb), li, dg);
+    load_scale_dwords<U, J, G>(rus, row_off, (uint32_t)(rpi * nb), li, du);
   };
 #pragma unroll
   for (int j = 0; j < J; ++j)
 #pragma unroll
     for (int u = 0; u < U; ++u) load_chunk(it0, u, j, it0 < it1 ? 0u : kPastEnd);
+  load_sc(it0, it0 < it1 ? 0u : kPastEnd);
   const int p0 = offsets[e];
   const int cnt = offsets[e + 1] - p0;
   auto stage = [&](int c, const uint4& v) { s_x4[(c & 3) * nb + (c >> 2)] = v; };
@@ -674,6 +715,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   for (int it = it0; it < it1; it += istep) {
     const uint32_t next_off = it + istep < it1 ? 0u : kPastEnd;
     const int n0 = it * rows_it;
+    spread_scale_bytes<U, J, G>(dg, gi, li, sg);
+    spread_scale_bytes<U, J, G>(du, gi, li, su);
+    load_sc(it + istep, next_off);
     float ag[U], au[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) ag[u] = au[u] = 0.0f;
@@ -1002,21 +1046,26 @@ __global__ __launch_bounds__(kRGThreads) void route_gateup_one_kernel(
   const __amdgpu_buffer_rsrc_t ruq = make_rsrc(w.up_q + eo, (uint32_t)I * qrow);
   const __amdgpu_buffer_rsrc_t rgs = make_rsrc(w.gate_s + eo, (uint32_t)(I * nb));
   const __amdgpu_buffer_rsrc_t rus = make_rsrc(w.up_s + eo, (uint32_t)(I * nb));
-  const uint32_t vq0 = (uint32_t)gi * qrow + 16u * li, vs0 = (uint32_t)(gi * nb + li);
+  const uint32_t vq0 = (uint32_t)gi * qrow + 16u * li;
   uint4 qg[U][J], qu[U][J];
   uint32_t sg[U][J], su[U][J];
   auto load_chunk = [&](int it, int u, int j, uint32_t off) {
     const int n = it * rows_it + u * rpi;
-    const uint32_t bq = (uint32_t)n * qrow + off, bs = (uint32_t)(n * nb) + off;
+    const uint32_t bq = (uint32_t)n * qrow + off;
     qg[u][j] = load16(rgq, vq0 + bq + 16u * G * j);
     qu[u][j] = load16(ruq, vq0 + bq + 16u * G * j);
-    sg[u][j] = load1(rgs, vs0 + bs + G * j);
-    su[u][j] = load1(rus, vs0 + bs + G * j);
+  };
+  uint32_t dg[U][scale_dwords<J>()], du[U][scale_dwords<J>()];  // the scale dwords of an iteration
+  auto load_sc = [&](int it, uint32_t off) {
+    const uint32_t row_off = (uint32_t)((it * rows_it + gi) * nb) + off;
+    load_scale_dwords<U, J, G>(rgs, row_off, (uint32_t)(rpi * nb), li, dg);
+    load_scale_dwords<U, J, G>(rus, row_off, (uint32_t)(rpi * nb), li, du);
   };
 #pragma unroll
   for (int j = 0; j < J; ++j)
 #pragma unroll
     for (int u = 0; u < U; ++u) load_chunk(it0, u, j, it0 < it1 ? 0u : kPastEnd);
+  load_sc(it0, it0 < it1 ? 0u : kPastEnd);
   if constexpr (RMS) {  // x = bf16(y_prev * factor) into LDS while the first weight loads are in flight
     float tot = 0.0f;
 #pragma unroll
@@ -1040,6 +1089,9 @@ __global__ __launch_bounds__(kRGThreads) void route_gateup_one_kernel(
   for (int it = it0; it < it1; it += istep) {
     const uint32_t next_off = it + istep < it1 ? 0u : kPastEnd;
     const int n0 = it * rows_it;
+    spread_scale_bytes<U, J, G>(dg, gi, li, sg);
+    spread_scale_bytes<U, J, G>(du, gi, li, su);
+    load_sc(it + istep, next_off);
     float ag[U], au[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) ag[u] = au[u] = 0.0f;
