@@ -625,10 +625,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     auto read_sc = [&](int st, int sl, uint32_t (&sa)[RBW], uint32_t (&sb)[2]) {
       const uint8_t* ab = sa_base(st);
 #pragma unroll
-      for (int j = 0; j < RBW; ++j) sa[j] = *(const uint32_t*)(ab + 32 * rel(j) * 16) >> (8 * half);
+      for (int j = 0; j < RBW; ++j) sa[j] = *(const uint32_t*)(ab + 32 * rel(j) * 16);
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-        sb[u] = *(const uint32_t*)(s_ring + sl * G::kStage + bs_off + u * kBSTerm) >> (8 * half * kBSShift);
+      for (int u = 0; u < 2; ++u) sb[u] = *(const uint32_t*)(s_ring + sl * G::kStage + bs_off + u * kBSTerm);
+    };
+    // The words arrive as stored (this lane's byte of step s at 2s + half);
+    // moving it to byte 2s, the MFMA's select, happens at the start of the
+    // stage that uses them, so no scale read waits for its data mid-stage.
+    auto place_sc = [&](uint32_t (&sa)[RBW], uint32_t (&sb)[2]) {
+#pragma unroll
+      for (int j = 0; j < RBW; ++j) sa[j] >>= 8 * half;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) sb[u] >>= 8 * half * kBSShift;
     };
 
     v16f_t acc[RBW];
@@ -701,6 +709,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       constexpr int kReads1 = RBW + 4;        // step-1 fragments: RBW of A, 4 of B
       constexpr int kReadsN = RBW + 4 + RBW + 2;  // next stage: A, B fragments and scale words
       uint4 a1[RBW], b1[2][2];
+      place_sc(sa, sb);
       const v8i_t B0 = pack_b(b0[0][0], b0[0][1]), B1 = pack_b(b0[1][0], b0[1][1]);
       const uint8_t* a1_base = s_ring + sl * G::kStage + a_off[1];
       static_for<0, kM>([&](auto i_c) {
@@ -741,9 +750,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             b0[(r - RBW) / 2][(r - RBW) % 2] =
                 ld_b(sn_base + b_off[0][(r - RBW) % 2] + ((r - RBW) / 2) * G::kTok * 128, (r - RBW) % 2);
           else if constexpr (r < 2 * RBW + 4)
-            sa[r - RBW - 4] = *(const uint32_t*)(san_base + 32 * rel(r - RBW - 4) * 16) >> (8 * half);
+            sa[r - RBW - 4] = *(const uint32_t*)(san_base + 32 * rel(r - RBW - 4) * 16);
           else
-            sb[r - 2 * RBW - 4] = *(const uint32_t*)(sn_base + bs_off + (r - 2 * RBW - 4) * kBSTerm) >> (8 * half * kBSShift);
+            sb[r - 2 * RBW - 4] = *(const uint32_t*)(sn_base + bs_off + (r - 2 * RBW - 4) * kBSTerm);
         });
         __builtin_amdgcn_sched_barrier(0);
       });
@@ -752,6 +761,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // Draining stage: nothing left to load.
     auto drain_stage = [&]() {
       uint4 a1[RBW], b1[2][2];
+      place_sc(sa, sb);
       read_a(sl, 1, a1);
       read_b(sl, 1, b1);
       mma(std::integral_constant<int, 0>(), a0, b0, sa, sb);
