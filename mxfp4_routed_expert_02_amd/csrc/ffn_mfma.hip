@@ -399,11 +399,13 @@ constexpr int kRingBytes = cmax(cmax(Ring<1, false>::kBytes, Ring<2, false>::kBy
 // LDS DMA loads of 16 and 4 bytes per lane to the wave-uniform LDS address
 // `lds` (lane l at lds + size*l).  Issued from asm, so the compiler neither
 // counts them nor waits for them: the ring's waits below are explicit.
-__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+// From a wave-uniform base (scalar registers) plus this lane's 32-bit
+// offset: a stage's loads advance only the bases, with scalar adds.
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds) : "memory", "m0");
 }
-__device__ __forceinline__ void lds_dma4(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+__device__ __forceinline__ void lds_dma4(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(lds) : "memory", "m0");
 }
 
 // s_waitcnt vmcnt(N) (N clamped to the counter's 63) with the other counters free
@@ -536,42 +538,48 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // fills chunk c = w + 4j: term c / (4TG), tokens 8 (c % 4TG) + lane/8,
     // slot lane%8 taking piece (lane%8) ^ ((token >> 1) & 7).  BS: entry
     // 64 (w % TG) + lane = term * 32TG + token (waves past TG repeat it).
+    // Each DMA source is a wave-uniform base (tile rows 0 and 128: the gate
+    // and up matrices of gate/up, or two halves of down) plus this lane's
+    // 32-bit offset, the same for every stage.
     const int apiece = (lane & 3) ^ ((lane >> 4) & 3);
-    const uint8_t* asrc[4];
+    const uint8_t* const a_base[2] = {a_row(0), a_row(kTileRows / 2)};
+    const uint8_t* const as_base[2] = {a_srow(0), a_srow(kTileRows / 2)};
+    uint32_t a_off_s[4], as_off_s[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) asrc[i] = a_row(16 * (4 * i + wave) + (lane >> 2)) + 16 * apiece;
+    for (int i = 0; i < 4; ++i)
+      a_off_s[i] = (uint32_t)((16 * (4 * i + wave) + (lane >> 2) - (i >= 2 ? kTileRows / 2 : 0)) * qrow + 16 * apiece);
     // AS: quarter q of a scale block = rows 64q + 16w + lane/4, word lane%4
-    const uint8_t* assrc[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) assrc[q] = a_srow(64 * q + 16 * wave + (lane >> 2)) + 4 * (lane & 3);
+    for (int q = 0; q < 4; ++q)
+      as_off_s[q] = (uint32_t)((64 * q + 16 * wave + (lane >> 2) - (q >= 2 ? kTileRows / 2 : 0)) * nsb + 4 * (lane & 3));
     const int nblk = nst >> 2;  // scale blocks per row
-    const uint8_t* bsrc[2 * TG];
+    uint32_t b_off_s[2 * TG];
 #pragma unroll
     for (int j = 0; j < 2 * TG; ++j) {
       const int c = wave + 4 * j, u = c / (4 * TG);
       const int t = 8 * (c % (4 * TG)) + (lane >> 3);
-      bsrc[j] = bq + (b_row(t) * 2 + u) * 128 + 16 * ((lane & 7) ^ ((t >> 1) & 7));
+      b_off_s[j] = (uint32_t)((b_row(t) * 2 + u) * 128 + 16 * ((lane & 7) ^ ((t >> 1) & 7)));
     }
     const int be = 64 * tgi + lane;
-    const uint8_t* bssrc = bs + (b_row(be % G::kTok) * 2 + be / G::kTok) * 4;
+    const uint32_t bs_off_s = (uint32_t)((b_row(be % G::kTok) * 2 + be / G::kTok) * 4);
     const int64_t bq_stage = (int64_t)brows * 256, bs_stage = (int64_t)brows * 8;
 
     // quarter q of weight-scale block b (clamped to the last block) into its buffer
     auto issue_scales = [&](int b, int q) {
-      const uint8_t* src = q == 0 ? assrc[0] : q == 1 ? assrc[1] : q == 2 ? assrc[2] : assrc[3];
       const uint32_t dst = lds0 + (uint32_t)(G::kScaleBase + (b % G::kScaleBufs) * kScaleBuf + (64 * q + 16 * wave) * 16);
-      lds_dma4(src + 16 * min(b, nblk - 1), dst);
+      const uint32_t off = q == 0 ? as_off_s[0] : q == 1 ? as_off_s[1] : q == 2 ? as_off_s[2] : as_off_s[3];
+      lds_dma4(as_base[q >= 2 ? 1 : 0] + 16 * min(b, nblk - 1), off, dst);
     };
     // load o (0 .. kOps-1) of this wave's share of stage st into slot sl;
     // load 4 is quarter st % 4 of the scale block after st's
     auto issue_op = [&](int st, int sl, auto o_c) {
       constexpr int o = decltype(o_c)::value;
       const uint32_t sb = lds0 + (uint32_t)(sl * G::kStage);
-      if constexpr (o < 4) lds_dma16(asrc[o] + st * 64, sb + (4 * o + wave) * 1024);
+      if constexpr (o < 4) lds_dma16(a_base[o >= 2 ? 1 : 0] + st * 64, a_off_s[o], sb + (4 * o + wave) * 1024);
       else if constexpr (o == 4) issue_scales((st >> 2) + 1, st & 3);
       else if constexpr (o < 5 + 2 * TG)
-        lds_dma16(bsrc[o - 5] + st * bq_stage, sb + G::kA + (wave + 4 * (o - 5)) * 1024);
-      else if constexpr (!FP6) lds_dma4(bssrc + st * bs_stage, sb + G::kA + G::kB + tgi * 256);
+        lds_dma16(bq + st * bq_stage, b_off_s[o - 5], sb + G::kA + (wave + 4 * (o - 5)) * 1024);
+      else if constexpr (!FP6) lds_dma4(bs + st * bs_stage, bs_off_s, sb + G::kA + G::kB + tgi * 256);
     };
     auto issue = [&](int st, int sl) { static_for<0, G::kOps>([&](auto o) { issue_op(st, sl, o); }); };
 
