@@ -390,6 +390,7 @@ struct Ring {
   static constexpr int kScaleBase = kSlots * kStage;
   static constexpr int kBytes = kScaleBase + kScaleBufs * kScaleBuf;
   static constexpr int kOps = 4 + 1 + 2 * TG + (FP6 ? 0 : 1);  // DMA loads per wave per stage
+  static constexpr int kX = 5;  // of them the weight codes and scales (loads 0 .. 4), issued first
   static_assert(kStage % 16 == 0, "16-byte aligned slots");
   static_assert(kBytes <= kLdsBytes, "ring fits in LDS");
 };
@@ -544,14 +545,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int apiece = (lane & 3) ^ ((lane >> 4) & 3);
     const uint8_t* const a_base[2] = {a_row(0), a_row(kTileRows / 2)};
     const uint8_t* const as_base[2] = {a_srow(0), a_srow(kTileRows / 2)};
-    uint32_t a_off_s[4], as_off_s[4];
+    uint32_t a_off_s[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       a_off_s[i] = (uint32_t)((16 * (4 * i + wave) + (lane >> 2) - (i >= 2 ? kTileRows / 2 : 0)) * qrow + 16 * apiece);
-    // AS: quarter q of a scale block = rows 64q + 16w + lane/4, word lane%4
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      as_off_s[q] = (uint32_t)((64 * q + 16 * wave + (lane >> 2) - (q >= 2 ? kTileRows / 2 : 0)) * nsb + 4 * (lane & 3));
+    // AS: quarter q of a scale block = rows 64q + 16w + lane/4, word lane%4:
+    // base q / 2 advanced by 64 rows for odd q (scalar), this lane's offset
+    const uint32_t as_off_s = (uint32_t)((16 * wave + (lane >> 2)) * nsb + 4 * (lane & 3));
     const int nblk = nst >> 2;  // scale blocks per row
     uint32_t b_off_s[2 * TG];
 #pragma unroll
@@ -567,8 +567,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // quarter q of weight-scale block b (clamped to the last block) into its buffer
     auto issue_scales = [&](int b, int q) {
       const uint32_t dst = lds0 + (uint32_t)(G::kScaleBase + (b % G::kScaleBufs) * kScaleBuf + (64 * q + 16 * wave) * 16);
-      const uint32_t off = q == 0 ? as_off_s[0] : q == 1 ? as_off_s[1] : q == 2 ? as_off_s[2] : as_off_s[3];
-      lds_dma4(as_base[q >= 2 ? 1 : 0] + 16 * min(b, nblk - 1), off, dst);
+      lds_dma4(as_base[q >= 2 ? 1 : 0] + (q & 1) * 64 * nsb + 16 * min(b, nblk - 1), as_off_s, dst);
     };
     // load o (0 .. kOps-1) of this wave's share of stage st into slot sl;
     // load 4 is quarter st % 4 of the scale block after st's
@@ -581,7 +580,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         lds_dma16(bq + st * bq_stage, b_off_s[o - 5], sb + G::kA + (wave + 4 * (o - 5)) * 1024);
       else if constexpr (!FP6) lds_dma4(bs + st * bs_stage, bs_off_s, sb + G::kA + G::kB + tgi * 256);
     };
-    auto issue = [&](int st, int sl) { static_for<0, G::kOps>([&](auto o) { issue_op(st, sl, o); }); };
+    // a stage's weight loads (X: codes, scale quarter) and activation loads (Y)
+    auto issue_x = [&](int st, int sl) { static_for<0, G::kX>([&](auto o) { issue_op(st, sl, o); }); };
+    auto issue_y = [&](int st, int sl) { static_for<G::kX, G::kOps>([&](auto o) { issue_op(st, sl, o); }); };
 
     // fragment offsets of this lane within a slot: A row 32 rb + n, piece
     // 2 s + half; B token 32 tgi + n, pieces 4 s + 2 half + i (i = 0, 1)
@@ -676,23 +677,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // ahead.  Within stage st: read its step-1 fragments, run step 0, wait
     // for this wave's loads of stage st+1 and meet the other waves (after
     // which stage st+1 is in LDS and nobody reads slot st % R any more),
-    // refill that slot with stage st+R, read stage st+1's step-0 fragments
-    // and scales, run step 1.  The steady-state loop (a stage R ahead left
-    // to load) is one basic block, so the step-0 MFMAs stay ahead of the
-    // wait and keep the pipe busy through it; the last R stages drain.
-    // scale block 0, then stages 0 .. R-1 (each with a quarter of block 1, 2, ...)
+    // refill that slot with stage st+R's weights, read stage st+1's step-0
+    // fragments and scales, run step 1; stage st+R's activation loads follow
+    // in step 0 of stage st+1, so each step carries a share of the DMA
+    // issues.  Loads still go out stage after stage, so the wait counts are
+    // those of whole stages.  The steady-state loop (a stage R ahead left to
+    // load) is one basic block, so the step-0 MFMAs stay ahead of the wait
+    // and keep the pipe busy through it; the last R stages drain.
+    // Scale block 0, then stages 0 .. R-1 (each with a quarter of block 1,
+    // 2, ...); stage R-1's activation loads go out in stage 0.
 #pragma unroll
     for (int q = 0; q < 4; ++q) issue_scales(0, q);
 #pragma unroll
     for (int j = 0; j < R; ++j)
-      if (j < nst) issue(j, j);
-    wait_stages<G::kOps>(min(R - 1, nst - 1));
+      if (j < nst) {
+        issue_x(j, j);
+        if (j < R - 1) issue_y(j, j);
+      }
+    if (nst >= R)
+      wait_vm<(R - 2) * G::kOps + G::kX>();
+    else
+      wait_stages<G::kOps>(nst - 1);
     __syncthreads();
     uint4 a0[RBW], b0[2][2];
-    uint32_t sa[RBW], sb[2];
-    read_sc(0, 0, sa, sb);
+    // scale words: two sets, the current stage's and the next one's, which
+    // trade roles every stage (no copies between them in the loop)
+    uint32_t sa[2][RBW], sb[2][2];
+    read_sc(0, 0, sa[0], sb[0]);
     read_a(0, 0, a0);
     read_b(0, 0, b0);
+    // all of them in before the loop: the loop's own waits then follow the
+    // order of its reads, not the order these were issued in
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     int st = 0, sl = 0;
     // one MFMA of row block j at step s with activation term u
     auto mma_ju = [&](auto s_c, auto j_c, auto u_c, const uint4& a, const v8i_t& Bu, uint32_t sa_j, uint32_t sb_u) {
@@ -703,7 +719,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       A[4] = 0; A[5] = 0; A[6] = 0; A[7] = 0;
       acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, Bu, acc[j], 4, kBFmt, OP, sa_j, OP, sb_u);
     };
-    // Steady stage (a stage R ahead left to load).  A step's MFMAs run term
+    // Steady stage (a stage R ahead left to load), scale set P current.  A step's MFMAs run term
     // major (term 0 of every row block, then term 1), so the two MFMAs that
     // accumulate into one row block are RBW issues apart.  Issue order, fixed
     // by scheduling fences between MFMAs: step 0's MFMAs each followed by a
@@ -712,19 +728,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // stage's step-0 and scale reads.  Vector-memory issues spread over the
     // MFMAs this way never back up the address path far enough to hold up
     // the next MFMA.
-    auto steady_stage = [&]() {
+    auto steady_stage = [&](auto p_c) {
+      constexpr int P = decltype(p_c)::value, Q = 1 - P;
       constexpr int kM = 2 * RBW;             // MFMAs per step
       constexpr int kReads1 = RBW + 4;        // step-1 fragments: RBW of A, 4 of B
       constexpr int kReadsN = RBW + 4 + RBW + 2;  // next stage: A, B fragments and scale words
+      constexpr int kY = G::kOps - G::kX;      // activation loads of stage st+R-1
       uint4 a1[RBW], b1[2][2];
-      place_sc(sa, sb);
       const v8i_t B0 = pack_b(b0[0][0], b0[0][1]), B1 = pack_b(b0[1][0], b0[1][1]);
       const uint8_t* a1_base = s_ring + sl * G::kStage + a_off[1];
+      const int psl = sl == 0 ? R - 1 : sl - 1;  // slot of stage st+R-1
       static_for<0, kM>([&](auto i_c) {
         constexpr int i = decltype(i_c)::value;
         constexpr int u = i / RBW;
+        // each scale word moves to the MFMA's byte select just before its
+        // first use, so the first MFMAs wait only for the first reads
+        if constexpr (i < RBW) sa[P][i] >>= 8 * half;
+        if constexpr (i % RBW == 0) sb[P][u] >>= 8 * half * kBSShift;
         mma_ju(std::integral_constant<int, 0>(), std::integral_constant<int, i % RBW>(),
-               std::integral_constant<int, u>(), a0[i % RBW], u == 0 ? B0 : B1, sa[i % RBW], sb[u]);
+               std::integral_constant<int, u>(), a0[i % RBW], u == 0 ? B0 : B1, sa[P][i % RBW], sb[P][u]);
+        static_for<G::kX + i * kY / kM, G::kX + (i + 1) * kY / kM>([&](auto o_c) { issue_op(st + R - 1, psl, o_c); });
         static_for<i * kReads1 / kM, (i + 1) * kReads1 / kM>([&](auto r_c) {
           constexpr int r = decltype(r_c)::value;
           if constexpr (r < RBW) a1[r] = *(const uint4*)(a1_base + 32 * rel(r) * 64);
@@ -733,11 +756,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         });
         __builtin_amdgcn_sched_barrier(0);
       });
-      uint32_t sa1[RBW], sb1[2];
-#pragma unroll
-      for (int j = 0; j < RBW; ++j) sa1[j] = sa[j];
-      sb1[0] = sb[0];
-      sb1[1] = sb[1];
       const int nsl = sl + 1 == R ? 0 : sl + 1;
       wait_vm<(R - 2) * G::kOps>();
       __syncthreads();
@@ -749,47 +767,69 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         constexpr int i = decltype(i_c)::value;
         constexpr int u = i / RBW;
         mma_ju(std::integral_constant<int, 1>(), std::integral_constant<int, i % RBW>(),
-               std::integral_constant<int, u>(), a1[i % RBW], u == 0 ? C0 : C1, sa1[i % RBW], sb1[u]);
-        static_for<i * G::kOps / kM, (i + 1) * G::kOps / kM>([&](auto o_c) { issue_op(st + R, sl, o_c); });
+               std::integral_constant<int, u>(), a1[i % RBW], u == 0 ? C0 : C1, sa[P][i % RBW], sb[P][u]);
+        static_for<i * G::kX / kM, (i + 1) * G::kX / kM>([&](auto o_c) { issue_op(st + R, sl, o_c); });
+        // next stage's reads in the order its step 0 uses them: term 0's
+        // scale word and fragment, then per row block its scale word and
+        // weight fragment, then term 1's scale word and fragment
         static_for<i * kReadsN / kM, (i + 1) * kReadsN / kM>([&](auto r_c) {
           constexpr int r = decltype(r_c)::value;
-          if constexpr (r < RBW) a0[r] = *(const uint4*)(an_base + 32 * rel(r) * 64);
-          else if constexpr (r < RBW + 4)
-            b0[(r - RBW) / 2][(r - RBW) % 2] =
-                ld_b(sn_base + b_off[0][(r - RBW) % 2] + ((r - RBW) / 2) * G::kTok * 128, (r - RBW) % 2);
-          else if constexpr (r < 2 * RBW + 4)
-            sa[r - RBW - 4] = *(const uint32_t*)(san_base + 32 * rel(r - RBW - 4) * 16);
-          else
-            sb[r - 2 * RBW - 4] = *(const uint32_t*)(sn_base + bs_off + (r - 2 * RBW - 4) * kBSTerm);
+          constexpr int rt = r < 3 ? r : r - 3 - 2 * RBW;  // 0 .. 2 within a term group
+          constexpr int ut = r < 3 ? 0 : 1;
+          if constexpr (r < 3 || r >= 3 + 2 * RBW) {
+            if constexpr (rt == 0)
+              sb[Q][ut] = *(const uint32_t*)(sn_base + bs_off + ut * kBSTerm);
+            else
+              b0[ut][rt - 1] = ld_b(sn_base + b_off[0][rt - 1] + ut * G::kTok * 128, rt - 1);
+          } else if constexpr ((r - 3) % 2 == 0) {
+            sa[Q][(r - 3) / 2] = *(const uint32_t*)(san_base + 32 * rel((r - 3) / 2) * 16);
+          } else {
+            a0[(r - 3) / 2] = *(const uint4*)(an_base + 32 * rel((r - 3) / 2) * 64);
+          }
         });
         __builtin_amdgcn_sched_barrier(0);
       });
       sl = nsl;
     };
-    // Draining stage: nothing left to load.
+    // Draining stage: nothing left to load; scale set 0 current.
     auto drain_stage = [&]() {
       uint4 a1[RBW], b1[2][2];
-      place_sc(sa, sb);
+      if (st + R - 1 < nst) issue_y(st + R - 1, sl == 0 ? R - 1 : sl - 1);  // the last stage's activations
+      place_sc(sa[0], sb[0]);
       read_a(sl, 1, a1);
       read_b(sl, 1, b1);
-      mma(std::integral_constant<int, 0>(), a0, b0, sa, sb);
-      uint32_t sa1[RBW], sb1[2];
-#pragma unroll
-      for (int j = 0; j < RBW; ++j) sa1[j] = sa[j];
-      sb1[0] = sb[0];
-      sb1[1] = sb[1];
+      mma(std::integral_constant<int, 0>(), a0, b0, sa[0], sb[0]);
       const int nsl = sl + 1 == R ? 0 : sl + 1;
       if (st + 1 < nst) {
         wait_stages<G::kOps>(nst - 2 - st);
         __syncthreads();
-        read_sc(st + 1, nsl, sa, sb);
+        read_sc(st + 1, nsl, sa[1], sb[1]);
         read_a(nsl, 0, a0);
         read_b(nsl, 0, b0);
       }
-      mma(std::integral_constant<int, 1>(), a1, b1, sa1, sb1);
+      mma(std::integral_constant<int, 1>(), a1, b1, sa[0], sb[0]);
+#pragma unroll
+      for (int j = 0; j < RBW; ++j) sa[0][j] = sa[1][j];
+      sb[0][0] = sb[1][0];
+      sb[0][1] = sb[1][1];
       sl = nsl;
     };
-    for (; st + R < nst; ++st) steady_stage();
+    // the steady loop two stages per trip, so the scale sets keep their registers
+    constexpr std::integral_constant<int, 0> kSet0;
+    constexpr std::integral_constant<int, 1> kSet1;
+    for (; st + R + 1 < nst; ++st) {
+      steady_stage(kSet0);
+      ++st;
+      steady_stage(kSet1);
+    }
+    if (st + R < nst) {
+      steady_stage(kSet0);
+      ++st;
+#pragma unroll
+      for (int j = 0; j < RBW; ++j) sa[0][j] = sa[1][j];
+      sb[0][0] = sb[1][0];
+      sb[0][1] = sb[1][1];
+    }
     for (; st < nst; ++st) drain_stage();
 
     // Epilogue: the tile's outputs pass through LDS (the ring is free once
