@@ -1331,7 +1331,7 @@ hipError_t expert_ffn_impl(const uint16_t* x, int T, int k, const moe_mxfp4_weig
   if (gateup_only) return hipSuccess;
   uint8_t* mfma_ws = (uint8_t*)ws + off;
   if (use_mfma) {
-    if ((err = launch_mfma_gateup(x, T, k, w, offsets, sorted_rows, active, hbuf, mfma_ws, s)) != hipSuccess)
+    if ((err = launch_mfma_gateup(x, T, k, w, offsets, sorted_rows, active, mfma_ws, s)) != hipSuccess)
       return err;
   } else if (!reg_g || (T > 1 && !all_reg)) {
     const int mt_g = pick_mt((size_t)H * 2);
@@ -1374,7 +1374,7 @@ hipError_t expert_ffn_impl(const uint16_t* x, int T, int k, const moe_mxfp4_weig
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (use_mfma) {
-    if ((err = launch_mfma_down(T, k, w, offsets, sorted_rows, active, hbuf, y_rows, mfma_ws, s)) != hipSuccess)
+    if ((err = launch_mfma_down(T, k, w, sorted_rows, y_rows, mfma_ws, s)) != hipSuccess)
       return err;
   } else if (!reg_d || (T > 1 && !all_reg)) {
     const int mt_d = pick_mt((size_t)I * 4);

@@ -68,32 +68,11 @@ typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef float v16f_t __attribute__((ext_vector_type(16)));
 
 // ------------------------------------------------------------ E4M3 terms --
-// Round |a| <= 448 to E4M3 (ties to even); returns the code and the rounded
-// value (in the same units as a).
-__device__ __forceinline__ uint32_t e4m3_rne(float a, float& qv) {
-  const float x = fabsf(a);
-  uint32_t code;
-  if (x < 0.015625f) {  // below 2^-6: the subnormal grid m * 2^-9 (m = 8 is 2^-6)
-    const float m = rintf(x * 512.0f);
-    code = (uint32_t)m;
-    qv = m * (1.0f / 512.0f);
-  } else {
-    uint32_t b = __float_as_uint(x);
-    b += 0x7FFFFu + ((b >> 20) & 1u);  // keep 3 mantissa bits
-    b &= 0xFFF00000u;
-    code = (b >> 20) - (120u << 3);    // exponent bias 127 -> 7
-    if (code > 0x7Eu) {
-      code = 0x7Eu;
-      b = 0x43E00000u;  // 448
-    }
-    qv = __uint_as_float(b);
-  }
-  if (a < 0.0f) {
-    code |= 0x80u;
-    qv = -qv;
-  }
-  return code;
-}
+// Rounding to E4M3 (the OCP format: bias 7, largest finite 448, subnormals
+// m * 2^-9) is the hardware conversion v_cvt_pk_fp8_f32, round to nearest
+// even in the default mode, and v_cvt_f32_fp8 gives the rounded value back
+// exactly.  Every input here has |a| <= 448 by the choice of the block
+// exponent, so no saturation or NaN case arises.
 
 // E8M0 exponent e with amax / 2^e <= 448, e = ceil(log2(amax / 448)); 0 for amax = 0
 __device__ __forceinline__ int e4m3_block_exp(float amax) {
@@ -189,41 +168,16 @@ __device__ __forceinline__ void quantize_block_fp6(const uint16_t* __restrict__ 
   }
 }
 
-// Quantizes rows of a [rows][K] matrix (bf16 bits or fp32) into two E4M3
-// terms, stored stage-major so that one 128-value K stage of every row is
-// one contiguous block (whatever rows a GEMM tile gathers, its loads of a
-// stage stay within a few pages):
+// Two E4M3 terms of one 32-value block v (row `row` of `rows`, block blk
+// along K), a = q1 * 2^e1 + q2 * 2^e2 with e = ceil(log2(amax / 448)) per
+// term, stored stage-major so that one 128-value K stage of every row is one
+// contiguous block (whatever rows a GEMM tile gathers, its loads of a stage
+// stay within a few pages):
 //   q[K/128][rows][2][128]  bytes (quarters of each 64 values in the order
 //                           0,2,1,3)
 //   s[K/128][rows][2][4]    E8M0 scale bytes of the stage's four 32-blocks
-// One thread per (row, 32-block).
-template <bool BF16_IN>
-__device__ __forceinline__ void quantize_block(const void* src, int row, int rows, int blk, int K, uint8_t* __restrict__ q,
+__device__ __forceinline__ void e4m3_two_terms(float (&v)[32], int row, int rows, int blk, uint8_t* __restrict__ q,
                                                uint8_t* __restrict__ s) {
-  float v[32];
-  if (BF16_IN) {
-    const uint4* p = (const uint4*)((const uint16_t*)src + (int64_t)row * K + 32 * blk);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 w = p[i];
-      const uint32_t d[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[8 * i + 2 * j] = __uint_as_float(d[j] << 16);
-        v[8 * i + 2 * j + 1] = __uint_as_float(d[j] & 0xFFFF0000u);
-      }
-    }
-  } else {
-    const float4* p = (const float4*)((const float*)src + (int64_t)row * K + 32 * blk);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float4 w = p[i];
-      v[4 * i] = w.x;
-      v[4 * i + 1] = w.y;
-      v[4 * i + 2] = w.z;
-      v[4 * i + 3] = w.w;
-    }
-  }
 #pragma unroll
   for (int term = 0; term < 2; ++term) {
     float amax = 0.0f;
@@ -234,15 +188,17 @@ __device__ __forceinline__ void quantize_block(const void* src, int row, int row
     const float scl = __uint_as_float((uint32_t)(127 + e) << 23);  // 2^e
     uint32_t packed[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) packed[i] = 0u;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      float qv;
-      const uint32_t c = e4m3_rne(v[i] * inv, qv);
-      packed[i >> 2] |= c << (8 * (i & 3));
-      v[i] -= qv * scl;  // residual for the next term (exact)
+    for (int i = 0; i < 8; ++i) {
+      // codes of values 4i .. 4i+3 in bytes 0 .. 3
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * i] * inv, v[4 * i + 1] * inv, 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * i + 2] * inv, v[4 * i + 3] * inv, w, true);
+      packed[i] = (uint32_t)w;
+      // residual for the next term (exact)
+      v[4 * i] -= __builtin_amdgcn_cvt_f32_fp8(w, 0) * scl;
+      v[4 * i + 1] -= __builtin_amdgcn_cvt_f32_fp8(w, 1) * scl;
+      v[4 * i + 2] -= __builtin_amdgcn_cvt_f32_fp8(w, 2) * scl;
+      v[4 * i + 3] -= __builtin_amdgcn_cvt_f32_fp8(w, 3) * scl;
     }
-    // quarters 0,1,2,3 of each 64 values are stored in the order 0,2,1,3
     const int64_t st = blk >> 2;
     uint8_t* g64 = q + (st * rows + row) * 256 + term * 128 + 64 * ((blk >> 1) & 1);
     *(uint4*)(g64 + 16 * (blk & 1)) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
@@ -346,15 +302,6 @@ __global__ __launch_bounds__(kThreads) void mfma_prep_kernel(const uint16_t* __r
   quantize_block_fp6(x, (int)(i / nblk), T, (int)(i % nblk), H, xq);
 }
 
-// h [R][I] fp32 -> two E4M3 terms, for every row
-__global__ __launch_bounds__(kThreads) void quantize_h_kernel(const float* __restrict__ h, int R, int I,
-                                                             uint8_t* __restrict__ hq, uint8_t* __restrict__ hs) {
-  const int nblk = I >> 5;
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= (int64_t)R * nblk) return;
-  quantize_block<false>(h, (int)(i / nblk), R, (int)(i % nblk), I, hq, hs);
-}
-
 // ------------------------------------------------------------------ GEMM --
 
 // LDS ring.  A slot holds one 128-value K stage of the tile's weight codes
@@ -452,7 +399,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     moe_mxfp4_weights w, int k, const int32_t* __restrict__ sorted_rows, const int32_t* __restrict__ plan,
     const uint8_t* __restrict__ bq,  // B terms [K/128][brows][2][128]
     const uint8_t* __restrict__ bs,  // B scales [K/128][brows][2][4]
-    int brows, float* __restrict__ out, int m_tiles) {
+    int brows, float* __restrict__ out, int m_tiles,
+    uint8_t* __restrict__ hq,  // gate/up: h terms written for the down GEMM ([I/128][hrows][2][128])
+    uint8_t* __restrict__ hs,  // and their scales ([I/128][hrows][2][4])
+    int hrows) {
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kRingBytes];
   constexpr int kRB = kTileRows / 32;  // 32-row blocks of the tile
 
@@ -869,12 +819,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       }
     }
     __syncthreads();
-    constexpr int kLanesPerRow = kCols / 4;           // float4 of an output row: 64 (down) or 32 (gate/up)
-    constexpr int kRowsPerOp = MOE_WAVE / kLanesPerRow;  // output rows per store instruction
-    const int nrow = min(G::kTok, cnt - tok0);        // tokens of the tile with routed rows
-    const int c4 = lane % kLanesPerRow;
-    for (int t = wave * kRowsPerOp + lane / kLanesPerRow; t < nrow; t += 4 * kRowsPerOp)
-      *(float4*)(out + (int64_t)(p0 + tok0 + t) * out_cols + row0 + 4 * c4) = *(const float4*)(so + t * kPitch + 4 * c4);
+    const int nrow = min(G::kTok, cnt - tok0);  // tokens of the tile with routed rows
+    if (GATEUP) {
+      // h never goes to memory in fp32: each thread takes (token, 32-block)
+      // items of the tile's 128 columns (one 128-value K stage of the down
+      // GEMM) and writes their two E4M3 terms, the down GEMM's B operand
+      for (int it = tid; it < 4 * nrow; it += kThreads) {
+        const int t = it >> 2, b = it & 3;
+        const float4* src = (const float4*)(so + t * kPitch + 32 * b);
+        float v[32];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float4 f = src[i];
+          v[4 * i] = f.x;
+          v[4 * i + 1] = f.y;
+          v[4 * i + 2] = f.z;
+          v[4 * i + 3] = f.w;
+        }
+        e4m3_two_terms(v, p0 + tok0 + t, hrows, row0 / 32 + b, hq, hs);
+      }
+    } else {
+      constexpr int kLanesPerRow = kCols / 4;              // float4 of an output row
+      constexpr int kRowsPerOp = MOE_WAVE / kLanesPerRow;  // output rows per store instruction
+      const int c4 = lane % kLanesPerRow;
+      for (int t = wave * kRowsPerOp + lane / kLanesPerRow; t < nrow; t += 4 * kRowsPerOp)
+        *(float4*)(out + (int64_t)(p0 + tok0 + t) * out_cols + row0 + 4 * c4) = *(const float4*)(so + t * kPitch + 4 * c4);
+    }
   };
   if (tg == 1) body(std::integral_constant<int, 1>());
   else if (tg == 2) body(std::integral_constant<int, 2>());
@@ -912,10 +882,10 @@ size_t mfma_max_pairs(int T, int k, int E) {
   return R / kTileTok + (mx < R / per ? mx : R / per) + 1;
 }
 
-// Launches prep, gate/up GEMM (h for experts with more than reg_rows_max(T) rows).
+// Launches prep and the gate/up GEMM, which writes h of the experts with
+// more than reg_rows_max(T) rows as the down GEMM's two E4M3 terms.
 hipError_t launch_mfma_gateup(const uint16_t* x, int T, int k, const moe_mxfp4_weights& w, const int32_t* offsets,
-                              const int32_t* sorted_rows, const int32_t* active, float* h, uint8_t* ws,
-                              hipStream_t s) {
+                              const int32_t* sorted_rows, const int32_t* active, uint8_t* ws, hipStream_t s) {
   const int H = w.hidden, I = w.inter;
   const size_t R = (size_t)T * k;
   uint8_t* xq = ws;
@@ -923,8 +893,6 @@ hipError_t launch_mfma_gateup(const uint16_t* x, int T, int k, const moe_mxfp4_w
   uint8_t* hq = xs + align256((size_t)T * 2 * (H / 32));
   uint8_t* hs = hq + align256(R * 2 * I);
   int32_t* plan = (int32_t*)(hs + align256(R * 2 * (I / 32)));
-  (void)hq;
-  (void)hs;
   const int64_t nq = (int64_t)T * (H / 32);
   hipLaunchKernelGGL(mfma_prep_kernel, dim3(1 + (unsigned)((nq + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
                      x, T, H, offsets, active, xq, plan, reg_rows_max(T));
@@ -933,13 +901,13 @@ hipError_t launch_mfma_gateup(const uint16_t* x, int T, int k, const moe_mxfp4_w
   const int m_tiles = I / (kTileRows / 2);
   const unsigned grid = (unsigned)(8 * ((mfma_max_pairs(T, k, w.num_experts) + 7) / 8) * m_tiles);
   hipLaunchKernelGGL((mfma_ffn_kernel<true>), dim3(grid), dim3(kThreads), 0, s, w, k, sorted_rows, plan, xq, xs, T,
-                     h, m_tiles);
+                     (float*)nullptr, m_tiles, hq, hs, (int)R);
   return hipGetLastError();
 }
 
-// Launches h quantization and the down GEMM (y_rows for the same experts).
-hipError_t launch_mfma_down(int T, int k, const moe_mxfp4_weights& w, const int32_t* offsets,
-                            const int32_t* sorted_rows, const int32_t* active, const float* h, float* y_rows,
+// Launches the down GEMM (y_rows for the same experts) on the h terms the
+// gate/up GEMM wrote.
+hipError_t launch_mfma_down(int T, int k, const moe_mxfp4_weights& w, const int32_t* sorted_rows, float* y_rows,
                             uint8_t* ws, hipStream_t s) {
   const int H = w.hidden, I = w.inter;
   const size_t R = (size_t)T * k;
@@ -948,15 +916,10 @@ hipError_t launch_mfma_down(int T, int k, const moe_mxfp4_weights& w, const int3
   uint8_t* hq = xs + align256((size_t)T * 2 * (H / 32));
   uint8_t* hs = hq + align256(R * 2 * I);
   int32_t* plan = (int32_t*)(hs + align256(R * 2 * (I / 32)));
-  const int64_t nq = (int64_t)R * (I / 32);
-  hipLaunchKernelGGL(quantize_h_kernel, dim3((unsigned)((nq + kThreads - 1) / kThreads)), dim3(kThreads), 0, s, h,
-                     (int)R, I, hq, hs);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
   const int m_tiles = H / kTileRows;
   const unsigned grid = (unsigned)(8 * ((mfma_max_pairs(T, k, w.num_experts) + 7) / 8) * m_tiles);
   hipLaunchKernelGGL((mfma_ffn_kernel<false>), dim3(grid), dim3(kThreads), 0, s, w, k, sorted_rows, plan, hq, hs,
-                     (int)R, y_rows, m_tiles);
+                     (int)R, y_rows, m_tiles, (uint8_t*)nullptr, (uint8_t*)nullptr, 0);
   return hipGetLastError();
 }
 

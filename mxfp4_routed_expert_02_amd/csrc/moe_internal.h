@@ -139,10 +139,8 @@ hipError_t launch_expert_ffn_combine(const uint16_t* x, int T, int k, const moe_
 bool mfma_shape_ok(int H, int I);
 size_t mfma_workspace(int T, int k, int E, int H, int I);
 hipError_t launch_mfma_gateup(const uint16_t* x, int T, int k, const moe_mxfp4_weights& w, const int32_t* offsets,
-                              const int32_t* sorted_rows, const int32_t* active, float* h, uint8_t* ws,
-                              hipStream_t s);
-hipError_t launch_mfma_down(int T, int k, const moe_mxfp4_weights& w, const int32_t* offsets,
-                            const int32_t* sorted_rows, const int32_t* active, const float* h, float* y_rows,
+                              const int32_t* sorted_rows, const int32_t* active, uint8_t* ws, hipStream_t s);
+hipError_t launch_mfma_down(int T, int k, const moe_mxfp4_weights& w, const int32_t* sorted_rows, float* y_rows,
                             uint8_t* ws, hipStream_t s);
 
 hipError_t launch_combine(const float* y_rows, const float* w, const int32_t* row_pos, int T, int k, int H,
