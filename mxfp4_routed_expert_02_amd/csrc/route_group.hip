@@ -199,20 +199,23 @@ __global__ __launch_bounds__(kGroupThreads) void group_scan_kernel(int nch, int 
   __shared__ int s_wave[kGroupThreads / 64 + 1];
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += kGroupThreads) {
-    // counts of up to 32 chunks are loaded before any is rewritten (one
-    // memory round trip per 32 chunks: 8192 rows are 32 chunks)
+    // counts of 8 chunks are loaded before any is rewritten
     int run = 0;
-    for (int c0 = 0; c0 < nch; c0 += 32) {
-      const int n = min(32, nch - c0);
-      int v[32];
+    int c0 = 0;
+    for (; c0 + 8 <= nch; c0 += 8) {
+      int v[8];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) v[i] = cnt[(int64_t)(c0 + min(i, n - 1)) * E + e];  // past n: a repeat
+      for (int i = 0; i < 8; ++i) v[i] = cnt[(int64_t)(c0 + i) * E + e];
 #pragma unroll
-      for (int i = 0; i < 32; ++i)
-        if (i < n) {
-          cnt[(int64_t)(c0 + i) * E + e] = run;
-          run += v[i];
-        }
+      for (int i = 0; i < 8; ++i) {
+        cnt[(int64_t)(c0 + i) * E + e] = run;
+        run += v[i];
+      }
+    }
+    for (int c = c0; c < nch; ++c) {
+      const int v = cnt[(int64_t)c * E + e];
+      cnt[(int64_t)c * E + e] = run;
+      run += v;
     }
     s_tot[e] = run;
   }
