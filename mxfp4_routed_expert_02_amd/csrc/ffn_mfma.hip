@@ -580,7 +580,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     auto sa_base = [&](int st) -> const uint8_t* {
       return s_ring + G::kScaleBase + ((st >> 2) % G::kScaleBufs) * kScaleBuf + as_off + 4 * (st & 3);
     };
-    // stage st's scale words (in slot sl), shifted so that step s's byte is byte 2s
+    // stage st's scale words (in slot sl), as stored
     auto read_sc = [&](int st, int sl, uint32_t (&sa)[RBW], uint32_t (&sb)[2]) {
       const uint8_t* ab = sa_base(st);
 #pragma unroll
@@ -589,8 +589,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       for (int u = 0; u < 2; ++u) sb[u] = *(const uint32_t*)(s_ring + sl * G::kStage + bs_off + u * kBSTerm);
     };
     // The words arrive as stored (this lane's byte of step s at 2s + half);
-    // moving it to byte 2s, the MFMA's select, happens at the start of the
-    // stage that uses them, so no scale read waits for its data mid-stage.
+    // moving it to byte 2s, the MFMA's select, happens in the stage that
+    // uses them (a draining stage at its start, a steady stage just before
+    // each word's first MFMA), so no scale read waits for its data mid-stage.
     auto place_sc = [&](uint32_t (&sa)[RBW], uint32_t (&sb)[2]) {
 #pragma unroll
       for (int j = 0; j < RBW; ++j) sa[j] >>= 8 * half;
@@ -632,8 +633,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // in step 0 of stage st+1, so each step carries a share of the DMA
     // issues.  Loads still go out stage after stage, so the wait counts are
     // those of whole stages.  The steady-state loop (a stage R ahead left to
-    // load) is one basic block, so the step-0 MFMAs stay ahead of the wait
-    // and keep the pipe busy through it; the last R stages drain.
+    // load) is one basic block of two stages, so the step-0 MFMAs stay ahead
+    // of the wait and keep the pipe busy through it; the last R stages drain.
     // Scale block 0, then stages 0 .. R-1 (each with a quarter of block 1,
     // 2, ...); stage R-1's activation loads go out in stage 0.
 #pragma unroll
