@@ -426,14 +426,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int plane = 4 * nb;  // uint4 per staged row
   uint4 qg[U][J], qu[U][J];
   uint32_t sg[U][J], su[U][J];
-  // chunk j of row group u of iteration it (off = kPastEnd: no memory access)
+  // chunk j of row group u of iteration it (off = kPastEnd: no memory
+  // access); with a compile-time row the scale bytes come separately, as
+  // dwords per iteration (load_sc)
   auto load_chunk = [&](int it, int u, int j, uint32_t off) {
     const int n = it * rows_it + u * rpi;
     const uint32_t bq = (uint32_t)n * qrow + off, bs = (uint32_t)(n * nb) + off;
     qg[u][j] = load16(rgq, vq0 + bq + 16u * G * j);
     qu[u][j] = load16(ruq, vq0 + bq + 16u * G * j);
-    sg[u][j] = load1(rgs, vs0 + bs + G * j);
-    su[u][j] = load1(rus, vs0 + bs + G * j);
+    if constexpr (NB == 0) {
+      sg[u][j] = load1(rgs, vs0 + bs + G * j);
+      su[u][j] = load1(rus, vs0 + bs + G * j);
+    }
+  };
+  constexpr int Gc = NB > 0 ? 1 << ctz_const(NB) : 4;  // G when the row is a compile-time shape
+  uint32_t dg[U][scale_dwords<J>()], du[U][scale_dwords<J>()];  // the scale dwords of an iteration
+  auto load_sc = [&](int it, uint32_t off) {
+    const uint32_t row_off = (uint32_t)((it * rows_it + gi) * nb) + off;
+    load_scale_dwords<U, J, Gc>(rgs, row_off, (uint32_t)(rpi * nb), li, dg);
+    load_scale_dwords<U, J, Gc>(rus, row_off, (uint32_t)(rpi * nb), li, du);
   };
   for (int m0 = 0; m0 < cnt; m0 += MT) {
     const int mt = min(MT, cnt - m0);
@@ -442,6 +453,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       for (int j = 0; j < J; ++j)
 #pragma unroll
         for (int u = 0; u < U; ++u) load_chunk(it0, u, j, it0 < it1 ? 0u : kPastEnd);
+      load_sc(it0, it0 < it1 ? 0u : kPastEnd);
     }
     __syncthreads();
     for (int i = threadIdx.x; i < mt * plane; i += kThreads) {
@@ -458,6 +470,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         for (int j = 0; j < J; ++j)
 #pragma unroll
           for (int u = 0; u < U; ++u) load_chunk(it, u, j, 0u);
+      } else {
+        spread_scale_bytes<U, J, Gc>(dg, gi, li, sg);
+        spread_scale_bytes<U, J, Gc>(du, gi, li, su);
+        load_sc(it + istep, next_off);
       }
       float ag[U][MT], au[U][MT];
 #pragma unroll
