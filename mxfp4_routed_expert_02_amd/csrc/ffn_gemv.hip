@@ -327,70 +327,15 @@ __device__ __forceinline__ void spread_scale_bytes(const uint32_t (&d)[U][scale_
 // (all are far below 2 GiB), so the load returns 0 without a memory access.
 constexpr uint32_t kPastEnd = 0x80000000u;
 
-// Slots of the experts with exactly one routed row (l1) and with 2 .. reg_max
-// rows (l4), in slot order: l[0] = count, l[1..] = slots.  One block.
+// The register GEMVs' class lists (build_small_lists), one block.
 __global__ __launch_bounds__(kThreads) void small_lists_kernel(const int32_t* __restrict__ offsets,
                                                               const int32_t* __restrict__ active,
                                                               int32_t* __restrict__ l1, int32_t* __restrict__ l4,
                                                               int lo4, int reg_max) {
-  __shared__ int s_part[2][kWaves];
-  const int na = active[0];
-  const int lane = threadIdx.x & (MOE_WAVE - 1), wave = threadIdx.x / MOE_WAVE;
-  int base1 = 0, base4 = 0;
-  for (int a0 = 0; a0 < na; a0 += kThreads) {
-    const int a = a0 + threadIdx.x;
-    int f1 = 0, f4 = 0;
-    if (a < na) {
-      const int e = active[1 + a];
-      const int cnt = offsets[e + 1] - offsets[e];
-      f1 = cnt == 1 && lo4 > 1;
-      f4 = cnt >= lo4 && cnt <= reg_max;
-    }
-    int v1 = f1, v4 = f4;
-#pragma unroll
-    for (int o = 1; o < MOE_WAVE; o <<= 1) {
-      const int u1 = __shfl_up(v1, o, MOE_WAVE), u4 = __shfl_up(v4, o, MOE_WAVE);
-      if (lane >= o) {
-        v1 += u1;
-        v4 += u4;
-      }
-    }
-    if (lane == MOE_WAVE - 1) {
-      s_part[0][wave] = v1;
-      s_part[1][wave] = v4;
-    }
-    __syncthreads();
-    int b1 = base1 + v1 - f1, b4 = base4 + v4 - f4, t1 = 0, t4 = 0;
-    for (int w2 = 0; w2 < kWaves; ++w2) {
-      if (w2 < wave) {
-        b1 += s_part[0][w2];
-        b4 += s_part[1][w2];
-      }
-      t1 += s_part[0][w2];
-      t4 += s_part[1][w2];
-    }
-    if (f1) l1[1 + b1] = a;
-    if (f4) l4[1 + b4] = a;
-    base1 += t1;
-    base4 += t4;
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    l1[0] = base1;
-    l4[0] = base4;
-  }
+  __shared__ int s_part[2 * kWaves];
+  build_small_lists<kThreads>(offsets, active, l1, l4, lo4, reg_max, s_part);
 }
 
-
-// Experts whose row count lies in [cnt_lo, cnt_hi] run here, MT rows at a
-// time: a weight chunk is loaded and dequantized once and applied to each of
-// the MT rows with exactly the arithmetic a single row gets, so a token's
-// result does not depend on how many other tokens share its experts.
-// The waves of an expert take its row-iterations round robin.  With a
-// compile-time row shape (NB > 0) each chunk's registers are refilled with
-// the wave's next iteration as soon as the chunk has been used (rolling
-// prefetch, as in the one-token kernels); run-time shapes load a whole
-// iteration at its start, which keeps their wider variants out of spills.
 template <int J, int U, int MT, int NB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void gateup_gemv_reg_kernel(
     const uint16_t* __restrict__ x, int k, moe_mxfp4_weights w, const int32_t* __restrict__ offsets,
@@ -1313,7 +1258,11 @@ hipError_t expert_ffn_impl(const uint16_t* x, int T, int k, const moe_mxfp4_weig
     l1 = (int32_t*)((uint8_t*)ws + off);
     l4 = l1 + 1 + max_active;
     off += lists_bytes(T, k, E);
-    if ((reg_g || reg_d) && !all_reg) {  // with every expert on the GEMVs the active list is the class list
+    if (use_mfma) {  // the grouped GEMM's prep launch also writes the class lists
+      if ((err = launch_mfma_prep(x, T, k, w, offsets, active, (uint8_t*)ws + off, l1, l4, lo4, reg_max, s)) !=
+          hipSuccess)
+        return err;
+    } else if ((reg_g || reg_d) && !all_reg) {  // with every expert on the GEMVs the active list is the class list
       hipLaunchKernelGGL(small_lists_kernel, dim3(1), dim3(kThreads), 0, s, offsets, active, l1, l4, lo4, reg_max);
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
@@ -1347,7 +1296,7 @@ hipError_t expert_ffn_impl(const uint16_t* x, int T, int k, const moe_mxfp4_weig
   if (gateup_only) return hipSuccess;
   uint8_t* mfma_ws = (uint8_t*)ws + off;
   if (use_mfma) {
-    if ((err = launch_mfma_gateup(x, T, k, w, offsets, sorted_rows, active, mfma_ws, s)) != hipSuccess)
+    if ((err = launch_mfma_gateup(T, k, w, sorted_rows, mfma_ws, s)) != hipSuccess)
       return err;
   } else if (!reg_g || (T > 1 && !all_reg)) {
     const int mt_g = pick_mt((size_t)H * 2);

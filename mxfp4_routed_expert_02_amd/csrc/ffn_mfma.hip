@@ -207,16 +207,23 @@ __device__ __forceinline__ void e4m3_two_terms(float (&v)[32], int row, int rows
   }
 }
 
-// x [T][H] bf16 -> two E2M3 terms; block 0 also writes the tile plan: the
-// pair count in plan[0], and from int4 1 on one record per token tile of
+// x [T][H] bf16 -> two E2M3 terms (blocks 2 ..).  Block 0 writes the tile
+// plan: the pair count in plan[0], and from int4 1 on one record per token tile of
 // every active expert with more than reg_max rows: (expert, its first
 // sorted row, its row count, the tile's first token), so a GEMM block finds
-// its work with one load after the count.
+// its work with one load after the count.  Block 1 writes the register
+// GEMVs' class lists l1 / l4, so they need no launch of their own.
 __global__ __launch_bounds__(kThreads) void mfma_prep_kernel(const uint16_t* __restrict__ x, int T, int H,
                                                             const int32_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ active,
                                                             uint8_t* __restrict__ xq, int32_t* __restrict__ plan,
-                                                            int reg_max) {
+                                                            int reg_max, int32_t* __restrict__ l1,
+                                                            int32_t* __restrict__ l4, int lo4) {
+  if (blockIdx.x == 1) {  // the register GEMVs' class lists, beside the plan
+    __shared__ int s_lists[2 * kThreads / MOE_WAVE];
+    build_small_lists<kThreads>(offsets, active, l1, l4, lo4, reg_max, s_lists);
+    return;
+  }
   if (blockIdx.x == 0) {
     // Tile plan: the (expert, token tile) pairs of experts with more than
     // reg_max rows, heaviest first: tiles with 4 token groups (65..128
@@ -297,7 +304,7 @@ __global__ __launch_bounds__(kThreads) void mfma_prep_kernel(const uint16_t* __r
     return;
   }
   const int nblk = H >> 5;
-  const int64_t i = (int64_t)(blockIdx.x - 1) * kThreads + threadIdx.x;
+  const int64_t i = (int64_t)(blockIdx.x - 2) * kThreads + threadIdx.x;
   if (i >= (int64_t)T * nblk) return;
   quantize_block_fp6(x, (int)(i / nblk), T, (int)(i % nblk), H, xq);
 }
@@ -883,10 +890,11 @@ size_t mfma_max_pairs(int T, int k, int E) {
   return R / kTileTok + (mx < R / per ? mx : R / per) + 1;
 }
 
-// Launches prep and the gate/up GEMM, which writes h of the experts with
-// more than reg_rows_max(T) rows as the down GEMM's two E4M3 terms.
-hipError_t launch_mfma_gateup(const uint16_t* x, int T, int k, const moe_mxfp4_weights& w, const int32_t* offsets,
-                              const int32_t* sorted_rows, const int32_t* active, uint8_t* ws, hipStream_t s) {
+// Launches prep: the x terms, the tile plan of the experts with more than
+// reg_rows_max(T) rows, and the register GEMVs' class lists l1 / l4.
+hipError_t launch_mfma_prep(const uint16_t* x, int T, int k, const moe_mxfp4_weights& w, const int32_t* offsets,
+                            const int32_t* active, uint8_t* ws, int32_t* l1, int32_t* l4, int lo4, int reg_max,
+                            hipStream_t s) {
   const int H = w.hidden, I = w.inter;
   const size_t R = (size_t)T * k;
   uint8_t* xq = ws;
@@ -895,10 +903,22 @@ hipError_t launch_mfma_gateup(const uint16_t* x, int T, int k, const moe_mxfp4_w
   uint8_t* hs = hq + align256(R * 2 * I);
   int32_t* plan = (int32_t*)(hs + align256(R * 2 * (I / 32)));
   const int64_t nq = (int64_t)T * (H / 32);
-  hipLaunchKernelGGL(mfma_prep_kernel, dim3(1 + (unsigned)((nq + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
-                     x, T, H, offsets, active, xq, plan, reg_rows_max(T));
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(mfma_prep_kernel, dim3(2 + (unsigned)((nq + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
+                     x, T, H, offsets, active, xq, plan, reg_max, l1, l4, lo4);
+  return hipGetLastError();
+}
+
+// Launches the gate/up GEMM, which writes h of the experts with more than
+// reg_rows_max(T) rows as the down GEMM's two E4M3 terms.
+hipError_t launch_mfma_gateup(int T, int k, const moe_mxfp4_weights& w, const int32_t* sorted_rows, uint8_t* ws,
+                              hipStream_t s) {
+  const int H = w.hidden, I = w.inter;
+  const size_t R = (size_t)T * k;
+  uint8_t* xq = ws;
+  uint8_t* xs = xq + align256((size_t)T * 2 * H);
+  uint8_t* hq = xs + align256((size_t)T * 2 * (H / 32));
+  uint8_t* hs = hq + align256(R * 2 * I);
+  int32_t* plan = (int32_t*)(hs + align256(R * 2 * (I / 32)));
   const int m_tiles = I / (kTileRows / 2);
   const unsigned grid = (unsigned)(8 * ((mfma_max_pairs(T, k, w.num_experts) + 7) / 8) * m_tiles);
   hipLaunchKernelGGL((mfma_ffn_kernel<true>), dim3(grid), dim3(kThreads), 0, s, w, k, sorted_rows, plan, xq, xs, T,

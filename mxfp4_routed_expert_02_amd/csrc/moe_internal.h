@@ -98,6 +98,62 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f +
 // owning float4 c + kRmsThreads*i of the row; a thread's squares summed
 // float4 by float4 (sumsq4), then a wave butterfly (wave_sum), then the
 // kRmsThreads/64 wave sums in wave order; factor 1/sqrt(mean + eps).
+// Slots of the experts with exactly one routed row (l1, when lo4 > 1) and
+// with lo4 .. reg_max rows (l4), in slot order: l[0] = count, l[1..] =
+// slots.  Run by one block of kThreadsT threads; s_part is LDS for
+// 2 * kThreadsT / MOE_WAVE ints.
+template <int kThreadsT>
+__device__ __forceinline__ void build_small_lists(const int32_t* __restrict__ offsets,
+                                                  const int32_t* __restrict__ active, int32_t* __restrict__ l1,
+                                                  int32_t* __restrict__ l4, int lo4, int reg_max, int* s_part) {
+  constexpr int kW = kThreadsT / MOE_WAVE;
+  const int na = active[0];
+  const int lane = threadIdx.x & (MOE_WAVE - 1), wave = threadIdx.x / MOE_WAVE;
+  int base1 = 0, base4 = 0;
+  for (int a0 = 0; a0 < na; a0 += kThreadsT) {
+    const int a = a0 + threadIdx.x;
+    int f1 = 0, f4 = 0;
+    if (a < na) {
+      const int e = active[1 + a];
+      const int cnt = offsets[e + 1] - offsets[e];
+      f1 = cnt == 1 && lo4 > 1;
+      f4 = cnt >= lo4 && cnt <= reg_max;
+    }
+    int v1 = f1, v4 = f4;
+#pragma unroll
+    for (int o = 1; o < MOE_WAVE; o <<= 1) {
+      const int u1 = __shfl_up(v1, o, MOE_WAVE), u4 = __shfl_up(v4, o, MOE_WAVE);
+      if (lane >= o) {
+        v1 += u1;
+        v4 += u4;
+      }
+    }
+    if (lane == MOE_WAVE - 1) {
+      s_part[wave] = v1;
+      s_part[kW + wave] = v4;
+    }
+    __syncthreads();
+    int b1 = base1 + v1 - f1, b4 = base4 + v4 - f4, t1 = 0, t4 = 0;
+    for (int w2 = 0; w2 < kW; ++w2) {
+      if (w2 < wave) {
+        b1 += s_part[w2];
+        b4 += s_part[kW + w2];
+      }
+      t1 += s_part[w2];
+      t4 += s_part[kW + w2];
+    }
+    if (f1) l1[1 + b1] = a;
+    if (f4) l4[1 + b4] = a;
+    base1 += t1;
+    base4 += t4;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    l1[0] = base1;
+    l4[0] = base4;
+  }
+}
+
 constexpr int kRmsThreads = 1024;
 constexpr int kRmsVec = 4;  // float4 per thread (H <= 16384)
 __device__ __forceinline__ float sumsq4(const float4& v) { return v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w; }
@@ -138,8 +194,11 @@ hipError_t launch_expert_ffn_combine(const uint16_t* x, int T, int k, const moe_
 // MFMA grouped-GEMM path (experts with more than 4 routed rows)
 bool mfma_shape_ok(int H, int I);
 size_t mfma_workspace(int T, int k, int E, int H, int I);
-hipError_t launch_mfma_gateup(const uint16_t* x, int T, int k, const moe_mxfp4_weights& w, const int32_t* offsets,
-                              const int32_t* sorted_rows, const int32_t* active, uint8_t* ws, hipStream_t s);
+hipError_t launch_mfma_prep(const uint16_t* x, int T, int k, const moe_mxfp4_weights& w, const int32_t* offsets,
+                            const int32_t* active, uint8_t* ws, int32_t* l1, int32_t* l4, int lo4, int reg_max,
+                            hipStream_t s);
+hipError_t launch_mfma_gateup(int T, int k, const moe_mxfp4_weights& w, const int32_t* sorted_rows, uint8_t* ws,
+                              hipStream_t s);
 hipError_t launch_mfma_down(int T, int k, const moe_mxfp4_weights& w, const int32_t* sorted_rows, float* y_rows,
                             uint8_t* ws, hipStream_t s);
 
