@@ -349,7 +349,35 @@ struct Ring {
   static_assert(kBytes <= kLdsBytes, "ring fits in LDS");
 };
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
-constexpr int kRingBytes = cmax(cmax(Ring<1, false>::kBytes, Ring<2, false>::kBytes), Ring<4, false>::kBytes);
+// One-group tiles (1..32 routed rows) are bound by their weight stream.
+// They run 256-value stages, so that every weight DMA load covers 8 rows x
+// 128 bytes (whole cache lines) and can carry the non-temporal policy.  A
+// slot holds
+//   A   [256 rows][128 B]              piece p of row r at r*128 + 16*(p ^ ((r >> 1) & 7))
+//   B   [2 terms][2 records][32][128 B] the stage's two 128-value records of
+//                                      each (term, token t), piece p at
+//                                      16*(p ^ ((t >> 1) & 7))
+//   BS  [2 terms][2 records][32][4 B]  (E4M3 terms only) their scale words
+// in a ring of 3 slots; the weight scales travel in blocks of two stages
+// (16 bytes per row) through 3 buffers after the ring.
+template <bool FP6>
+struct Ring1 {
+  static constexpr int kA = kTileRows * 128;
+  static constexpr int kB = 2 * 2 * 32 * 128;
+  static constexpr int kBS = FP6 ? 0 : 2 * 2 * 32 * 4;
+  static constexpr int kStage = kA + kB + kBS;
+  static constexpr int kSlots = 3;
+  // a scale block is refilled only after the barrier that follows its last
+  // reader: 2 * kScaleBufs >= kSlots + 3
+  static constexpr int kScaleBufs = (kSlots + 3 + 1) / 2;
+  static constexpr int kScaleBase = kSlots * kStage;
+  static constexpr int kBytes = kScaleBase + kScaleBufs * kScaleBuf;
+  static constexpr int kX = 8 + 2;                       // weight loads per wave and stage: codes, 2 scale quarters
+  static constexpr int kOps = kX + 4 + (FP6 ? 0 : 1);    // and activation loads (terms, E4M3 scale words)
+  static_assert(kBytes <= kLdsBytes, "ring fits in LDS");
+};
+constexpr int kRingBytes = cmax(cmax(cmax(Ring<2, false>::kBytes, Ring<4, false>::kBytes), Ring1<false>::kBytes),
+                                Ring1<true>::kBytes);
 
 // LDS DMA loads of 16 and 4 bytes per lane to the wave-uniform LDS address
 // `lds` (lane l at lds + size*l).  Issued from asm, so the compiler neither
@@ -361,6 +389,10 @@ __device__ __forceinline__ void lds_dma16(const void* base, uint32_t off, uint32
 }
 __device__ __forceinline__ void lds_dma4(const void* base, uint32_t off, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(lds) : "memory", "m0");
+}
+
+__device__ __forceinline__ void lds_dma16_nt(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(off), "s"(base), "s"(lds) : "memory", "m0");
 }
 
 // s_waitcnt vmcnt(N) (N clamped to the counter's 63) with the other counters free
@@ -478,6 +510,76 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // blocks: gate/up keeps each gate block with its up block (b and b+4).
   const int rows_in_tile = min(cnt - tok0, kTileTok);
   const int tg = rows_in_tile <= 32 ? 1 : rows_in_tile <= 64 ? 2 : 4;
+
+  // Epilogue of a tile (acc: RBW row blocks of 32 rows x 32 tokens, row
+  // block j at rows 32 rb_of(j); this lane's token tt).
+  auto store_tile = [&](auto tok_c, auto rbw_c, const auto& acc, auto rb_of, int tt) {
+    constexpr int kTok = decltype(tok_c)::value;
+    constexpr int RBW = decltype(rbw_c)::value;
+    // Epilogue: the tile's outputs pass through LDS (the ring is free once
+    // every wave is past its last fragment reads), so that each store
+    // instruction writes whole output rows (1 KB contiguous) instead of 64
+    // scattered 16-byte pieces of 32 token rows.  LDS rows are padded by 4
+    // floats: a 16-lane group's float4 writes then hit 64 distinct banks.
+    constexpr int kCols = GATEUP ? kTileRows / 2 : kTileRows;  // output columns of the tile
+    constexpr int kPitch = kCols + 4;                           // floats per LDS row
+    static_assert(kTok * kPitch * 4 <= kRingBytes, "the output tile fits in the ring's LDS");
+    float* so = (float*)s_ring;
+    wait_vm<0>();  // no LDS DMA of this wave still in flight (the last scale prefetch)
+    __syncthreads();
+    float* srow = so + tt * kPitch;  // this lane's token
+    if (GATEUP) {
+      // j < RBW/2: gate block rb_of(j); j + RBW/2: the matching up block
+#pragma unroll
+      for (int j = 0; j < RBW / 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int c = 32 * rb_of(j) + 8 * g + 4 * half;
+          float4 v;
+          v.x = silu_mul(acc[j][4 * g + 0], acc[j + RBW / 2][4 * g + 0]);
+          v.y = silu_mul(acc[j][4 * g + 1], acc[j + RBW / 2][4 * g + 1]);
+          v.z = silu_mul(acc[j][4 * g + 2], acc[j + RBW / 2][4 * g + 2]);
+          v.w = silu_mul(acc[j][4 * g + 3], acc[j + RBW / 2][4 * g + 3]);
+          *(float4*)(srow + c) = v;
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < RBW; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int c = 32 * rb_of(j) + 8 * g + 4 * half;
+          *(float4*)(srow + c) = make_float4(acc[j][4 * g + 0], acc[j][4 * g + 1], acc[j][4 * g + 2], acc[j][4 * g + 3]);
+        }
+      }
+    }
+    __syncthreads();
+    const int nrow = min(kTok, cnt - tok0);  // tokens of the tile with routed rows
+    if (GATEUP) {
+      // h never goes to memory in fp32: each thread takes (token, 32-block)
+      // items of the tile's 128 columns (one 128-value K stage of the down
+      // GEMM) and writes their two E4M3 terms, the down GEMM's B operand
+      for (int it = tid; it < 4 * nrow; it += kThreads) {
+        const int t = it >> 2, b = it & 3;
+        const float4* src = (const float4*)(so + t * kPitch + 32 * b);
+        float v[32];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float4 f = src[i];
+          v[4 * i] = f.x;
+          v[4 * i + 1] = f.y;
+          v[4 * i + 2] = f.z;
+          v[4 * i + 3] = f.w;
+        }
+        e4m3_two_terms(v, p0 + tok0 + t, hrows, row0 / 32 + b, hq, hs);
+      }
+    } else {
+      constexpr int kLanesPerRow = kCols / 4;              // float4 of an output row
+      constexpr int kRowsPerOp = MOE_WAVE / kLanesPerRow;  // output rows per store instruction
+      const int c4 = lane % kLanesPerRow;
+      for (int t = wave * kRowsPerOp + lane / kLanesPerRow; t < nrow; t += 4 * kRowsPerOp)
+        *(float4*)(out + (int64_t)(p0 + tok0 + t) * out_cols + row0 + 4 * c4) = *(const float4*)(so + t * kPitch + 4 * c4);
+    }
+  };
 
   auto body = [&](auto tg_c) {
     constexpr int TG = decltype(tg_c)::value;
@@ -790,71 +892,272 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     }
     for (; st < nst; ++st) drain_stage();
 
-    // Epilogue: the tile's outputs pass through LDS (the ring is free once
-    // every wave is past its last fragment reads), so that each store
-    // instruction writes whole output rows (1 KB contiguous) instead of 64
-    // scattered 16-byte pieces of 32 token rows.  LDS rows are padded by 4
-    // floats: a 16-lane group's float4 writes then hit 64 distinct banks.
-    constexpr int kCols = GATEUP ? kTileRows / 2 : kTileRows;  // output columns of the tile
-    constexpr int kPitch = kCols + 4;                           // floats per LDS row
-    static_assert(G::kTok * kPitch * 4 <= kRingBytes, "the output tile fits in the ring's LDS");
-    float* so = (float*)s_ring;
-    wait_vm<0>();  // no LDS DMA of this wave still in flight (the last scale prefetch)
-    __syncthreads();
-    float* srow = so + tt * kPitch;  // this lane's token
-    if (GATEUP) {
-      // j < RBW/2: gate block rb_of(j); j + RBW/2: the matching up block
+    store_tile(std::integral_constant<int, G::kTok>(), std::integral_constant<int, RBW>(), acc, rb_of, tt);
+  };
+  // One-group tiles: 256-value stages of four 64-deep steps (Ring1).  Wave
+  // w takes row blocks w and w + 4 (gate/up: a gate block and its up block)
+  // for the tile's 32 token slots.  Per stage and wave: 8 weight-code loads
+  // (chunk c = 4i + w: rows 8c .. 8c+7, 128 bytes each, non-temporal), 2
+  // quarters of a weight-scale block, 4 activation-term loads (chunk c = w +
+  // 4j: units v = 8c + lane/8 = (term, record, token)), for E4M3 terms one
+  // scale-word load.  The pipeline is the generic one's with four steps: the
+  // barrier follows the reads of the stage's last step, the freed slot's
+  // weight loads and the next stage's reads go with step 3, and the
+  // activation loads of a stage follow in step 0 of the stage after.
+  auto body1 = [&]() {
+    constexpr bool FP6 = GATEUP;
+    using G = Ring1<FP6>;
+    constexpr int R = G::kSlots;
+    constexpr int RBW = 2;
+    constexpr int S = 4;
+    const int nst1 = K / 256;
+    const int nblk = nst1 >> 1;  // scale blocks (two stages) per row
+    auto rel = [](int j) { return j == 0 ? 0 : kRB / 2; };
+    auto rb_of = [&](int j) { return wave + rel(j); };
+
+    // DMA sources: wave-uniform bases, per-lane 32-bit offsets
+    const int apiece = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
+    const uint8_t* const a_base[2] = {a_row(0), a_row(kTileRows / 2)};
+    const uint8_t* const as_base[2] = {a_srow(0), a_srow(kTileRows / 2)};
+    uint32_t a_off_s[8];
 #pragma unroll
-      for (int j = 0; j < RBW / 2; ++j)
+    for (int i = 0; i < 8; ++i)
+      a_off_s[i] = (uint32_t)((8 * (4 * i + wave) + (lane >> 3) - (i >= 4 ? kTileRows / 2 : 0)) * qrow + 16 * apiece);
+    const uint32_t as_off_s = (uint32_t)((16 * wave + (lane >> 2)) * nsb + 4 * (lane & 3));
+    uint32_t b_off_s[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int c = 32 * rb_of(j) + 8 * g + 4 * half;
-          float4 v;
-          v.x = silu_mul(acc[j][4 * g + 0], acc[j + RBW / 2][4 * g + 0]);
-          v.y = silu_mul(acc[j][4 * g + 1], acc[j + RBW / 2][4 * g + 1]);
-          v.z = silu_mul(acc[j][4 * g + 2], acc[j + RBW / 2][4 * g + 2]);
-          v.w = silu_mul(acc[j][4 * g + 3], acc[j + RBW / 2][4 * g + 3]);
-          *(float4*)(srow + c) = v;
+    for (int j = 0; j < 4; ++j) {
+      const int v = 8 * (wave + 4 * j) + (lane >> 3);
+      const int u = v >> 6, r = (v >> 5) & 1, t = v & 31;
+      b_off_s[j] = (uint32_t)(((r * (int64_t)brows + b_row(t)) * 2 + u) * 128 + 16 * ((lane & 7) ^ ((t >> 1) & 7)));
+    }
+    const int bsd = 64 * (wave & 1) + lane;  // E4M3 scale word: (term, record, token) = (bsd >> 6, (bsd >> 5) & 1, bsd & 31)
+    const uint32_t bs_off_s =
+        (uint32_t)((((bsd >> 5) & 1) * (int64_t)brows + b_row(bsd & 31)) * 8 + 4 * (bsd >> 6));
+    const int64_t bq_stage = (int64_t)brows * 512, bs_stage = (int64_t)brows * 16;
+
+    auto issue_scales = [&](int b, int q) {
+      const uint32_t dst = lds0 + (uint32_t)(G::kScaleBase + (b % G::kScaleBufs) * kScaleBuf + (64 * q + 16 * wave) * 16);
+      lds_dma4(as_base[q >= 2 ? 1 : 0] + (q & 1) * 64 * nsb + 16 * min(b, nblk - 1), as_off_s, dst);
+    };
+    // load o of this wave's share of stage st into slot sl; loads 8 and 9
+    // are quarters 2 (st % 2) and 2 (st % 2) + 1 of the scale block after st's
+    auto issue_op = [&](int st, int sl, auto o_c) {
+      constexpr int o = decltype(o_c)::value;
+      const uint32_t sb = lds0 + (uint32_t)(sl * G::kStage);
+      if constexpr (o < 8) lds_dma16_nt(a_base[o >= 4 ? 1 : 0] + st * 128, a_off_s[o], sb + (4 * o + wave) * 1024);
+      else if constexpr (o < G::kX) issue_scales((st >> 1) + 1, 2 * (st & 1) + (o - 8));
+      else if constexpr (o < G::kX + 4)
+        lds_dma16(bq + st * bq_stage, b_off_s[o - G::kX], sb + G::kA + (wave + 4 * (o - G::kX)) * 1024);
+      else lds_dma4(bs + st * bs_stage, bs_off_s, sb + G::kA + G::kB + (wave & 1) * 256);
+    };
+    auto issue_x = [&](int st, int sl) { static_for<0, G::kX>([&](auto o) { issue_op(st, sl, o); }); };
+    auto issue_y = [&](int st, int sl) { static_for<G::kX, G::kOps>([&](auto o) { issue_op(st, sl, o); }); };
+
+    // fragment offsets within a slot: A row 32 rb + n, piece 2s + half; B
+    // record (term u, record s/2, token n): E2M3 the 16 bytes of piece
+    // 3(s%2) + half and the 8 bytes at 8 half in piece 3(s%2) + 2, its scale
+    // word at 4 half in piece 6; E4M3 pieces 4(s%2) + 2 half + i
+    const int bsw = (n >> 1) & 7;
+    uint32_t a_off[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) a_off[s] = (uint32_t)((32 * wave + n) * 128 + 16 * ((2 * s + half) ^ bsw));
+    constexpr int kRecB = 32 * 128;  // bytes between records of one term
+    uint32_t b_off[S][2];
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int sp = s & 1;
+        const uint32_t rec = (uint32_t)(G::kA + (s >> 1) * kRecB + n * 128);
+        b_off[s][i] = FP6 ? rec + (i == 0 ? 16 * ((3 * sp + half) ^ bsw) : 16 * ((3 * sp + 2) ^ bsw) + 8 * half)
+                          : rec + 16 * ((4 * sp + 2 * half + i) ^ bsw);
+      }
+    // scale words of record r (steps 2r, 2r+1): E2M3 in the record, E4M3 in BS
+    auto sb_off = [&](int u, int r) -> uint32_t {
+      return FP6 ? (uint32_t)(G::kA + (2 * u + r) * kRecB + n * 128 + 16 * (6 ^ bsw) + 4 * half)
+                 : (uint32_t)(G::kA + G::kB + ((2 * u + r) * 32 + n) * 4);
+    };
+    constexpr int kTermB = 2 * kRecB;  // bytes between the terms' records
+    constexpr int kBSShift = FP6 ? 0 : 1;
+    const uint32_t as_off = (uint32_t)((32 * wave + n) * 16);  // within a scale buffer
+    auto ld_b = [&](const uint8_t* p, int i) -> uint4 {
+      if (FP6 && i == 1) {
+        const uint2 v = *(const uint2*)p;
+        return make_uint4(v.x, v.y, 0u, 0u);
+      }
+      return *(const uint4*)p;
+    };
+    // fragments of step s of the stage in slot sl
+    auto read_a = [&](int sl, int s, uint4 (&a)[RBW]) {
+      const uint8_t* base = s_ring + sl * G::kStage + a_off[s];
+#pragma unroll
+      for (int j = 0; j < RBW; ++j) a[j] = *(const uint4*)(base + 32 * rel(j) * 128);
+    };
+    auto read_b = [&](int sl, int s, uint4 (&b)[2][2]) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) b[u][i] = ld_b(s_ring + sl * G::kStage + b_off[s][i] + u * kTermB, i);
+    };
+    // scale words of stage st (slot sl) as stored: sa[j][r], sb[u][r] serve steps 2r, 2r+1
+    auto read_sc = [&](int st, int sl, uint32_t (&sa)[RBW][2], uint32_t (&sb)[2][2]) {
+      const uint8_t* ab = s_ring + G::kScaleBase + ((st >> 1) % G::kScaleBufs) * kScaleBuf + as_off + 8 * (st & 1);
+#pragma unroll
+      for (int j = 0; j < RBW; ++j)
+#pragma unroll
+        for (int r = 0; r < 2; ++r) sa[j][r] = *(const uint32_t*)(ab + 32 * rel(j) * 16 + 4 * r);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int r = 0; r < 2; ++r) sb[u][r] = *(const uint32_t*)(s_ring + sl * G::kStage + sb_off(u, r));
+    };
+
+    v16f_t acc[RBW];
+#pragma unroll
+    for (int j = 0; j < RBW; ++j)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[j][i] = 0.0f;
+    constexpr int kBFmt = FP6 ? 2 : 0;
+    // the MFMAs of step s, term major; scale words shifted to the MFMA's byte
+    // select on their first use (step 2r for record r)
+    auto mma_step = [&](auto s_c, const uint4 (&a)[RBW], const uint4 (&b)[2][2], uint32_t (&sa)[RBW][2],
+                        uint32_t (&sb)[2][2]) {
+      constexpr int s = decltype(s_c)::value;
+      constexpr int r = s >> 1, OP = 2 * (s & 1);
+      if constexpr ((s & 1) == 0) {
+#pragma unroll
+        for (int j = 0; j < RBW; ++j) sa[j][r] >>= 8 * half;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) sb[u][r] >>= 8 * half * kBSShift;
+      }
+      const v8i_t B0 = pack_b(b[0][0], b[0][1]), B1 = pack_b(b[1][0], b[1][1]);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < RBW; ++j) {
+          v8i_t A;
+          A[0] = a[j].x; A[1] = a[j].y; A[2] = a[j].z; A[3] = a[j].w;
+          A[4] = 0; A[5] = 0; A[6] = 0; A[7] = 0;
+          acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, u == 0 ? B0 : B1, acc[j], 4, kBFmt, OP,
+                                                                   sa[j][r], OP, sb[u][r]);
         }
-    } else {
+    };
+
+    // prologue: scale block 0, then stages 0 .. R-1 (stage R-1's activation
+    // loads go out in stage 0)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) issue_scales(0, q);
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+      if (j < nst1) {
+        issue_x(j, j);
+        if (j < R - 1) issue_y(j, j);
+      }
+    if (nst1 >= R)
+      wait_vm<(R - 2) * G::kOps + G::kX>();
+    else
+      wait_stages<G::kOps>(nst1 - 1);
+    __syncthreads();
+    uint4 fa[2][RBW], fb[2][2][2];  // fragments of the current and the next step
+    uint32_t sa[2][RBW][2], sb[2][2][2];
+    read_sc(0, 0, sa[0], sb[0]);
+    read_a(0, 0, fa[0]);
+    read_b(0, 0, fb[0]);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the loop's waits then follow its own reads
+    int st = 0, sl = 0;
+
+    // Steady stage (a stage R ahead left to load), scale set P current
+    auto steady_stage = [&](auto p_c) {
+      constexpr int P = decltype(p_c)::value, Q = 1 - P;
+      const int psl = sl == 0 ? R - 1 : sl - 1;  // slot of stage st+R-1
+      const int nsl = sl + 1 == R ? 0 : sl + 1;
+      // step 0: its MFMAs, the activation loads of stage st+R-1, step 1's fragments
+      read_a(sl, 1, fa[1]);
+      read_b(sl, 1, fb[1]);
+      mma_step(std::integral_constant<int, 0>(), fa[0], fb[0], sa[P], sb[P]);
+      issue_y(st + R - 1, psl);
+      __builtin_amdgcn_sched_barrier(0);
+      // step 1, step 2's fragments
+      read_a(sl, 2, fa[0]);
+      read_b(sl, 2, fb[0]);
+      mma_step(std::integral_constant<int, 1>(), fa[1], fb[1], sa[P], sb[P]);
+      __builtin_amdgcn_sched_barrier(0);
+      // step 2, step 3's fragments (the last reads of this slot)
+      read_a(sl, 3, fa[1]);
+      read_b(sl, 3, fb[1]);
+      mma_step(std::integral_constant<int, 2>(), fa[0], fb[0], sa[P], sb[P]);
+      __builtin_amdgcn_sched_barrier(0);
+      // stage st+1 in LDS, nobody reads slot sl any more
+      wait_vm<(R - 2) * G::kOps>();
+      __syncthreads();
+      // step 3, the freed slot's weight loads, the next stage's step-0 fragments and scale words
+      issue_x(st + R, sl);
+      read_sc(st + 1, nsl, sa[Q], sb[Q]);
+      read_a(nsl, 0, fa[0]);
+      read_b(nsl, 0, fb[0]);
+      mma_step(std::integral_constant<int, 3>(), fa[1], fb[1], sa[P], sb[P]);
+      __builtin_amdgcn_sched_barrier(0);
+      sl = nsl;
+    };
+    // Draining stage: nothing left to load; scale set 0 current
+    auto drain_stage = [&]() {
+      if (st + R - 1 < nst1) issue_y(st + R - 1, sl == 0 ? R - 1 : sl - 1);  // the last stage's activations
+      const int nsl = sl + 1 == R ? 0 : sl + 1;
+      read_a(sl, 1, fa[1]);
+      read_b(sl, 1, fb[1]);
+      mma_step(std::integral_constant<int, 0>(), fa[0], fb[0], sa[0], sb[0]);
+      read_a(sl, 2, fa[0]);
+      read_b(sl, 2, fb[0]);
+      mma_step(std::integral_constant<int, 1>(), fa[1], fb[1], sa[0], sb[0]);
+      read_a(sl, 3, fa[1]);
+      read_b(sl, 3, fb[1]);
+      mma_step(std::integral_constant<int, 2>(), fa[0], fb[0], sa[0], sb[0]);
+      if (st + 1 < nst1) {
+        wait_stages<G::kOps>(nst1 - 2 - st);
+        __syncthreads();
+        read_sc(st + 1, nsl, sa[1], sb[1]);
+        read_a(nsl, 0, fa[0]);
+        read_b(nsl, 0, fb[0]);
+      }
+      mma_step(std::integral_constant<int, 3>(), fa[1], fb[1], sa[0], sb[0]);
 #pragma unroll
       for (int j = 0; j < RBW; ++j) {
+        sa[0][j][0] = sa[1][j][0];
+        sa[0][j][1] = sa[1][j][1];
+      }
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int c = 32 * rb_of(j) + 8 * g + 4 * half;
-          *(float4*)(srow + c) = make_float4(acc[j][4 * g + 0], acc[j][4 * g + 1], acc[j][4 * g + 2], acc[j][4 * g + 3]);
-        }
+      for (int u = 0; u < 2; ++u) {
+        sb[0][u][0] = sb[1][u][0];
+        sb[0][u][1] = sb[1][u][1];
+      }
+      sl = nsl;
+    };
+    constexpr std::integral_constant<int, 0> kSet0;
+    constexpr std::integral_constant<int, 1> kSet1;
+    for (; st + R + 1 < nst1; ++st) {
+      steady_stage(kSet0);
+      ++st;
+      steady_stage(kSet1);
+    }
+    if (st + R < nst1) {
+      steady_stage(kSet0);
+      ++st;
+#pragma unroll
+      for (int j = 0; j < RBW; ++j) {
+        sa[0][j][0] = sa[1][j][0];
+        sa[0][j][1] = sa[1][j][1];
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        sb[0][u][0] = sb[1][u][0];
+        sb[0][u][1] = sb[1][u][1];
       }
     }
-    __syncthreads();
-    const int nrow = min(G::kTok, cnt - tok0);  // tokens of the tile with routed rows
-    if (GATEUP) {
-      // h never goes to memory in fp32: each thread takes (token, 32-block)
-      // items of the tile's 128 columns (one 128-value K stage of the down
-      // GEMM) and writes their two E4M3 terms, the down GEMM's B operand
-      for (int it = tid; it < 4 * nrow; it += kThreads) {
-        const int t = it >> 2, b = it & 3;
-        const float4* src = (const float4*)(so + t * kPitch + 32 * b);
-        float v[32];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float4 f = src[i];
-          v[4 * i] = f.x;
-          v[4 * i + 1] = f.y;
-          v[4 * i + 2] = f.z;
-          v[4 * i + 3] = f.w;
-        }
-        e4m3_two_terms(v, p0 + tok0 + t, hrows, row0 / 32 + b, hq, hs);
-      }
-    } else {
-      constexpr int kLanesPerRow = kCols / 4;              // float4 of an output row
-      constexpr int kRowsPerOp = MOE_WAVE / kLanesPerRow;  // output rows per store instruction
-      const int c4 = lane % kLanesPerRow;
-      for (int t = wave * kRowsPerOp + lane / kLanesPerRow; t < nrow; t += 4 * kRowsPerOp)
-        *(float4*)(out + (int64_t)(p0 + tok0 + t) * out_cols + row0 + 4 * c4) = *(const float4*)(so + t * kPitch + 4 * c4);
-    }
+    for (; st < nst1; ++st) drain_stage();
+    store_tile(std::integral_constant<int, 32>(), std::integral_constant<int, RBW>(), acc, rb_of, n);
   };
-  if (tg == 1) body(std::integral_constant<int, 1>());
+  if (tg == 1) body1();
   else if (tg == 2) body(std::integral_constant<int, 2>());
   else body(std::integral_constant<int, 4>());
 }
