@@ -38,15 +38,16 @@
 // rows, so SiLU(g)*u is formed in registers.  Every operand of a 128-value
 // K stage (weight codes and scales, activation terms and scales) travels
 // from global memory into an LDS ring slot by LDS DMA loads, with no trip
-// through registers; the ring keeps up to five stages in flight per CU, so
-// tiles with few tokens stream their weights at memory speed and full
-// tiles keep the MFMA pipe fed.  The waits on those loads are explicit
+// through registers; the ring keeps two or three stages in flight per CU
+// while one is read, so tiles with few tokens stream their weights at
+// memory speed and full tiles keep the MFMA pipe fed.  The waits on those loads are explicit
 // counts of each wave's own loads, which complete in issue order.
 // A tile's 128 token slots form 4 groups of 32; a tile whose expert rows
 // fill only 1 or 2 groups runs with the 4 waves splitting the row blocks
 // instead (2 or 4 blocks each, gate blocks kept with their up blocks) and a
-// deeper ring of smaller slots, so MFMA work follows the routed rows rather
-// than the padded tile.  The plan orders (expert, token tile) pairs
+// ring shaped for them (two groups: a deeper ring of smaller slots; one
+// group: 256-value stages whose weight loads take whole cache lines), so
+// MFMA work follows the routed rows rather than the padded tile.  The plan orders (expert, token tile) pairs
 // heaviest first, an expert's full token tiles next to each other, and
 // deals them to the 8 XCDs in runs of four; each XCD steps through the
 // weight tiles of its run with all four token tiles at each, so the token
@@ -321,8 +322,8 @@ __global__ __launch_bounds__(kThreads) void mfma_prep_kernel(const uint16_t* __r
 //   BS  [2][32*TG][4 B]     their four scale bytes of the stage
 // The XOR swizzles give the 16 lanes that read one K offset of 16
 // consecutive rows or tokens 16 distinct 16-byte bank groups.  A tile with
-// TG token groups of 32 has slots of 24.3, 32.5 or 49 KB and a ring of 5, 4
-// or 3 of them, so 4, 3 or 2 stages are in flight per CU while one is read.
+// TG = 2 or 4 token groups of 32 has slots of 32.5 or 49 KB and a ring of 4
+// or 3 of them, so 3 or 2 stages are in flight per CU while one is read.
 // The weight scales travel in blocks of four stages (16 bytes per row, one
 // memory request per row instead of four) through kScaleBufs buffers of
 // [256 rows][16 B] after the ring; each stage's loads carry a quarter of
@@ -332,12 +333,13 @@ constexpr int kScaleBuf = kTileRows * 16;
 
 template <int TG, bool FP6>
 struct Ring {
+  static_assert(TG == 2 || TG == 4, "one-group tiles use Ring1");
   static constexpr int kTok = 32 * TG;
   static constexpr int kA = kTileRows * 64;
   static constexpr int kB = 2 * kTok * 128;
   static constexpr int kBS = FP6 ? 0 : 2 * kTok * 4;  // FP6 records carry their scales
   static constexpr int kStage = kA + kB + kBS;
-  static constexpr int kSlots = TG == 1 ? 5 : TG == 2 ? 4 : 3;
+  static constexpr int kSlots = TG == 2 ? 4 : 3;
   // a scale block is refilled only after the barrier that follows its last
   // reader: 4 * kScaleBufs >= kSlots + 7
   static constexpr int kScaleBufs = (kSlots + 7 + 3) / 4;

@@ -1,10 +1,11 @@
 """The grouped GEMM's tile classes and stage counts against the oracle.
 
 A tile of 128 token slots runs as one of three classes by the rows it
-holds (1..32, 33..64, 65..128), each with its own LDS ring depth R (5, 4, 3
-slots), and K runs in 128-value stages: K / 128 stages, of which the first
-R are loaded before the loop, the steady loop (two stages per trip) takes
-the rest that still have a stage R ahead to load, and the last R drain.
+holds (1..32, 33..64, 65..128), each with its own LDS ring: 3 slots of
+256-value stages for the first, 4 and 3 slots of 128-value stages for the
+others.  Of the K / stage stages the first R are loaded before the loop,
+the steady loop takes the rest that still have a stage R ahead to load
+(two stages per trip on the 128-value rings), and the last R drain.
 The prefill workloads reach every class only at K = 7168 and 1536.  Here
 expert row counts hit each class and its edges (32/33, 64/65, 128/129 and
 several tiles of one expert) at K = 512, 1024, 1536 and 2048 on both GEMMs
