@@ -9,6 +9,9 @@ decode on one layer of 896 resident experts (hidden 7168, intermediate
 the routed experts differ from step to step and the 256 MB last-level cache
 cannot serve them.
 
+Every timed region is queued behind a short spin kernel, so the host's
+latency to its first launch stays out of the figure.
+
 Prints one JSON line: value = routed-expert weight GB/s of the whole layer
 (its own fraction of the HBM peak in layer_roofline), the roofline of the
 expert-FFN call (HIP events on the launch stream), and the CPU oracle's rate
@@ -185,20 +188,12 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # timed region: K whole-layer steps
     stream = torch.cuda.current_stream(dev)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ms_step = ev0.elapsed_time(ev1) / args.steps
+    sleep_cycles = sleep_calibration(stream)
+    # timed region: K whole-layer steps
+    ms_step = timed_eager(lambda: [step(i) for i in range(args.steps)], stream, sleep_cycles) / args.steps
     value = weight_bytes / (ms_step * 1e-3) / 1e9
-    log(f"layer: {ms_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us), {value:.0f} GB/s")
+    log(f"layer: {ms_step * 1e3:.1f} us/step, {value:.0f} GB/s")
 
     # expert-FFN call alone, events on its launch stream around every call
     K = args.steps
@@ -214,14 +209,10 @@ def main():
     for i in range(args.warmup):
         expert_ffn_mxfp4(xs[i % V], wl.k, pool, gobjs[i % V], layer.workspace, y_rows)
     torch.cuda.synchronize()
-    # average launch duration: K back-to-back calls between one event pair
-    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    f0.record(stream)
-    for i in range(K):
-        expert_ffn_mxfp4(xs[i % V], wl.k, pool, gobjs[i % V], layer.workspace, y_rows)
-    f1.record(stream)
-    torch.cuda.synchronize()
-    ffn_us = f0.elapsed_time(f1) * 1e3 / K
+    # average launch duration: K back-to-back calls between one event pair,
+    # queued behind a spin kernel so the host's launch latency stays outside
+    ffn_us = timed_eager(lambda: [expert_ffn_mxfp4(xs[i % V], wl.k, pool, gobjs[i % V], layer.workspace, y_rows)
+                                  for i in range(K)], stream, sleep_cycles) * 1e3 / K
     # spread of single calls (each bracketed by its own events, whose records add some time)
     for i in range(K):
         a, b = evs[i]
@@ -270,6 +261,47 @@ def main():
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(args, wl)
     print(json.dumps(res), flush=True)
+
+
+def sleep_calibration(stream):
+    """Device-clock cycles of torch's spin kernel that keep the GPU busy for
+    about 2 ms (0 if the build has no spin kernel)."""
+    import torch
+
+    if not hasattr(torch.cuda, "_sleep"):
+        return 0
+    torch.cuda._sleep(1000)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    torch.cuda._sleep(200000)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = max(a.elapsed_time(b), 1e-3)
+    return int(min(2.0 / ms, 100.0) * 200000)
+
+
+def prime(stream, cycles):
+    """Queue a spin kernel, so the launches that follow are queued before
+    the GPU reaches them."""
+    import torch
+
+    if cycles > 0:
+        torch.cuda._sleep(cycles)
+
+
+def timed_eager(fn, stream, cycles):
+    """ms between two events around fn()'s launches, queued behind a spin
+    kernel so the first launch's host latency is not in the figure."""
+    import torch
+
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    prime(stream, cycles)
+    a.record(stream)
+    fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b)
 
 
 def per_call_us(fn, reps, stream):
