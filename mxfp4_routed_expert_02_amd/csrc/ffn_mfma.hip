@@ -35,23 +35,25 @@
 // Tiles: 256 weight rows x 128 tokens per block of 4 waves, one block per
 // CU (32 tokens per wave, 8 row blocks of 32 each, accumulators in AGPRs).
 // For gate/up the 256 rows are gate rows i0..i0+127 followed by the same up
-// rows, so SiLU(g)*u is formed in registers.  Every operand of a 128-value
-// K stage (weight codes and scales, activation terms and scales) travels
-// from global memory into an LDS ring slot by LDS DMA loads, with no trip
+// rows, so SiLU(g)*u is formed in registers.  Every operand of a K stage
+// (weight codes and scales, activation terms and scales) travels from
+// global memory into an LDS ring slot by LDS DMA loads, with no trip
 // through registers; the ring keeps two or three stages in flight per CU
 // while one is read, so tiles with few tokens stream their weights at
-// memory speed and full tiles keep the MFMA pipe fed.  The waits on those loads are explicit
-// counts of each wave's own loads, which complete in issue order.
+// memory speed and full tiles keep the MFMA pipe fed.  The waits on those
+// loads are explicit counts of each wave's own loads, which complete in
+// issue order.
 // A tile's 128 token slots form 4 groups of 32; a tile whose expert rows
 // fill only 1 or 2 groups runs with the 4 waves splitting the row blocks
 // instead (2 or 4 blocks each, gate blocks kept with their up blocks) and a
-// ring shaped for them (two groups: a deeper ring of smaller slots; one
-// group: 256-value stages whose weight loads take whole cache lines), so
-// MFMA work follows the routed rows rather than the padded tile.  The plan orders (expert, token tile) pairs
-// heaviest first, an expert's full token tiles next to each other, and
-// deals them to the 8 XCDs in runs of four; each XCD steps through the
-// weight tiles of its run with all four token tiles at each, so the token
-// tiles of one expert read each weight tile into that XCD's L2 together.
+// ring shaped for them (two groups: a deeper ring of smaller 128-value
+// stages; one group: 256-value stages whose weight loads take whole cache
+// lines), so MFMA work follows the routed rows rather than the padded tile.
+// The plan orders (expert, token tile) pairs heaviest first, an expert's
+// full token tiles next to each other, and deals them to the 8 XCDs in runs
+// of four; each XCD steps through the weight tiles of its run with all four
+// token tiles at each, so the token tiles of one expert read each weight
+// tile into that XCD's L2 together.
 #include <climits>
 #include <type_traits>
 
