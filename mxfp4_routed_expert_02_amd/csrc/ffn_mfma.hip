@@ -387,7 +387,12 @@ constexpr int kRingBytes = cmax(cmax(cmax(Ring<2, false>::kBytes, Ring<4, false>
 // `lds` (lane l at lds + size*l).  Issued from asm, so the compiler neither
 // counts them nor waits for them: the ring's waits below are explicit.
 // From a wave-uniform base (scalar registers) plus this lane's 32-bit
-// offset: a stage's loads advance only the bases, with scalar adds.
+// offset: a stage's loads advance only the bases, with scalar adds.  The
+// asm sets m0 (the LDS address) itself and declares it clobbered; the
+// compiler's note that a reserved register may not be preserved is moot,
+// since no code here reads m0 after these loads.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_dma16(const void* base, uint32_t off, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds) : "memory", "m0");
 }
@@ -398,6 +403,7 @@ __device__ __forceinline__ void lds_dma4(const void* base, uint32_t off, uint32_
 __device__ __forceinline__ void lds_dma16_nt(const void* base, uint32_t off, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(off), "s"(base), "s"(lds) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // s_waitcnt vmcnt(N) (N clamped to the counter's 63) with the other counters free
 template <int N>
