@@ -117,11 +117,12 @@ __global__ __launch_bounds__(kRoute4Threads) void route_group_one_kernel(const f
 }
 
 // ------------------------------------------------------------------ group --
-constexpr int kGroupThreads = 1024;
-// In-place exclusive scan of a[0..n) in LDS by the whole block; returns total.
+// In-place exclusive scan of a[0..n) in LDS by the whole block (NT threads,
+// s_wave holding NT/64 + 1 ints); returns the total.
+template <int NT>
 __device__ int block_exclusive_scan(int* a, int n, int* s_wave) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int per = (n + kGroupThreads - 1) / kGroupThreads;
+  const int per = (n + NT - 1) / NT;
   const int beg = min(n, tid * per), end = min(n, beg + per);
   int local = 0;
   for (int i = beg; i < end; ++i) local += a[i];
@@ -136,12 +137,12 @@ __device__ int block_exclusive_scan(int* a, int n, int* s_wave) {
   __syncthreads();
   if (tid == 0) {
     int acc = 0;
-    for (int w = 0; w < kGroupThreads / 64; ++w) {
+    for (int w = 0; w < NT / 64; ++w) {
       const int c = s_wave[w];
       s_wave[w] = acc;
       acc += c;
     }
-    s_wave[kGroupThreads / 64] = acc;
+    s_wave[NT / 64] = acc;
   }
   __syncthreads();
   int run = s_wave[wave] + v - local;
@@ -150,7 +151,7 @@ __device__ int block_exclusive_scan(int* a, int n, int* s_wave) {
     a[i] = run;
     run += c;
   }
-  const int total = s_wave[kGroupThreads / 64];
+  const int total = s_wave[NT / 64];
   __syncthreads();
   return total;
 }
@@ -159,13 +160,15 @@ __device__ int block_exclusive_scan(int* a, int n, int* s_wave) {
 //   count:   per chunk, each expert's row count and each row's rank among
 //            the chunk's earlier rows of the same expert (many blocks)
 //   scan:    per expert, the chunks' counts become exclusive positions
-//            within the expert, and the totals become expert_offsets and the
-//            active list (one block)
-//   scatter: each row goes to expert offset + chunk position + rank (many
-//            blocks)
+//            within the expert, and the expert's total is written (many
+//            blocks: 32 lanes per expert, each over a run of chunks, the
+//            runs joined by a scan across the 32 lanes)
+//   scatter: every block scans the E totals into expert offsets in LDS;
+//            block 0 also writes expert_offsets and the active list; each
+//            row goes to expert offset + chunk position + rank (many blocks)
 // Positions follow (chunk, rank in chunk) = ascending row index within each
 // expert, the same stable order as a counting sort.  Workspace: cnt
-// [chunks][E] then rank [R] (int32).
+// [chunks][E], rank [R], then the totals [E] (int32).
 constexpr int kChunkRows = 256;
 
 __global__ __launch_bounds__(kChunkRows) void group_count_kernel(const int32_t* __restrict__ ids, int R, int E,
@@ -190,68 +193,80 @@ __global__ __launch_bounds__(kChunkRows) void group_count_kernel(const int32_t* 
   for (int x = tid; x < E; x += kChunkRows) cnt[(int64_t)c * E + x] = s_cnt[x];
 }
 
-__global__ __launch_bounds__(kGroupThreads) void group_scan_kernel(int nch, int E, int32_t* __restrict__ cnt,
-                                                                  int32_t* __restrict__ offsets,
-                                                                  int32_t* __restrict__ active) {
-  extern __shared__ int s_mem[];
-  int* s_tot = s_mem;       // [E] totals, then offsets
-  int* s_flag = s_mem + E;  // [E] active flags, then their scan
-  __shared__ int s_wave[kGroupThreads / 64 + 1];
-  const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += kGroupThreads) {
-    // counts of 8 chunks are loaded before any is rewritten
-    int run = 0;
-    int c0 = 0;
-    for (; c0 + 8 <= nch; c0 += 8) {
+constexpr int kScanExperts = 8;  // experts per scan block (2 per wave of 64 lanes)
+__global__ __launch_bounds__(kChunkRows) void group_scan_kernel(int nch, int E, int32_t* __restrict__ cnt,
+                                                                int32_t* __restrict__ tot) {
+  static_assert(kChunkRows == 32 * kScanExperts, "32 lanes per expert");
+  const int e = blockIdx.x * kScanExperts + (threadIdx.x >> 5), cl = threadIdx.x & 31;
+  const int per = (nch + 31) / 32;
+  const int c0 = min(nch, cl * per), c1 = min(nch, c0 + per);
+  int local = 0;
+  if (e < E) {
+    // all of this lane's counts are loaded before any is rewritten
+    for (int c = c0; c < c1; c += 8) {
       int v[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = cnt[(int64_t)(c0 + i) * E + e];
+      for (int i = 0; i < 8; ++i) v[i] = c + i < c1 ? cnt[(int64_t)(c + i) * E + e] : 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        cnt[(int64_t)(c0 + i) * E + e] = run;
-        run += v[i];
-      }
+      for (int i = 0; i < 8; ++i) local += v[i];
     }
-    for (int c = c0; c < nch; ++c) {
-      const int v = cnt[(int64_t)c * E + e];
-      cnt[(int64_t)c * E + e] = run;
-      run += v;
+  }
+  // inclusive scan across the expert's 32 lanes (chunk runs in order)
+  int incl = local;
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) {
+    const int u = __shfl_up(incl, o, 32);
+    if (cl >= o) incl += u;
+  }
+  if (e >= E) return;
+  int run = incl - local;
+  for (int c = c0; c < c1; ++c) {
+    const int v = cnt[(int64_t)c * E + e];
+    cnt[(int64_t)c * E + e] = run;
+    run += v;
+  }
+  if (cl == 31) tot[e] = incl;
+}
+
+__global__ __launch_bounds__(kChunkRows) void group_scatter_kernel(const int32_t* __restrict__ ids, int R, int E,
+                                                                  const int32_t* __restrict__ tot,
+                                                                  const int32_t* __restrict__ cnt,
+                                                                  const int32_t* __restrict__ rank,
+                                                                  int32_t* __restrict__ offsets,
+                                                                  int32_t* __restrict__ active,
+                                                                  int32_t* __restrict__ sorted_rows,
+                                                                  int32_t* __restrict__ row_pos) {
+  extern __shared__ int s_off[];  // [E] offsets, then [E] active flags (block 0)
+  __shared__ int s_wave[kChunkRows / 64 + 1];
+  const int tid = threadIdx.x;
+  for (int x = tid; x < E; x += kChunkRows) s_off[x] = tot[x];
+  __syncthreads();
+  const int total = block_exclusive_scan<kChunkRows>(s_off, E, s_wave);
+  if (blockIdx.x == 0) {
+    int* s_flag = s_off + E;
+    for (int x = tid; x < E; x += kChunkRows) {
+      offsets[x] = s_off[x];
+      const int next = x + 1 < E ? s_off[x + 1] : total;
+      s_flag[x] = next > s_off[x] ? 1 : 0;
     }
-    s_tot[e] = run;
-  }
-  __syncthreads();
-  const int total = block_exclusive_scan(s_tot, E, s_wave);  // s_tot = offsets
-  for (int e = tid; e < E; e += kGroupThreads) {
-    offsets[e] = s_tot[e];
-    const int next = (e + 1 < E) ? s_tot[e + 1] : total;
-    s_flag[e] = next > s_tot[e] ? 1 : 0;
-  }
-  if (tid == 0) offsets[E] = total;
-  __syncthreads();
-  {
-    const int per = (E + kGroupThreads - 1) / kGroupThreads;
+    if (tid == 0) offsets[E] = total;
+    __syncthreads();
+    // the flags' scan gives each active expert its place in the list
+    const int per = (E + kChunkRows - 1) / kChunkRows;
     const int beg = min(E, tid * per), end = min(E, beg + per);
-    int mine[MOE_MAX_EXPERTS / kGroupThreads];
+    int mine[MOE_MAX_EXPERTS / kChunkRows];
     for (int i = beg; i < end; ++i) mine[i - beg] = s_flag[i];
     __syncthreads();
-    const int na = block_exclusive_scan(s_flag, E, s_wave);
+    const int na = block_exclusive_scan<kChunkRows>(s_flag, E, s_wave);
     for (int i = beg; i < end; ++i)
       if (mine[i - beg]) active[1 + s_flag[i]] = i;
     if (tid == 0) active[0] = na;
   }
-}
-
-__global__ __launch_bounds__(kChunkRows) void group_scatter_kernel(const int32_t* __restrict__ ids, int R, int E,
-                                                                  const int32_t* __restrict__ offsets,
-                                                                  const int32_t* __restrict__ cnt,
-                                                                  const int32_t* __restrict__ rank,
-                                                                  int32_t* __restrict__ sorted_rows,
-                                                                  int32_t* __restrict__ row_pos) {
-  const int c = blockIdx.x, r = c * kChunkRows + threadIdx.x;
+  const int c = blockIdx.x, r = c * kChunkRows + tid;
   if (r >= R) return;
   const int e = ids[r];
   if ((unsigned)e >= (unsigned)E) return;
-  const int pos = offsets[e] + cnt[(int64_t)c * E + e] + rank[r];
+  const int pos = s_off[e] + cnt[(int64_t)c * E + e] + rank[r];
   sorted_rows[pos] = r;
   row_pos[r] = pos;
 }
@@ -374,7 +389,7 @@ size_t group_rows_workspace(int T, int k, int E) {
   const size_t R = (size_t)T * k;
   if (R <= (size_t)kSmallRows) return 0;
   const size_t nch = (R + kChunkRows - 1) / kChunkRows;
-  return (nch * (size_t)E + R) * sizeof(int32_t);
+  return (nch * (size_t)E + R + (size_t)E) * sizeof(int32_t);
 }
 
 hipError_t launch_group_rows(const int32_t* ids, int T, int k, int E, int32_t* offsets, int32_t* sorted_rows,
@@ -388,13 +403,15 @@ hipError_t launch_group_rows(const int32_t* ids, int T, int k, int E, int32_t* o
   const int nch = (R + kChunkRows - 1) / kChunkRows;
   int32_t* cnt = (int32_t*)ws;
   int32_t* rank = cnt + (size_t)nch * E;
+  int32_t* tot = rank + R;
   hipLaunchKernelGGL(group_count_kernel, dim3(nch), dim3(kChunkRows), (size_t)4 * E, s, ids, R, E, cnt, rank);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(kGroupThreads), (size_t)8 * E, s, nch, E, cnt, offsets, active);
+  hipLaunchKernelGGL(group_scan_kernel, dim3((E + kScanExperts - 1) / kScanExperts), dim3(kChunkRows), 0, s, nch, E,
+                     cnt, tot);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(group_scatter_kernel, dim3(nch), dim3(kChunkRows), 0, s, ids, R, E, offsets, cnt, rank,
-                     sorted_rows, row_pos);
+  hipLaunchKernelGGL(group_scatter_kernel, dim3(nch), dim3(kChunkRows), (size_t)8 * E, s, ids, R, E, tot, cnt, rank,
+                     offsets, active, sorted_rows, row_pos);
   return hipGetLastError();
 }
 
