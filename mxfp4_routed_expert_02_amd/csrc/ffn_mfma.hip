@@ -69,6 +69,8 @@ constexpr int kBand = 4;          // consecutive plan pairs per XCD
 
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef float v16f_t __attribute__((ext_vector_type(16)));
+typedef float v32f_t __attribute__((ext_vector_type(32)));
+typedef unsigned v6u_t __attribute__((ext_vector_type(6)));
 
 // ------------------------------------------------------------ E4M3 terms --
 // Rounding to E4M3 (the OCP format: bias 7, largest finite 448, subnormals
@@ -84,29 +86,6 @@ __device__ __forceinline__ int e4m3_block_exp(float amax) {
   const int E = (int)((b >> 23) & 0xFF) - 127;
   int e = ((b & 0x7FFFFFu) <= 0x600000u) ? E - 8 : E - 7;  // 448 = 1.75 * 2^8
   return e < -126 ? -126 : (e > 126 ? 126 : e);  // 2^e and 2^-e stay normal floats
-}
-
-// Round |a| <= 7.5 to E2M3 (FP6: sign, 2 exponent bits with bias 1, 3
-// mantissa bits; ties to even); returns the 6-bit code and the rounded value.
-__device__ __forceinline__ uint32_t e2m3_rne(float a, float& qv) {
-  const float x = fabsf(a);
-  uint32_t code;
-  if (x < 1.0f) {  // the subnormal grid m / 8 (m = 8 is 1.0, code 8)
-    const float m = rintf(x * 8.0f);
-    code = (uint32_t)m;
-    qv = m * 0.125f;
-  } else {
-    uint32_t b = __float_as_uint(x);
-    b += 0x7FFFFu + ((b >> 20) & 1u);  // keep 3 mantissa bits
-    b &= 0xFFF00000u;
-    code = (b >> 20) - (126u << 3);    // exponent bias 127 -> 1
-    qv = __uint_as_float(b);
-  }
-  if (a < 0.0f) {
-    code |= 0x20u;
-    qv = -qv;
-  }
-  return code;
 }
 
 // E8M0 exponent e with amax / 2^e <= 7.5, e = ceil(log2(amax / 7.5)); 0 for amax = 0
@@ -151,19 +130,24 @@ __device__ __forceinline__ void quantize_block_fp6(const uint16_t* __restrict__ 
 #pragma unroll
     for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
     const int e = e2m3_block_exp(amax);
-    const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e
     const float scl = __uint_as_float((uint32_t)(127 + e) << 23);  // 2^e
-    uint32_t pk[6];
+    // v_cvt_scalef32_2xpk16_fp6_f32 rounds a[j] / 2^e and b[j] / 2^e to E2M3
+    // (nearest, ties to even) into codes 2j and 2j+1, 6 bits each, code i at
+    // bits 6i .. 6i+5; v_cvt_scalef32_pk32_f32_fp6 gives the 32 rounded
+    // values times 2^e back.  (Checked against a software rounding over every
+    // E2M3 value, the midpoints between neighbours and points just off them at
+    // several scales, and 20,000 random blocks: equal codes and values, but
+    // for the sign of a zero code from an input of -0.)
+    v16f_t a, b;
 #pragma unroll
-    for (int i = 0; i < 6; ++i) pk[i] = 0u;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      float qv;
-      const uint32_t c = e2m3_rne(v[i] * inv, qv);
-      pk[(6 * i) >> 5] |= c << ((6 * i) & 31);
-      if (((6 * i) & 31) > 26) pk[((6 * i) >> 5) + 1] |= c >> (32 - ((6 * i) & 31));
-      v[i] -= qv * scl;  // residual for the next term (exact)
+    for (int j = 0; j < 16; ++j) {
+      a[j] = v[2 * j];
+      b[j] = v[2 * j + 1];
     }
+    const v6u_t pk = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(a, b, scl);
+    const v32f_t qv = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(pk, scl);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] -= qv[i];  // residual for the next term (exact)
     uint8_t* r = rec + term * 128;
     *(uint4*)(r + 48 * s + 16 * h) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
     *(uint2*)(r + 48 * s + 32 + 8 * h) = make_uint2(pk[4], pk[5]);
