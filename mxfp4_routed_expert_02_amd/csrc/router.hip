@@ -82,18 +82,19 @@ __global__ __launch_bounds__(kThreads) void router_gemv_kernel(const uint16_t* _
 // remainder, at most 8 significant bits), so every product x * w_i is exact
 // in fp32 and the MFMA accumulates sum_c x[c] * (w1 + w2 + w3)[c] in fp32,
 // three bf16 MFMAs per 16-deep step (a third of the bf16 rate, five times
-// the fp32 MFMA's).  Tile: 64 experts x 64 tokens per block of 8 waves:
-// waves 0-3 take the first half of K and waves 4-7 the second, each wave
-// one 32 x 32 output block of its half, and the halves' sums meet in LDS
-// at the end, first half plus second half (the weights are split once per
-// token tile, so wider token tiles split less); K stages of 64 values in LDS as
-// three weight planes and one x plane of [64][64] bf16, double-buffered,
-// the 16-byte piece p of row r at
-// r*128 + 16*(p ^ ((r >> 1) & 7)) so that the fragment reads of 16
-// consecutive rows hit distinct bank groups.  Global loads run two stages
-// ahead through two register sets.  Blocks of one expert tile run on one
-// XCD, which then reads that tile of Wr once.
-constexpr int kRe = 64, kRtok = 64;  // experts and tokens per block
+// the fp32 MFMA's).  Tile: 32 experts x 64 tokens per block of 8 waves (at
+// 512 tokens and 896 experts, 224 blocks for the 256 CUs): waves 0-3 take
+// the first half of K and waves 4-7 the second; within a half, wave w takes
+// token block w % 2 and the 16-deep steps 2 (w / 2), 2 (w / 2) + 1 of every
+// 64-value stage, so each output element has four partial sums, which meet
+// in LDS at the end in a fixed order (first half's two, then the second
+// half's two).  K stages of 64 values sit in LDS as three weight planes
+// [32][64] and one x plane [64][64] of bf16, double-buffered, the 16-byte
+// piece p of row r at r*128 + 16*(p ^ ((r >> 1) & 7)) so that the fragment
+// reads of 16 consecutive rows hit distinct bank groups.  Global loads run
+// two stages ahead through two register sets.  Blocks of one expert tile
+// run on one XCD, which then reads that tile of Wr once.
+constexpr int kRe = 32, kRtok = 64;  // experts and tokens per block
 constexpr int kRk = 64;              // K values per stage
 constexpr int kRthreads = 512;  // two halves of 4 waves
 constexpr int kWPlane = kRe * kRk * 2, kXPlane = kRtok * kRk * 2;  // bytes
@@ -103,7 +104,7 @@ typedef float v16f_t __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ int swz(int r, int p) { return r * 128 + 16 * (p ^ ((r >> 1) & 7)); }
 
 struct RouterStage {
-  float4 w[4];  // 16 weights of one expert row
+  float4 w[2];  // 8 weights of one expert row
   uint4 x[2];   // 16 bf16 of one token row
 };
 
@@ -129,9 +130,9 @@ __global__ __launch_bounds__(kRthreads) void router_mfma_kernel(const uint16_t* 
   const int e0 = et * kRe, t0 = ttile * kRtok;
   if (e0 >= E) return;
 
-  // staging: thread t takes expert row t/4 and token row t/4, K values
-  // 16 (t%4) .. +15 of the stage
-  const int wrow = tid >> 2, wk = 16 * (tid & 3), xrow = tid >> 2, xk = 16 * (tid & 3);
+  // staging: thread t takes expert row t/8, K values 8 (t%8) .. +7 of the
+  // stage, and token row t/4, K values 16 (t%4) .. +15
+  const int wrow = tid >> 3, wk = 8 * (tid & 7), xrow = tid >> 2, xk = 16 * (tid & 3);
   // rows past E or T read row 0 (their outputs are never stored); K past H
   // reads in range and is zeroed, so every load is unconditional
   // this half's stages: nst of 64 K values from kbase (both halves run the
@@ -142,12 +143,12 @@ __global__ __launch_bounds__(kRthreads) void router_mfma_kernel(const uint16_t* 
   const float* wsrc = wr + (int64_t)(e0 + wrow < E ? e0 + wrow : 0) * H;
   const uint16_t* xsrc = x + (int64_t)(t0 + xrow < T ? t0 + xrow : 0) * H;
   auto load = [&](int k0, RouterStage& r) {
-    // H % 32 == 0: a 16-value segment is all in or all out
+    // H % 32 == 0: an 8- or 16-value segment is all in or all out
     const bool win = kbase + k0 + wk < H, xin = kbase + k0 + xk < H;
     const int kw = win ? kbase + k0 + wk : 0, kx = xin ? kbase + k0 + xk : 0;
     const uint32_t mw = win ? ~0u : 0u, mx = xin ? ~0u : 0u;  // bit masks, not branches
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
       const uint4 v = *(const uint4*)(wsrc + kw + 4 * i);
       r.w[i] = make_float4(__uint_as_float(v.x & mw), __uint_as_float(v.y & mw), __uint_as_float(v.z & mw),
                            __uint_as_float(v.w & mw));
@@ -159,39 +160,37 @@ __global__ __launch_bounds__(kRthreads) void router_mfma_kernel(const uint16_t* 
     }
   };
   auto store = [&](int b, const RouterStage& r) {
+    const float f[8] = {r.w[0].x, r.w[0].y, r.w[0].z, r.w[0].w, r.w[1].x, r.w[1].y, r.w[1].z, r.w[1].w};
+    uint32_t t1[4], t2[4], t3[4];
 #pragma unroll
-    for (int pc = 0; pc < 2; ++pc) {  // 8 weights per 16-byte piece
-      const float f[8] = {r.w[2 * pc].x, r.w[2 * pc].y, r.w[2 * pc].z, r.w[2 * pc].w,
-                          r.w[2 * pc + 1].x, r.w[2 * pc + 1].y, r.w[2 * pc + 1].z, r.w[2 * pc + 1].w};
-      uint32_t t1[4], t2[4], t3[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float a = f[2 * i], c = f[2 * i + 1];
-        const float ra = lo_rest(a), rc = lo_rest(c);      // w - w1
-        const float qa = lo_rest(ra), qc = lo_rest(rc);    // w - w1 - w2 = w3
-        t1[i] = hi_pair(a, c);
-        t2[i] = hi_pair(ra, rc);
-        t3[i] = hi_pair(qa, qc);
-      }
-      const int o = swz(wrow, (wk >> 3) + pc);
-      *(uint4*)&s_buf[b][o] = make_uint4(t1[0], t1[1], t1[2], t1[3]);
-      *(uint4*)&s_buf[b][kWPlane + o] = make_uint4(t2[0], t2[1], t2[2], t2[3]);
-      *(uint4*)&s_buf[b][2 * kWPlane + o] = make_uint4(t3[0], t3[1], t3[2], t3[3]);
+    for (int i = 0; i < 4; ++i) {
+      const float a = f[2 * i], c = f[2 * i + 1];
+      const float ra = lo_rest(a), rc = lo_rest(c);    // w - w1
+      const float qa = lo_rest(ra), qc = lo_rest(rc);  // w - w1 - w2 = w3
+      t1[i] = hi_pair(a, c);
+      t2[i] = hi_pair(ra, rc);
+      t3[i] = hi_pair(qa, qc);
     }
+    const int o = swz(wrow, wk >> 3);  // 8 weights = one 16-byte piece per plane
+    *(uint4*)&s_buf[b][o] = make_uint4(t1[0], t1[1], t1[2], t1[3]);
+    *(uint4*)&s_buf[b][kWPlane + o] = make_uint4(t2[0], t2[1], t2[2], t2[3]);
+    *(uint4*)&s_buf[b][2 * kWPlane + o] = make_uint4(t3[0], t3[1], t3[2], t3[3]);
 #pragma unroll
     for (int h = 0; h < 2; ++h) *(uint4*)&s_buf[b][3 * kWPlane + swz(xrow, (xk >> 3) + h)] = r.x[h];
   };
 
-  // wave's output block: experts 32 (wave & 1) .., tokens 32 (wave >> 1) ..
+  // wave's output block: all 32 experts x tokens 32 (wave & 1) ..; its
+  // 16-deep steps 2 (wave >> 1) and 2 (wave >> 1) + 1 of every stage
   const int n = lane & 31, kh = lane >> 5;
-  const int arow = 32 * (wave & 1) + n, brow = 32 * (wave >> 1) + n;
+  const int tb = wave & 1, kg = wave >> 1;
+  const int arow = n, brow = 32 * tb + n;
   v16f_t acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
   auto compute = [&](int b) {
 #pragma unroll
-    for (int s = 0; s < kRk / 16; ++s) {
-      const int p = 2 * s + kh;  // lane's 8 K values: 16 s + 8 kh
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int p = 2 * (2 * kg + s2) + kh;  // lane's 8 K values: 16 s + 8 kh
       const bf16x8_t xb = *(const bf16x8_t*)&s_buf[b][3 * kWPlane + swz(brow, p)];
 #pragma unroll
       for (int term = 0; term < 3; ++term) {
@@ -234,23 +233,29 @@ __global__ __launch_bounds__(kRthreads) void router_mfma_kernel(const uint16_t* 
       compute(0);
     }
   }
-  // the second half's sums to LDS (over its buffers, now free), then the
-  // first half adds them in and stores.  D lane l, register r: token l % 32
-  // of the wave's block, expert 8 (r/4) + 4 (l/32) + r%4
-  float* s_red = (float*)&s_all[1][0][0];
+  // the four partial sums of each output element meet in LDS (over the
+  // stage buffers, now free): every wave but the first half's kg = 0 pair
+  // writes its sums to slot (half, kg) of its token block; those two waves
+  // add them in the order (half 0, kg 1), (half 1, kg 0), (half 1, kg 1).
+  // D lane l, register r: token l % 32 of the block, expert 8 (r/4) + 4 (l/32) + r%4
+  float* s_red = (float*)&s_all[0][0][0];
   __syncthreads();  // every wave is done reading its stages
-  if (khalf == 1) {
+  const int part = 2 * khalf + kg;  // 0 .. 3
+  if (part > 0) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s_red[(wave * 16 + r) * 64 + lane] = acc[r];
+    for (int r = 0; r < 16; ++r) s_red[(((part - 1) * 2 + tb) * 16 + r) * 64 + lane] = acc[r];
   }
   __syncthreads();
-  if (khalf == 1) return;
-  const int t = t0 + 32 * (wave >> 1) + n;
+  if (part > 0) return;
+  const int t = t0 + 32 * tb + n;
   if (t >= T) return;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const int e = e0 + 32 * (wave & 1) + 8 * (r >> 2) + 4 * kh + (r & 3);
-    if (e < E) logits[(int64_t)t * E + e] = acc[r] + s_red[(wave * 16 + r) * 64 + lane];
+    const int e = e0 + 8 * (r >> 2) + 4 * kh + (r & 3);
+    float v = acc[r];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) v += s_red[((q * 2 + tb) * 16 + r) * 64 + lane];
+    if (e < E) logits[(int64_t)t * E + e] = v;
   }
 }
 
