@@ -59,9 +59,10 @@ def parse():
     return p.parse_args()
 
 
-def profiled_traffic():
-    """HBM bytes per expert-FFN call from the committed counter summary, or
-    None when the kernel sources changed since those counters were taken."""
+def profiled_traffic(what="ffn_call"):
+    """HBM bytes per expert-FFN call (what="ffn_call") or per decode layer
+    (what="layer") from the committed counter summary, or None when the
+    kernel sources changed since those counters were taken."""
     import re
 
     path = os.path.join(ROOT, "profiles", "decode896_hbm_traffic.md")
@@ -69,7 +70,8 @@ def profiled_traffic():
         return None
     text = open(path).read()
     m_sha = re.search(r"sources_sha256: ([0-9a-f]{64})", text)
-    m_bytes = re.search(r"ffn_call_traffic_bytes: (\d+)", text)
+    pattern = r"ffn_call_traffic_bytes: (\d+)" if what == "ffn_call" else r"Per decode layer: (\d+) bytes"
+    m_bytes = re.search(pattern, text)
     if not (m_sha and m_bytes):
         return None
     return int(m_bytes.group(1)) if ffn_sources_sha256() == m_sha.group(1) else None
@@ -236,7 +238,8 @@ def main():
                          "what": "untimed layer steps before the warm-up steps, until the GPU runs at its sustained clock"},
         "layer_roofline": {"bound": "hbm", "what": "whole decode layer (value / peak)", "achieved": round(value, 1),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(value / HBM_PEAK_GBS, 4),
-                           "algorithmic_bytes": weight_bytes, "us_per_step": round(ms_step * 1e3, 2)},
+                           "algorithmic_bytes": weight_bytes, "us_per_step": round(ms_step * 1e3, 2),
+                           "traffic": profiled_traffic("layer")},
         "roofline": {"bound": "hbm", "kernel": "moe_expert_ffn_mxfp4 call", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": profiled_traffic(), "launch_us": round(ffn_us, 2),
