@@ -136,8 +136,9 @@ __device__ __forceinline__ void quantize_block_fp6(const uint16_t* __restrict__ 
     // bits 6i .. 6i+5; v_cvt_scalef32_pk32_f32_fp6 gives the 32 rounded
     // values times 2^e back.  (Checked against a software rounding over every
     // E2M3 value, the midpoints between neighbours and points just off them at
-    // several scales, and 20,000 random blocks: equal codes and values, but
-    // for the sign of a zero code from an input of -0.)
+    // several scales, 20,000 random blocks and 2,000 blocks of fp32
+    // subnormals: equal codes and values, but for the sign of a zero code
+    // from an input of -0.)
     v16f_t a, b;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
